@@ -1,0 +1,284 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU reference of the routed NVFP4 mixture-of-experts FFN. Only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg load this library; the GPU
+ * library shares no code, header, table or helper with it.
+ *
+ * What it computes, and where each step comes from:
+ *  - NVFP4 weights: 64 weights in a 36-byte block, four UE4M3 sub-scales (one per 16 weights)
+ *    followed by 32 code bytes of E2M1 nibbles (moe_sel_census.rs, the NVFP4 block constants;
+ *    moe_union_probe.rs, the per-expert byte arithmetic: half a byte of code per weight plus one
+ *    scale byte per 16 weights). Inside a block: byte j (j<4) is the scale of weights 16j..16j+15; byte 4+i holds
+ *    weight 2i in its low nibble and weight 2i+1 in its high nibble (the plainest reading; the
+ *    pages give no nibble order). A row is out-row o, contiguous along the input features.
+ *  - E2M1 and UE4M3 values: the OCP Microscaling (MX) FP4 E2M1 element type and the OCP FP8
+ *    E4M3 ("fn": bias 7, no infinities, 0x7F NaN) type with its sign bit required to be 0.
+ *  - Routing buckets: pairs p = t*k + j are pushed into per-expert lists in ascending p, the
+ *    non-empty lists are concatenated in ascending expert id, and the offsets are the running
+ *    totals (moe_sk_repro.rs, the host bucketing in main before the grouped calls). Ids outside
+ *    [expert_base, expert_base+E) are not routed here and are counted instead.
+ *  - The FFN per routed pair: gate and up projections of the token's activation row, SiLU of
+ *    the gate times the up value, the down projection, and the router-weighted sum over the
+ *    token's k slots taken in ascending slot order (moe_union_probe.rs: the fused
+ *    sel_gu_silu and sel_v3 kernels it names; moe_sk_repro.rs: gate, up and down grouped
+ *    calls). Everything is fp64; the intermediate h is not rounded.
+ *
+ * Two forms of the FFN are provided. The per-slot form walks the pairs of each token and decodes
+ * each needed weight row as it goes. The union form decodes every distinct active expert once
+ * and then walks that expert's bucket (moe_union_probe.rs: the union-of-experts gather). Both
+ * perform the same fp64 operations in the same order and must agree bit for bit.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_BLOCK_WEIGHTS 64
+#define ORC_BLOCK_BYTES 36
+
+/* OCP MX FP4 E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa. */
+double orc_e2m1(int code)
+{
+    int s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+    double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -mag : mag;
+}
+
+/* OCP FP8 E4M3 (fn) with the sign bit fixed at 0: bits 6..3 exponent (bias 7), bits 2..0
+ * mantissa; exponent 0 is subnormal (m * 2^-9); 0x7F is NaN. Bytes with bit 7 set are not
+ * UE4M3 values and also return NaN. */
+double orc_ue4m3(int byte)
+{
+    if (byte < 0 || byte > 0x7E) return NAN;
+    int e = (byte >> 3) & 15, m = byte & 7;
+    if (e == 0) return ldexp((double)m, -9);
+    return ldexp(1.0 + m / 8.0, e - 7);
+}
+
+/* bfloat16 bit pattern to its exact value. */
+double orc_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Weight i of one NVFP4 row. */
+double orc_nvfp4_weight(const uint8_t *row, int64_t i)
+{
+    const uint8_t *blk = row + (i / ORC_BLOCK_WEIGHTS) * ORC_BLOCK_BYTES;
+    int w = (int)(i % ORC_BLOCK_WEIGHTS);
+    int scale_byte = blk[w / 16];
+    int code_byte = blk[4 + w / 2];
+    int code = (w & 1) ? (code_byte >> 4) : (code_byte & 15);
+    return orc_e2m1(code) * orc_ue4m3(scale_byte);
+}
+
+int64_t orc_row_bytes(int64_t in_f) { return in_f / ORC_BLOCK_WEIGHTS * ORC_BLOCK_BYTES; }
+
+/* Decode n_rows consecutive rows of in_f weights into out[n_rows][in_f]. */
+void orc_dequant_rows(const uint8_t *rows, int64_t n_rows, int64_t in_f, double *out)
+{
+    int64_t rb = orc_row_bytes(in_f);
+    for (int64_t r = 0; r < n_rows; r++)
+        for (int64_t i = 0; i < in_f; i++) out[r * in_f + i] = orc_nvfp4_weight(rows + r * rb, i);
+}
+
+/*
+ * Expert-first bucketing. ids[T*k] (pair p = t*k + j). Local expert = id - expert_base.
+ * Writes offsets[E+1] (exclusive running totals over all E local experts), pair_ids[0 ..
+ * offsets[E]) (pairs grouped by expert, ascending p inside a bucket), active[0 .. n_active)
+ * (non-empty local experts, ascending), counts[0] = n_active, counts[1] = n_nonlocal.
+ * Returns 0, or -1 on bad arguments.
+ */
+int orc_route_bucket(const int32_t *ids, int64_t T, int32_t k, int32_t E, int32_t expert_base,
+                     int32_t *offsets, int32_t *pair_ids, int32_t *active, int32_t *counts)
+{
+    if (T < 0 || k < 1 || E < 1) return -1;
+    int64_t P = T * k;
+    int64_t *count = calloc((size_t)E, sizeof *count);
+    int64_t *cursor = calloc((size_t)E, sizeof *cursor);
+    if (!count || !cursor) { free(count); free(cursor); return -1; }
+    int64_t nonlocal = 0;
+    for (int64_t p = 0; p < P; p++) {
+        int64_t e = (int64_t)ids[p] - expert_base;
+        if (e < 0 || e >= E) nonlocal++;
+        else count[e]++;
+    }
+    int64_t run = 0, n_active = 0;
+    for (int32_t e = 0; e < E; e++) {
+        offsets[e] = (int32_t)run;
+        cursor[e] = run;
+        run += count[e];
+        if (count[e] > 0) active[n_active++] = e;
+    }
+    offsets[E] = (int32_t)run;
+    for (int64_t p = 0; p < P; p++) {
+        int64_t e = (int64_t)ids[p] - expert_base;
+        if (e < 0 || e >= E) continue;
+        pair_ids[cursor[e]++] = (int32_t)p;
+    }
+    counts[0] = (int32_t)n_active;
+    counts[1] = (int32_t)nonlocal;
+    free(count);
+    free(cursor);
+    return 0;
+}
+
+static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One pair through one expert, from dense decoded matrices:
+ * g = Wg x, u = Wu x, h = silu(g) * u, d = Wd h. Sums run in ascending index. */
+static void pair_ffn_dense(const double *x, const double *Wg, const double *Wu, const double *Wd,
+                           int32_t H, int32_t F, double *h, double *d)
+{
+    for (int32_t o = 0; o < F; o++) {
+        double g = 0.0, u = 0.0;
+        for (int32_t i = 0; i < H; i++) g += Wg[(int64_t)o * H + i] * x[i];
+        for (int32_t i = 0; i < H; i++) u += Wu[(int64_t)o * H + i] * x[i];
+        h[o] = orc_silu(g) * u;
+    }
+    for (int32_t r = 0; r < H; r++) {
+        double s = 0.0;
+        for (int32_t o = 0; o < F; o++) s += Wd[(int64_t)r * F + o] * h[o];
+        d[r] = s;
+    }
+}
+
+/* The same arithmetic, decoding each weight row just before it is used. */
+static void pair_ffn_rowwise(const double *x, const uint8_t *gate, const uint8_t *up,
+                             const uint8_t *down, int32_t H, int32_t F, double *row, double *h,
+                             double *d)
+{
+    int64_t rbh = orc_row_bytes(H), rbf = orc_row_bytes(F);
+    for (int32_t o = 0; o < F; o++) {
+        double g = 0.0, u = 0.0;
+        orc_dequant_rows(gate + o * rbh, 1, H, row);
+        for (int32_t i = 0; i < H; i++) g += row[i] * x[i];
+        orc_dequant_rows(up + o * rbh, 1, H, row);
+        for (int32_t i = 0; i < H; i++) u += row[i] * x[i];
+        h[o] = orc_silu(g) * u;
+    }
+    for (int32_t r = 0; r < H; r++) {
+        double s = 0.0;
+        orc_dequant_rows(down + r * rbf, 1, F, row);
+        for (int32_t o = 0; o < F; o++) s += row[o] * h[o];
+        d[r] = s;
+    }
+}
+
+static void set_threads(int32_t n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/*
+ * Per-slot form. Computes y for the n_tokens token indices in tokens[] (all T tokens if tokens
+ * is NULL; then n_tokens must equal T) into y[n_tokens][H], fp64.
+ * Banks: expert e's gate rows start at gate + e*gate_stride (bytes), likewise up and down;
+ * gate/up rows have H inputs, down rows F inputs.
+ */
+int orc_ffn_per_slot(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
+                     int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
+                     const uint8_t *gate, int64_t gate_stride, const uint8_t *up,
+                     int64_t up_stride, const uint8_t *down, int64_t down_stride,
+                     const int64_t *tokens, int64_t n_tokens, double *y, int32_t n_threads)
+{
+    if (T < 0 || k < 1 || E < 1 || H % 64 || F % 64 || H < 64 || F < 64) return -1;
+    if (!tokens && n_tokens != T) return -1;
+    set_threads(n_threads);
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t n = 0; n < n_tokens; n++) {
+        int64_t t = tokens ? tokens[n] : n;
+        if (t < 0 || t >= T) { bad = 1; continue; }
+        double *xr = malloc(sizeof(double) * (size_t)H);
+        double *row = malloc(sizeof(double) * (size_t)(H > F ? H : F));
+        double *h = malloc(sizeof(double) * (size_t)F);
+        double *d = malloc(sizeof(double) * (size_t)H);
+        double *yr = y + n * H;
+        for (int32_t i = 0; i < H; i++) xr[i] = orc_bf16(x_bf16[t * H + i]);
+        for (int32_t r = 0; r < H; r++) yr[r] = 0.0;
+        for (int32_t j = 0; j < k; j++) {
+            int64_t e = (int64_t)ids[t * k + j] - expert_base;
+            if (e < 0 || e >= E) continue;
+            pair_ffn_rowwise(xr, gate + e * gate_stride, up + e * up_stride,
+                             down + e * down_stride, H, F, row, h, d);
+            double wt = (double)topk_w[t * k + j];
+            for (int32_t r = 0; r < H; r++) yr[r] += wt * d[r];
+        }
+        free(xr); free(row); free(h); free(d);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
+ * Union form over all T tokens: bucket the pairs, decode each active expert once, run every
+ * pair of its bucket, then combine each token's slots in ascending slot order. y[T][H] fp64.
+ * If h_out is not NULL it receives h[p][F] for every local pair p (rows of non-local pairs are
+ * left untouched).
+ */
+int orc_ffn_union(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
+                  int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
+                  const uint8_t *gate, int64_t gate_stride, const uint8_t *up, int64_t up_stride,
+                  const uint8_t *down, int64_t down_stride, double *y, double *h_out,
+                  int32_t n_threads)
+{
+    if (T < 0 || k < 1 || E < 1 || H % 64 || F % 64 || H < 64 || F < 64) return -1;
+    set_threads(n_threads);
+    int64_t P = T * k;
+    int32_t *offsets = malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t *pair_ids = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    int32_t *active = malloc(sizeof(int32_t) * (size_t)E);
+    int32_t counts[2];
+    double *D = calloc((size_t)(P > 0 ? P : 1) * (size_t)H, sizeof(double));
+    char *has = calloc((size_t)(P > 0 ? P : 1), 1);
+    double *Wg = malloc(sizeof(double) * (size_t)F * H);
+    double *Wu = malloc(sizeof(double) * (size_t)F * H);
+    double *Wd = malloc(sizeof(double) * (size_t)H * F);
+    int rc = -1;
+    if (!offsets || !pair_ids || !active || !D || !has || !Wg || !Wu || !Wd) goto out;
+    if (orc_route_bucket(ids, T, k, E, expert_base, offsets, pair_ids, active, counts)) goto out;
+    for (int32_t a = 0; a < counts[0]; a++) {
+        int32_t e = active[a];
+        orc_dequant_rows(gate + e * gate_stride, F, H, Wg);
+        orc_dequant_rows(up + e * up_stride, F, H, Wu);
+        orc_dequant_rows(down + e * down_stride, H, F, Wd);
+        int32_t b0 = offsets[e], b1 = offsets[e + 1];
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int32_t q = b0; q < b1; q++) {
+            int64_t p = pair_ids[q], t = p / k;
+            double *xr = malloc(sizeof(double) * (size_t)H);
+            double *h = malloc(sizeof(double) * (size_t)F);
+            for (int32_t i = 0; i < H; i++) xr[i] = orc_bf16(x_bf16[t * H + i]);
+            pair_ffn_dense(xr, Wg, Wu, Wd, H, F, h, D + p * H);
+            if (h_out) memcpy(h_out + p * F, h, sizeof(double) * (size_t)F);
+            has[p] = 1;
+            free(xr); free(h);
+        }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        double *yr = y + t * H;
+        for (int32_t r = 0; r < H; r++) yr[r] = 0.0;
+        for (int32_t j = 0; j < k; j++) {
+            int64_t p = t * k + j;
+            if (!has[p]) continue;
+            double wt = (double)topk_w[p];
+            for (int32_t r = 0; r < H; r++) yr[r] += wt * D[p * H + r];
+        }
+    }
+    rc = 0;
+out:
+    free(offsets); free(pair_ids); free(active); free(D); free(has); free(Wg); free(Wu); free(Wd);
+    return rc;
+}

@@ -1,0 +1,89 @@
+"""The seeded input generator (CPU only)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+
+
+def _route_bigint(p, E):
+    """The moe_sk_repro probe's router in Python integers (wrapping 64-bit arithmetic spelled
+    out with masks), independent of the vectorised numpy version."""
+    M = (1 << 64) - 1
+    h = (p * 0x9E3779B97F4A7C15) & M
+    h ^= h >> 29
+    h = (h * 0xBF58476D1CE4E5B9) & M
+    h ^= h >> 32
+    u = (h >> 11) / float(1 << 53)
+    return min(int(u ** 1.35 * E), E - 1)
+
+
+def test_route_skewed_bit_exact():
+    ids = gen.route_skewed(4096, 8, 288).reshape(-1)
+    ref = np.array([_route_bigint(p, 288) for p in range(ids.size)])
+    assert np.array_equal(ids, ref)
+
+
+def test_route_skewed_closed_form_hot_expert():
+    """P(expert 0) = P(u^1.35 < 1/E) = (1/E)^(1/1.35)."""
+    ids = gen.route_skewed(4096, 8, 288).reshape(-1)
+    p0 = (1 / 288) ** (1 / 1.35)
+    n = ids.size
+    assert abs((ids == 0).sum() - n * p0) < 4 * np.sqrt(n * p0)
+
+
+@pytest.mark.parametrize("U", [10, 30, 60])
+def test_route_union(U):
+    ids, w = gen.make_routing("verify_chunk", 6, U=U)
+    assert ids.shape == (6, 10)
+    assert np.unique(ids).size == U
+    assert all(np.unique(r).size == 10 for r in ids)
+    assert np.all(np.bincount(ids.reshape(-1), minlength=512)[np.unique(ids)] == 60 // U)
+
+
+def test_route_cyclic_all_active_from_32():
+    for T, U in [(16, 160), (32, 256), (128, 256)]:
+        ids, _ = gen.make_routing("e256_plateau", T)
+        assert np.unique(ids).size == U
+        assert all(np.unique(r).size == 10 for r in ids)
+
+
+def test_route_distinct():
+    ids, _ = gen.make_routing("tiny_decode", 3)
+    assert all(np.unique(r).size == 10 for r in ids) and ids.max() < 64
+
+
+def test_router_weights_softmax_rows():
+    w = gen.router_weights(3, 50, 8)
+    assert w.dtype == np.float32 and np.all(w > 0)
+    assert np.abs(w.astype(np.float64).sum(1) - 1).max() < 1e-6
+
+
+def test_bank_scale_distributions():
+    b = gen.nvfp4_bank(1, 1, 2, 4, 128, scales="pow2").reshape(-1, 36)
+    s = b[:, :4]
+    assert np.all(s % 8 == 0) and s.min() >= 0x08 and s.max() <= 0x48
+    assert set(np.unique(s)) == {8 * e for e in range(1, 10)}
+    b = gen.nvfp4_bank(1, 1, 8, 64, 256, scales="all").reshape(-1, 36)
+    assert b[:, :4].max() <= 0x7E and np.unique(b[:, :4]).size == 127
+    # code bytes are uniform: both nibbles take all 16 values
+    c = b[:, 4:]
+    assert np.unique(c & 15).size == 16 and np.unique(c >> 4).size == 16
+
+
+def test_bf16_rounding_is_rne():
+    vals = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e38], dtype=np.float32)
+    got = gen.f32_to_bf16_bits(vals)
+    ref = torch.tensor(vals).to(torch.bfloat16).view(torch.int16).numpy().astype(np.uint16)
+    assert np.array_equal(got, ref)
+    x = gen.bf16_normal(1, (4, 256))
+    xf = torch.tensor(x.astype(np.int16)).view(torch.bfloat16).float().numpy()
+    assert abs(xf.mean()) < 0.2 and 0.8 < xf.std() < 1.2
+
+
+def test_streams_are_independent_and_reproducible():
+    a = gen.make_workload("tiny_decode", 1, with_banks=False)
+    b = gen.make_workload("tiny_decode", 1, with_banks=False)
+    assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["ids"], b["ids"])
+    c = gen.make_workload("tiny_decode", 1, seed=9, with_banks=False)
+    assert not np.array_equal(a["x"], c["x"])
