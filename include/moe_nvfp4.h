@@ -1,0 +1,148 @@
+/*
+ * moe_nvfp4.h -- C ABI of the routed NVFP4 mixture-of-experts FFN for one AMD MI355X (gfx950).
+ *
+ * The layer (the routed MoE FFN that the memra-engine probes moe_sk_repro.rs,
+ * moe_sel_census.rs and moe_union_probe.rs time, and whose rank-local E256 shape the Rocket
+ * post "Rank-local E256 MoE misses the Qwen K1 and K4 step budgets" measures):
+ *
+ *   for every token t and slot j < k with local expert e = topk_ids[t*k+j] - expert_base:
+ *     g = Wg[e] x_t,  u = Wu[e] x_t,  h = silu(g) * u,  d = Wd[e] h
+ *   y_t = sum over local slots j, in ascending j, of topk_w[t*k+j] * d     (fp32, no atomics)
+ *
+ * Two calls make one layer: moe_route_bucket (expert-first CSR of the routed pairs) and then
+ * moe_ffn_nvfp4 (the FFN over that CSR).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are GPU device addresses; the library never allocates, frees,
+ *    copies to the host or synchronizes. All work is enqueued on `stream` in order.
+ *  - The caller owns every buffer. Workspaces are caller-allocated device memory of at least the
+ *    size the matching *_ws() function returns; their content need not be initialized and is
+ *    overwritten.
+ *  - Return value: MOE_OK, or an error code for conditions the host can check (arguments,
+ *    sizes, launch limits) -- nothing is enqueued then. A device fault surfaces at the caller's
+ *    next synchronization. Inputs holding NaN or Inf give undefined outputs.
+ *  - Calls that share no workspace or output may run concurrently on different streams.
+ *
+ * NVFP4 weight format (moe_sel_census.rs, its block constants; moe_union_probe.rs, its
+ * per-expert byte arithmetic): 64 weights per 36-byte block; bytes 0..3 hold the UE4M3 scales of
+ * weights 16j..16j+15 (j = 0..3), bytes 4..35 hold E2M1 codes, weight 2i in the low nibble and
+ * weight 2i+1 in the high nibble of byte 4+i. E2M1 is the OCP MX FP4 element type; UE4M3 is the
+ * OCP FP8 E4M3 type with its sign bit 0 (bytes 0x00..0x7E; others are undefined). A weight is
+ * code value * scale. A row holds in_f weights (in_f/64 blocks) for one output feature and is
+ * contiguous along the input features (moe_sk_repro.rs, its bank construction: row_bytes =
+ * in_f/64*36 and per-expert stride out_f*row_bytes).
+ */
+#ifndef MOE_NVFP4_H
+#define MOE_NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *moe_stream_t; /* a hipStream_t; NULL is the default stream */
+
+/* Status codes. */
+enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,  /* null pointer, negative T, k<1, E<1, k>4096, H or F not a multiple of 64,
+                        H not a multiple of 256, bank base or stride not a multiple of 16 bytes */
+    MOE_EWS = 2,     /* workspace smaller than the matching *_ws() size */
+    MOE_ESHAPE = 3,  /* a size beyond what this build can launch (see MOE_MAX_*) */
+    MOE_ELAUNCH = 4  /* the HIP runtime reported an error when the work was enqueued */
+};
+
+/* Path selection for moe_ffn_nvfp4. */
+enum {
+    MOE_PATH_AUTO = 0,          /* decode path for T <= 128, grouped-GEMM prefill path above */
+    MOE_PATH_DECODE = 1,        /* force the bandwidth-bound decode path */
+    MOE_PATH_PREFILL = 2        /* force the bf16-MFMA grouped-GEMM path */
+};
+
+#define MOE_MAX_EXPERTS 2048       /* E limit of the bucketing kernel */
+#define MOE_MAX_PAIRS (1 << 24)    /* T*k limit */
+#define MOE_MAX_HIDDEN 16384       /* H limit */
+#define MOE_MAX_FF 8192            /* F limit */
+
+/* One weight bank: expert e's rows start at base + e*expert_stride (bytes, device). */
+typedef struct {
+    const uint8_t *base;
+    int64_t expert_stride;
+} moe_bank;
+
+/*
+ * Workspace bytes moe_route_bucket needs for T tokens, k slots and E local experts.
+ */
+size_t moe_route_bucket_ws(int32_t T, int32_t k, int32_t E);
+
+/*
+ * Expert-first bucketing of the routed (token, expert) pairs (moe_sk_repro.rs: the host
+ * bucketing that builds ex_ids / ex_off / ex_pairs before the grouped calls, and the gather
+ * index csr_tok = pair / top_k).
+ *
+ *   topk_ids  (device) int32 [T*k], pair p = t*k + j names expert topk_ids[p].
+ *   expert_base        local expert of p is topk_ids[p] - expert_base; pairs whose local id is
+ *                      outside [0, E) belong to another expert-parallel rank and are not routed.
+ *   offsets   (device, out) int32 [E+1]: offsets[e] = number of local pairs with local expert
+ *                      < e; offsets[E] = number of local pairs.
+ *   pair_ids  (device, out) int32 [T*k]: positions [offsets[e], offsets[e+1]) list the pairs of
+ *                      expert e in ascending p (stable); positions [offsets[E], T*k) list the
+ *                      non-local pairs in ascending p.
+ *   active    (device, out) int32 [E]: the first n_active entries are the non-empty local
+ *                      experts in ascending order; the rest are unspecified.
+ *   counts    (device, out) int32 [2]: n_active, n_nonlocal.
+ *   ws, ws_bytes (device) scratch of at least moe_route_bucket_ws(T, k, E) bytes.
+ *
+ * Bit-exact: outputs depend only on topk_ids. T = 0 is valid (offsets all 0, counts 0).
+ * Errors: MOE_EINVAL (null pointer, T<0, k<1, E<1), MOE_ESHAPE (E > MOE_MAX_EXPERTS or
+ * T*k > MOE_MAX_PAIRS), MOE_EWS, MOE_ELAUNCH.
+ */
+int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t expert_base,
+                     int32_t *offsets, int32_t *pair_ids, int32_t *active, int32_t *counts,
+                     void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * Workspace bytes moe_ffn_nvfp4 needs (for any path).
+ */
+size_t moe_ffn_nvfp4_ws(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
+
+/*
+ * The routed FFN over the CSR that moe_route_bucket wrote (moe_union_probe.rs: the fused
+ * gate/up + SiLU and down kernels it prices, reading each distinct expert's weights once per
+ * call; moe_sk_repro.rs: the gate, up and down grouped calls of a prefill layer).
+ *
+ *   x         (device) bf16 bit patterns [T, H], row-major.
+ *   topk_w    (device) fp32 [T*k] router weights, used as given.
+ *   offsets, pair_ids, active, counts  (device) exactly as moe_route_bucket wrote them for the
+ *                      same topk_ids, T, k, E.
+ *   gate, up  rows of H weights: expert e's gate row o (o < F) starts at
+ *                      gate.base + e*gate.expert_stride + o*(H/64*36); likewise up. A fused
+ *                      gate_up bank [E, 2F, H] with gate rows first is gate = {B, 2F*rb},
+ *                      up = {B + F*rb, 2F*rb}, rb = H/64*36.
+ *   down      rows of F weights: expert e's down row r (r < H) starts at
+ *                      down.base + e*down.expert_stride + r*(F/64*36).
+ *   y         (device, out) fp32 [T, H], fully overwritten; a token with no local slot gets 0.
+ *   path      MOE_PATH_AUTO / MOE_PATH_DECODE / MOE_PATH_PREFILL.
+ *   ws, ws_bytes (device) scratch of at least moe_ffn_nvfp4_ws(T, k, E, H, F) bytes.
+ *
+ * Deterministic: the same inputs give bit-identical y on every call (the combine sums each
+ * token's slots in ascending j in fp32, with no atomics).
+ * Errors: MOE_EINVAL, MOE_ESHAPE (H > MOE_MAX_HIDDEN, F > MOE_MAX_FF, E > MOE_MAX_EXPERTS,
+ * T*k > MOE_MAX_PAIRS), MOE_EWS, MOE_ELAUNCH. T = 0 is a valid no-op.
+ */
+int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets,
+                  const int32_t *pair_ids, const int32_t *active, const int32_t *counts,
+                  moe_bank gate, moe_bank up, moe_bank down, int32_t T, int32_t k, int32_t E,
+                  int32_t H, int32_t F, float *y, int32_t path, void *ws, size_t ws_bytes,
+                  moe_stream_t stream);
+
+/* Name of a status code ("MOE_OK", ...); never NULL. */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_NVFP4_H */

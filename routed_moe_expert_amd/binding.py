@@ -1,0 +1,107 @@
+"""ctypes binding of libmoe_nvfp4.so: same entry points as include/moe_nvfp4.h.
+
+Argument marshalling only: tensors become device pointers, the stream becomes a hipStream_t.
+Every step of the layer runs in the library's HIP kernels. Importing this module fails loudly
+when the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
+
+MOE_OK, MOE_EINVAL, MOE_EWS, MOE_ESHAPE, MOE_ELAUNCH = 0, 1, 2, 3, 4
+MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {moe_status_str(status)} ({status})")
+        self.status = status
+
+
+class moe_bank(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python routed_moe_expert_amd/build.py` (hipcc, gfx950)")
+    l = ctypes.CDLL(LIB_PATH)
+    i32, sz, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    l.moe_route_bucket_ws.restype = sz
+    l.moe_route_bucket_ws.argtypes = [i32, i32, i32]
+    l.moe_route_bucket.restype = ctypes.c_int
+    l.moe_route_bucket.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+    l.moe_ffn_nvfp4_ws.restype = sz
+    l.moe_ffn_nvfp4_ws.argtypes = [i32, i32, i32, i32, i32]
+    l.moe_ffn_nvfp4.restype = ctypes.c_int
+    l.moe_ffn_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
+                                i32, i32, i32, i32, i32, vp, i32, vp, sz, vp]
+    l.moe_status_str.restype = ctypes.c_char_p
+    l.moe_status_str.argtypes = [ctypes.c_int]
+    return l
+
+
+lib = _load()
+
+
+def _ptr(t) -> int:
+    """Device address of a tensor (or an int address / None)."""
+    if t is None:
+        return 0
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int, raise_on_error: bool) -> int:
+    if status != MOE_OK and raise_on_error:
+        raise MoeError(fn, status)
+    return status
+
+
+def moe_status_str(status: int) -> str:
+    return lib.moe_status_str(int(status)).decode()
+
+
+def moe_route_bucket_ws(T: int, k: int, E: int) -> int:
+    return int(lib.moe_route_bucket_ws(T, k, E))
+
+
+def moe_ffn_nvfp4_ws(T: int, k: int, E: int, H: int, F: int) -> int:
+    return int(lib.moe_ffn_nvfp4_ws(T, k, E, H, F))
+
+
+def moe_route_bucket(topk_ids, T: int, k: int, E: int, expert_base: int, offsets, pair_ids,
+                     active, counts, ws=None, ws_bytes: int = 0, stream=None,
+                     raise_on_error: bool = True) -> int:
+    st = lib.moe_route_bucket(_ptr(topk_ids), T, k, E, expert_base, _ptr(offsets), _ptr(pair_ids),
+                              _ptr(active), _ptr(counts), _ptr(ws), ws_bytes, _stream(stream))
+    return _check("moe_route_bucket", st, raise_on_error)
+
+
+def bank(base, expert_stride: int, byte_offset: int = 0) -> moe_bank:
+    """A moe_bank for a device tensor (or address) plus an optional byte offset."""
+    return moe_bank(_ptr(base) + byte_offset if base is not None else None, int(expert_stride))
+
+
+def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, up: moe_bank,
+                  down: moe_bank, T: int, k: int, E: int, H: int, F: int, y, path: int = MOE_PATH_AUTO,
+                  ws=None, ws_bytes: int = 0, stream=None, raise_on_error: bool = True) -> int:
+    st = lib.moe_ffn_nvfp4(_ptr(x), _ptr(topk_w), _ptr(offsets), _ptr(pair_ids), _ptr(active),
+                           _ptr(counts), gate, up, down, T, k, E, H, F, _ptr(y), path, _ptr(ws),
+                           ws_bytes, _stream(stream))
+    return _check("moe_ffn_nvfp4", st, raise_on_error)

@@ -1,0 +1,87 @@
+// The C ABI of libmoe_nvfp4: argument validation, workspace sizing and path dispatch.
+// Every check here runs on the host before anything is enqueued.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool bank_ok(const moe_bank &b) {
+    return b.base != nullptr && aligned(b.base, 16) && b.expert_stride >= 0 &&
+           b.expert_stride % 16 == 0;
+}
+
+int check_common(int32_t T, int32_t k, int32_t E) {
+    if (T < 0 || k < 1 || E < 1 || k > 4096) return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS || (int64_t)T * k > MOE_MAX_PAIRS) return MOE_ESHAPE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_route_bucket_ws(int32_t T, int32_t k, int32_t E) {
+    (void)T;
+    (void)k;
+    (void)E;
+    return 0;  // the bucketing kernel works in LDS only
+}
+
+int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t expert_base,
+                     int32_t *offsets, int32_t *pair_ids, int32_t *active, int32_t *counts,
+                     void *ws, size_t ws_bytes, moe_stream_t stream) {
+    int st = check_common(T, k, E);
+    if (st != MOE_OK) return st;
+    if (!offsets || !active || !counts) return MOE_EINVAL;
+    if (T > 0 && (!topk_ids || !pair_ids)) return MOE_EINVAL;
+    if (ws_bytes < moe_route_bucket_ws(T, k, E)) return MOE_EWS;
+    (void)ws;
+    return launch_bucket(topk_ids, T, k, E, expert_base, offsets, pair_ids, active, counts,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t moe_ffn_nvfp4_ws(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
+    if (T < 0 || k < 1 || E < 1 || H < 1 || F < 1) return 0;
+    return std::max(decode_ws_bytes(T, k, E, H, F), prefill_ws_bytes(T, k, E, H, F));
+}
+
+int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets,
+                  const int32_t *pair_ids, const int32_t *active, const int32_t *counts,
+                  moe_bank gate, moe_bank up, moe_bank down, int32_t T, int32_t k, int32_t E,
+                  int32_t H, int32_t F, float *y, int32_t path, void *ws, size_t ws_bytes,
+                  moe_stream_t stream) {
+    int st = check_common(T, k, E);
+    if (st != MOE_OK) return st;
+    if (H < 256 || F < 64 || H % 256 || F % 64) return MOE_EINVAL;
+    if (H > MOE_MAX_HIDDEN || F > MOE_MAX_FF) return MOE_ESHAPE;
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!x || !topk_w || !offsets || !pair_ids || !active || !counts || !y || !ws)
+        return MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return MOE_EINVAL;
+    if (!bank_ok(gate) || !bank_ok(up) || !bank_ok(down)) return MOE_EINVAL;
+    if (ws_bytes < moe_ffn_nvfp4_ws(T, k, E, H, F)) return MOE_EWS;
+    FfnArgs a{x, topk_w, offsets, pair_ids, active, counts, gate, up, down, T, k, E, H, F, y,
+              ws, ws_bytes};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (path == MOE_PATH_AUTO) path = (T <= 128) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    return path == MOE_PATH_DECODE ? launch_decode(a, s) : launch_prefill(a, s);
+}
+
+const char *moe_status_str(int status) {
+    switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL";
+    case MOE_EWS: return "MOE_EWS";
+    case MOE_ESHAPE: return "MOE_ESHAPE";
+    case MOE_ELAUNCH: return "MOE_ELAUNCH";
+    default: return "MOE_UNKNOWN";
+    }
+}
+
+}  // extern "C"

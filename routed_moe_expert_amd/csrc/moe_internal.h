@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libmoe_nvfp4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_nvfp4.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+constexpr int kBlockWeights = 64;  // NVFP4: weights per block
+constexpr int kBlockBytes = 36;    // NVFP4: 4 UE4M3 scale bytes + 32 code bytes
+constexpr int kGroup = 16;         // weights per UE4M3 scale
+
+inline int64_t row_bytes(int64_t in_f) { return in_f / kBlockWeights * kBlockBytes; }
+
+// UE4M3 scale byte -> fp32, exact for all 127 finite codes. Shifting the 7 value bits into the
+// fp32 exponent/mantissa position gives value * 2^-120 for normal codes and, as an fp32 denormal,
+// m * 2^-129 for subnormal codes; a multiply by 2^120 (denormals are preserved) restores both.
+__device__ __forceinline__ float ue4m3_to_f32(uint32_t byte) {
+    return __uint_as_float(byte << 20) * 0x1p120f;
+}
+
+// Two E2M1 codes of byte `sel` of `w` -> two bf16 (low nibble first), exact. The gfx950 scaled
+// conversion applies only the exponent of its scale operand, so the scale is 1.0 here and the
+// UE4M3 group scale is applied by the caller.
+template <int sel>
+__device__ __forceinline__ bf16x2_t e2m1x2_to_bf16(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, sel);
+}
+template <int sel>
+__device__ __forceinline__ f32x2_t e2m1x2_to_f32(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, sel);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    bf16x2_t va = __builtin_bit_cast(bf16x2_t, a);
+    bf16x2_t vb = __builtin_bit_cast(bf16x2_t, b);
+    return __builtin_amdgcn_fdot2_f32_bf16(va, vb, c, false);
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ----------------------------------------------------------------------------- host launchers
+// Each returns a MOE_* status; arguments have been validated by the ABI layer.
+
+int launch_bucket(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t expert_base,
+                  int32_t *offsets, int32_t *pair_ids, int32_t *active, int32_t *counts,
+                  hipStream_t s);
+
+struct FfnArgs {
+    const uint16_t *x;
+    const float *w;
+    const int32_t *offsets, *pair_ids, *active, *counts;
+    moe_bank gate, up, down;
+    int32_t T, k, E, H, F;
+    float *y;
+    void *ws;
+    size_t ws_bytes;
+};
+
+size_t decode_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
+size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
+int launch_decode(const FfnArgs &a, hipStream_t s);
+int launch_prefill(const FfnArgs &a, hipStream_t s);
+
+// y[t] = sum_j w[t,j] * ypair[pos[t*k+j]] over local slots; pos[p] >= n_local means non-local.
+int launch_combine(const float *w, const int32_t *pos, const int32_t *offsets, int32_t E,
+                   const float *ypair, int32_t T, int32_t k, int32_t H, float *y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,93 @@
+"""Helpers for the GPU tests: upload a generated case, run the layer through the C ABI,
+compare against the fp64 oracle to the parity bound."""
+import numpy as np
+import torch
+
+import routed_moe_expert_amd as moe
+
+REL_RMS_BOUND = 1e-3    # relative RMS of (y_gpu - y_oracle) over RMS(y_oracle)
+MAX_ABS_BOUND = 2e-3    # max |y_gpu - y_oracle| over RMS(y_oracle)
+
+
+def to_dev(a, dtype=None):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    t = torch.from_numpy(a)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+class DeviceCase:
+    """A generated case resident on the GPU, with every output and workspace preallocated."""
+
+    def __init__(self, case: dict):
+        self.case = case
+        self.T, self.k, self.E, self.H, self.F = case["T"], case["k"], case["E"], case["H"], case["F"]
+        self.base = case.get("expert_base", 0)
+        P = self.T * self.k
+        self.ids = to_dev(case["ids"].astype(np.int32).reshape(-1))
+        self.w = to_dev(case["w"].astype(np.float32).reshape(-1))
+        self.x = to_dev(case["x"])
+        H, F = self.H, self.F
+        rbh, rbf = H // 64 * 36, F // 64 * 36
+        if "gate_up" in case:
+            self.gu = to_dev(case["gate_up"])
+            self.gate = moe.bank(self.gu, 2 * F * rbh)
+            self.up = moe.bank(self.gu, 2 * F * rbh, F * rbh)
+        else:
+            self.g = to_dev(case["gate"])
+            self.u = to_dev(case["up"])
+            self.gate = moe.bank(self.g, F * rbh)
+            self.up = moe.bank(self.u, F * rbh)
+        self.d = to_dev(case["down"])
+        self.down = moe.bank(self.d, H * rbf)
+        dev = self.ids.device
+        self.offsets = torch.empty(self.E + 1, dtype=torch.int32, device=dev)
+        self.pair_ids = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
+        self.active = torch.empty(self.E, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(2, dtype=torch.int32, device=dev)
+        self.bws = moe.moe_route_bucket_ws(self.T, self.k, self.E)
+        self.bucket_ws = torch.empty(max(self.bws, 1), dtype=torch.uint8, device=dev)
+        self.ws_bytes = moe.moe_ffn_nvfp4_ws(self.T, self.k, self.E, H, F)
+        self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
+        self.y = torch.empty(max(self.T, 1), H, dtype=torch.float32, device=dev)
+
+    def bucket(self, stream=None):
+        moe.moe_route_bucket(self.ids, self.T, self.k, self.E, self.base, self.offsets,
+                             self.pair_ids, self.active, self.counts, self.bucket_ws, self.bws,
+                             stream=stream)
+
+    def ffn(self, path=moe.MOE_PATH_AUTO, stream=None):
+        moe.moe_ffn_nvfp4(self.x, self.w, self.offsets, self.pair_ids, self.active, self.counts,
+                          self.gate, self.up, self.down, self.T, self.k, self.E, self.H, self.F,
+                          self.y, path, self.ws, self.ws_bytes, stream=stream)
+
+    def run(self, path=moe.MOE_PATH_AUTO):
+        self.bucket()
+        self.ffn(path)
+        torch.cuda.synchronize()
+        return self.y[: self.T].cpu().numpy()
+
+    def bucket_result(self):
+        torch.cuda.synchronize()
+        return (self.offsets.cpu().numpy(), self.pair_ids.cpu().numpy()[: self.T * self.k],
+                self.active.cpu().numpy(), self.counts.cpu().numpy())
+
+
+def parity(y: np.ndarray, ref: np.ndarray):
+    """(relative RMS error, max abs error / RMS(ref))."""
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.asarray(y, dtype=np.float64) - ref
+    if rms == 0.0:
+        return (0.0 if not np.any(err) else np.inf), (0.0 if not np.any(err) else np.inf)
+    return float(np.sqrt(np.mean(err ** 2)) / rms), float(np.abs(err).max() / rms)
+
+
+def assert_parity(y, ref, what=""):
+    rel, mx = parity(y, ref)
+    assert rel <= REL_RMS_BOUND and mx <= MAX_ABS_BOUND, \
+        f"{what}: relRMS {rel:.3e} (bound {REL_RMS_BOUND}), max abs/RMS {mx:.3e} (bound {MAX_ABS_BOUND})"
+    return rel, mx

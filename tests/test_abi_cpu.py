@@ -1,0 +1,100 @@
+"""The C ABI without a GPU: the library loads, exports every declared entry point, sizes its
+workspaces, and rejects bad arguments on the host before anything is enqueued."""
+import os
+import re
+
+import pytest
+
+import routed_moe_expert_amd as moe
+from routed_moe_expert_amd.binding import moe_bank
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000      # a 256-aligned non-null address; never dereferenced on these paths
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", fn)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(moe_\w+)\s*\(", src))
+    return names
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert {"moe_route_bucket", "moe_ffn_nvfp4", "moe_route_bucket_ws", "moe_ffn_nvfp4_ws",
+            "moe_status_str"} <= names
+    for n in names:
+        assert hasattr(moe.lib, n), n
+
+
+def test_status_strings():
+    assert moe.moe_status_str(0) == "MOE_OK"
+    assert moe.moe_status_str(moe.MOE_EWS) == "MOE_EWS"
+    assert moe.moe_status_str(99) == "MOE_UNKNOWN"
+
+
+def test_workspace_sizes():
+    T, k, E, H, F = 6, 10, 512, 2560, 640
+    P = T * k
+    ws = moe.moe_ffn_nvfp4_ws(T, k, E, H, F)
+    assert ws >= P * 4 + P * F * 4 + P * H * 4
+    assert moe.moe_ffn_nvfp4_ws(4096, 8, 288, 4096, 1280) >= 32768 * 4096 * 4
+    assert moe.moe_route_bucket_ws(T, k, E) >= 0
+    assert moe.moe_ffn_nvfp4_ws(-1, 1, 1, 256, 64) == 0
+
+
+def _bank(addr=FAKE, stride=4096):
+    return moe_bank(addr, stride)
+
+
+def _ffn(**over):
+    a = dict(x=FAKE, topk_w=FAKE, offsets=FAKE, pair_ids=FAKE, active=FAKE, counts=FAKE,
+             gate=_bank(), up=_bank(), down=_bank(), T=4, k=2, E=8, H=256, F=64, y=FAKE,
+             path=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    return moe.moe_ffn_nvfp4(a["x"], a["topk_w"], a["offsets"], a["pair_ids"], a["active"],
+                             a["counts"], a["gate"], a["up"], a["down"], a["T"], a["k"], a["E"],
+                             a["H"], a["F"], a["y"], a["path"], a["ws"], a["ws_bytes"], stream=0,
+                             raise_on_error=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(x=0), moe.MOE_EINVAL), (dict(y=0), moe.MOE_EINVAL), (dict(ws=0), moe.MOE_EINVAL),
+    (dict(T=-1), moe.MOE_EINVAL), (dict(k=0), moe.MOE_EINVAL), (dict(E=0), moe.MOE_EINVAL),
+    (dict(H=320), moe.MOE_EINVAL), (dict(F=96), moe.MOE_EINVAL), (dict(path=7), moe.MOE_EINVAL),
+    (dict(gate=_bank(FAKE + 4)), moe.MOE_EINVAL), (dict(down=_bank(stride=100)), moe.MOE_EINVAL),
+    (dict(up=_bank(0)), moe.MOE_EINVAL), (dict(x=FAKE + 2), moe.MOE_EINVAL),
+    (dict(ws=FAKE + 16), moe.MOE_EINVAL),
+    (dict(E=4096), moe.MOE_ESHAPE), (dict(H=1 << 15), moe.MOE_ESHAPE),
+    (dict(ws_bytes=16), moe.MOE_EWS),
+    (dict(T=0), moe.MOE_OK), (dict(T=0, x=0, y=0), moe.MOE_OK),
+])
+def test_ffn_host_checks(over, status):
+    assert _ffn(**over) == status
+
+
+def _bucket(**over):
+    a = dict(ids=FAKE, T=4, k=2, E=8, base=0, offsets=FAKE, pair_ids=FAKE, active=FAKE,
+             counts=FAKE, ws=FAKE, ws_bytes=0)
+    a.update(over)
+    return moe.moe_route_bucket(a["ids"], a["T"], a["k"], a["E"], a["base"], a["offsets"],
+                                a["pair_ids"], a["active"], a["counts"], a["ws"], a["ws_bytes"],
+                                stream=0, raise_on_error=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ids=0), moe.MOE_EINVAL), (dict(offsets=0), moe.MOE_EINVAL),
+    (dict(pair_ids=0), moe.MOE_EINVAL), (dict(counts=0), moe.MOE_EINVAL),
+    (dict(T=-3), moe.MOE_EINVAL), (dict(k=0), moe.MOE_EINVAL), (dict(E=0), moe.MOE_EINVAL),
+    (dict(E=5000), moe.MOE_ESHAPE), (dict(T=1 << 22, k=8), moe.MOE_ESHAPE),
+])
+def test_bucket_host_checks(over, status):
+    assert _bucket(**over) == status
+
+
+def test_errors_raise_by_default():
+    with pytest.raises(moe.MoeError):
+        moe.moe_route_bucket(0, 4, 2, 8, 0, 0, 0, 0, 0, stream=0)

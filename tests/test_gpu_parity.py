@@ -1,0 +1,161 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bucketing must match bit for bit; the FFN output must be within relRMS <= 1e-3 and
+max abs <= 2e-3 * RMS(y) of the oracle; repeated calls must be bit-identical.
+"""
+import hashlib
+
+import numpy as np
+import pytest
+import torch
+
+import gen
+import oracle
+import routed_moe_expert_amd as moe
+from gpu_util import DeviceCase, assert_parity
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _print_case(tag, **kw):
+    print(f"[case] {tag} " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+def _check_bucket(dc: DeviceCase):
+    case = dc.case
+    off, pairs, act, cnt = dc.bucket_result()
+    r_off, r_pairs, r_act, r_nact, r_non = oracle.route_bucket(case["ids"], dc.E, dc.base)
+    assert np.array_equal(off, r_off)
+    n_local = int(r_off[-1])
+    assert np.array_equal(pairs[:n_local], r_pairs)
+    flat = case["ids"].reshape(-1).astype(np.int64) - dc.base
+    nonlocal_pairs = np.nonzero((flat < 0) | (flat >= dc.E))[0]
+    assert np.array_equal(pairs[n_local:], nonlocal_pairs)
+    assert cnt[0] == r_nact and cnt[1] == r_non
+    assert np.array_equal(act[:r_nact], r_act)
+
+
+# ----------------------------------------------------------------------------------- bucketing
+
+@pytest.mark.parametrize("T,k,E,base,frac", [
+    (1, 10, 64, 0, 0.0), (6, 10, 512, 0, 0.0), (7, 3, 5, 0, 0.0), (50, 4, 16, 100, 0.3),
+    (9, 2, 1, 0, 0.0), (200, 8, 288, 0, 0.5), (1000, 8, 2048, 0, 0.1), (3, 4, 7, 0, 1.0),
+    (0, 4, 8, 0, 0.0), (513, 2, 3, 0, 0.0)])
+def test_bucket_random(T, k, E, base, frac):
+    _print_case("bucket_random", T=T, k=k, E=E, base=base, frac=frac)
+    case = gen.make_random_case(T * 7 + k + E, T, k, E, 256, 64, nonlocal_frac=frac,
+                                expert_base=base)
+    dc = DeviceCase(case)
+    dc.bucket()
+    _check_bucket(dc)
+
+
+@pytest.mark.parametrize("name,T,U", [("tiny_decode", 1, None), ("verify_chunk", 6, 10),
+                                      ("verify_chunk", 6, 60), ("e256_plateau", 128, None),
+                                      ("skewed_prefill", 512, None), ("skewed_prefill", 4096, None)])
+def test_bucket_workloads(name, T, U):
+    _print_case("bucket_workload", name=name, T=T, U=U)
+    w = gen.WORKLOADS[name]
+    ids, wts = gen.make_routing(name, T, U)
+    case = dict(T=T, k=w["k"], E=w["E"], H=256, F=64, ids=ids, w=wts,
+                x=np.zeros((T, 256), np.uint16), gate=np.zeros((w["E"], 64, 144), np.uint8),
+                up=np.zeros((w["E"], 64, 144), np.uint8), down=np.zeros((w["E"], 256, 36), np.uint8))
+    dc = DeviceCase(case)
+    dc.bucket()
+    _check_bucket(dc)
+
+
+# ----------------------------------------------------------------------------- FFN: decode path
+
+SMALL = [
+    # seed, T, k, E, H, F, scales, nonlocal fraction, expert base, fused
+    (1, 1, 1, 1, 256, 64, "all", 0.0, 0, False),
+    (2, 5, 2, 3, 256, 128, "all", 0.0, 0, True),
+    (3, 17, 4, 8, 512, 192, "all", 0.2, 5, False),
+    (4, 40, 2, 2, 256, 64, "pow2", 0.0, 0, False),     # > 8 tokens per expert: token chunks
+    (5, 3, 6, 4, 768, 128, "all", 0.5, 0, True),       # duplicates within tokens
+    (6, 12, 3, 16, 256, 320, "all", 0.0, 0, False),
+]
+
+
+@pytest.mark.parametrize("seed,T,k,E,H,F,scales,frac,base,fused", SMALL)
+def test_decode_small(seed, T, k, E, H, F, scales, frac, base, fused):
+    _print_case("decode_small", seed=seed, T=T, k=k, E=E, H=H, F=F, frac=frac)
+    case = gen.make_random_case(seed, T, k, E, H, F, scales=scales, nonlocal_frac=frac,
+                                expert_base=base, fused=fused)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_DECODE)
+    _check_bucket(dc)
+    ref = oracle.ffn_union(case)
+    assert_parity(y, ref, "decode_small")
+
+
+_WL = {}
+
+
+def _workload(name, T, U=None):
+    key = (name, T, U)
+    if key not in _WL:
+        _WL.clear()
+        _WL[key] = gen.make_workload(name, T, U=U)
+    return _WL[key]
+
+
+@pytest.mark.parametrize("name,T,U,n_check", [
+    ("tiny_decode", 1, None, None), ("verify_chunk", 6, 10, None), ("verify_chunk", 6, 30, None),
+    ("verify_chunk", 6, 60, None), ("e256_plateau", 16, None, None),
+    ("e256_plateau", 128, None, 12)])
+def test_decode_workloads(name, T, U, n_check):
+    """Full-size decode workloads; the largest compares a sample of tokens one by one."""
+    _print_case("decode_workload", name=name, T=T, U=U)
+    case = _workload(name, T, U)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_DECODE)
+    _check_bucket(dc)
+    if n_check is None:
+        ref = oracle.ffn_per_slot(case)
+        assert_parity(y, ref, name)
+    else:
+        tok = np.random.default_rng(T).choice(T, size=n_check, replace=False)
+        tok[0] = T - 1
+        ref = oracle.ffn_per_slot(case, tokens=tok)
+        assert_parity(y[tok], ref, name)
+
+
+def test_decode_deterministic():
+    case = gen.make_random_case(31, 24, 4, 6, 512, 128, nonlocal_frac=0.1)
+    dc = DeviceCase(case)
+    hashes = set()
+    for _ in range(10):
+        y = dc.run(moe.MOE_PATH_DECODE)
+        hashes.add(hashlib.sha256(y.tobytes()).hexdigest())
+    assert len(hashes) == 1
+
+
+def test_tokens_without_local_slots_get_zero():
+    case = gen.make_random_case(32, 6, 3, 4, 256, 64)
+    ids = case["ids"].copy()
+    ids[2, :] = 77              # token 2: every slot on another rank
+    ids[4, :] = -5
+    case["ids"] = ids
+    dc = DeviceCase(case)
+    dc.y.fill_(np.nan)
+    y = dc.run(moe.MOE_PATH_DECODE)
+    assert np.all(y[2] == 0) and np.all(y[4] == 0)
+    assert_parity(y, oracle.ffn_union(case), "nonlocal rows")
+
+
+def test_zero_tokens_is_noop():
+    case = gen.make_random_case(33, 0, 2, 3, 256, 64)
+    dc = DeviceCase(case)
+    dc.bucket()
+    off, _, _, cnt = dc.bucket_result()
+    assert np.all(off == 0) and np.all(cnt == 0)
+    assert moe.moe_ffn_nvfp4(dc.x, dc.w, dc.offsets, dc.pair_ids, dc.active, dc.counts, dc.gate,
+                             dc.up, dc.down, 0, 2, 3, 256, 64, dc.y, 0, dc.ws, dc.ws_bytes) == moe.MOE_OK
