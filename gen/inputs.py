@@ -107,6 +107,18 @@ def route_union(seed: int, T: int, k: int, E: int, U: int) -> np.ndarray:
     return pi[p % U].astype(np.int32).reshape(T, k)
 
 
+def route_union_rotated(seed: int, T: int, k: int, E: int, U: int, variant: int) -> np.ndarray:
+    """Like route_union, with the U-subset taken as the variant-th window of U experts of one
+    seeded permutation (windows wrap around E), so consecutive variants touch disjoint experts.
+    Benchmarks rotate variants so that an expert's bytes are not still cached from a recent call."""
+    if not (k <= U <= E):
+        raise ValueError("need k <= U <= E")
+    perm = rng_for(seed, S_PERM, 1 << 19).permutation(E)
+    pi = perm[(variant * U + np.arange(U)) % E]
+    p = np.arange(T * k)
+    return pi[p % U].astype(np.int32).reshape(T, k)
+
+
 def route_cyclic(seed: int, T: int, k: int, E: int) -> np.ndarray:
     """Uniform routing that activates every expert as soon as T*k >= E:
     slot (t,j) -> pi[(t*k+j) mod E], pi a seeded permutation of the E experts."""

@@ -138,6 +138,29 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
                   int32_t H, int32_t F, float *y, int32_t path, void *ws, size_t ws_bytes,
                   moe_stream_t stream);
 
+/*
+ * Diagnostics: timing of one kernel of the layer with caller-created HIP events.
+ * After this call, the next n_events launches of kernel `kernel_id` (a MOE_KERNEL_* value) are
+ * bracketed by hipEventRecord(start_events[i]) / hipEventRecord(stop_events[i]) on the launch
+ * stream. kernel_id = MOE_KERNEL_NONE (or n_events = 0) switches this off. The event arrays
+ * (host arrays of hipEvent_t) must stay valid while it is on. Process-wide state, not thread
+ * safe; meant for benchmarks. Returns MOE_OK, or MOE_EINVAL for a bad id or null arrays.
+ */
+enum {
+    MOE_KERNEL_NONE = 0,
+    MOE_KERNEL_BUCKET = 1,       /* moe_route_bucket's kernel */
+    MOE_KERNEL_GU_DECODE = 2,    /* decode gate/up + SiLU */
+    MOE_KERNEL_DN_DECODE = 3,    /* decode down projection */
+    MOE_KERNEL_COMBINE = 4,      /* ordered router-weighted combine */
+    MOE_KERNEL_SCHEDULE = 5,     /* prefill tile schedule */
+    MOE_KERNEL_GU_PREFILL = 6,   /* prefill gate/up grouped GEMM */
+    MOE_KERNEL_DN_PREFILL = 7    /* prefill down grouped GEMM */
+};
+int moe_profile_kernel(int32_t kernel_id, void *const *start_events, void *const *stop_events,
+                       int32_t n_events);
+/* Number of launches recorded since the last moe_profile_kernel call. */
+int32_t moe_profile_count(void);
+
 /* Name of a status code ("MOE_OK", ...); never NULL. */
 const char *moe_status_str(int status);
 

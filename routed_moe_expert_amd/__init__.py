@@ -3,6 +3,10 @@
 The compute lives in libmoe_nvfp4.so (hand-written HIP kernels behind a C ABI, declared in
 include/moe_nvfp4.h). This package only marshals arguments to it; see binding.py.
 """
-from .binding import (MOE_EINVAL, MOE_ELAUNCH, MOE_ESHAPE, MOE_EWS, MOE_OK, MOE_PATH_AUTO, bank,
-                      MOE_PATH_DECODE, MOE_PATH_PREFILL, MoeError, lib, moe_ffn_nvfp4,
-                      moe_ffn_nvfp4_ws, moe_route_bucket, moe_route_bucket_ws, moe_status_str)
+from .binding import (MOE_EINVAL, MOE_ELAUNCH, MOE_ESHAPE, MOE_EWS, MOE_KERNEL_BUCKET,
+                      MOE_KERNEL_COMBINE, MOE_KERNEL_DN_DECODE, MOE_KERNEL_DN_PREFILL,
+                      MOE_KERNEL_GU_DECODE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_NONE,
+                      MOE_KERNEL_SCHEDULE, MOE_OK, MOE_PATH_AUTO, MOE_PATH_DECODE,
+                      MOE_PATH_PREFILL, MoeError, bank, lib, moe_ffn_nvfp4, moe_ffn_nvfp4_ws,
+                      moe_profile_count, moe_profile_kernel, moe_route_bucket,
+                      moe_route_bucket_ws, moe_status_str)

@@ -14,6 +14,8 @@ LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EWS, MOE_ESHAPE, MOE_ELAUNCH = 0, 1, 2, 3, 4
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+(MOE_KERNEL_NONE, MOE_KERNEL_BUCKET, MOE_KERNEL_GU_DECODE, MOE_KERNEL_DN_DECODE, MOE_KERNEL_COMBINE,
+ MOE_KERNEL_SCHEDULE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_DN_PREFILL) = range(8)
 
 
 class MoeError(RuntimeError):
@@ -41,6 +43,10 @@ def _load():
     l.moe_ffn_nvfp4.restype = ctypes.c_int
     l.moe_ffn_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
                                 i32, i32, i32, i32, i32, vp, i32, vp, sz, vp]
+    l.moe_profile_kernel.restype = ctypes.c_int
+    l.moe_profile_kernel.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
+    l.moe_profile_count.restype = i32
+    l.moe_profile_count.argtypes = []
     l.moe_status_str.restype = ctypes.c_char_p
     l.moe_status_str.argtypes = [ctypes.c_int]
     return l
@@ -105,3 +111,19 @@ def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, 
                            _ptr(counts), gate, up, down, T, k, E, H, F, _ptr(y), path, _ptr(ws),
                            ws_bytes, _stream(stream))
     return _check("moe_ffn_nvfp4", st, raise_on_error)
+
+
+def moe_profile_kernel(kernel_id: int, start_events, stop_events) -> int:
+    """start_events / stop_events: sequences of raw hipEvent_t handles (ints)."""
+    n = len(start_events)
+    arr = ctypes.c_void_p * max(n, 1)
+    _profile_keep[:] = [arr(*start_events), arr(*stop_events)]
+    st = lib.moe_profile_kernel(kernel_id, _profile_keep[0], _profile_keep[1], n)
+    return _check("moe_profile_kernel", st, True)
+
+
+def moe_profile_count() -> int:
+    return int(lib.moe_profile_count())
+
+
+_profile_keep = []

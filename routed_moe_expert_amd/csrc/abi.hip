@@ -6,6 +6,10 @@
 
 using namespace moe;
 
+namespace moe {
+KernelProfile g_profile;
+}
+
 namespace {
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -72,6 +76,22 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
     if (path == MOE_PATH_AUTO) path = (T <= 128) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
     return path == MOE_PATH_DECODE ? launch_decode(a, s) : launch_prefill(a, s);
 }
+
+int moe_profile_kernel(int32_t kernel_id, void *const *start_events, void *const *stop_events,
+                       int32_t n_events) {
+    if (kernel_id < MOE_KERNEL_NONE || kernel_id > MOE_KERNEL_DN_PREFILL || n_events < 0)
+        return MOE_EINVAL;
+    if (kernel_id != MOE_KERNEL_NONE && n_events > 0 && (!start_events || !stop_events))
+        return MOE_EINVAL;
+    g_profile.kernel = n_events > 0 ? kernel_id : MOE_KERNEL_NONE;
+    g_profile.starts = reinterpret_cast<hipEvent_t *>(const_cast<void **>(start_events));
+    g_profile.stops = reinterpret_cast<hipEvent_t *>(const_cast<void **>(stop_events));
+    g_profile.n = n_events;
+    g_profile.next = 0;
+    return MOE_OK;
+}
+
+int32_t moe_profile_count(void) { return g_profile.next; }
 
 const char *moe_status_str(int status) {
     switch (status) {

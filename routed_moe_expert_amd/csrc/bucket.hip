@@ -2,13 +2,14 @@
 //
 // Computes what moe_sk_repro.rs's host bucketing computes (pairs pushed into per-expert lists in
 // ascending pair id, non-empty lists concatenated in ascending expert id, running-total offsets),
-// on the GPU, in one workgroup of 16 wave64s:
+// on the GPU, in one workgroup of 8 wave64s:
 //   1. LDS histogram of the local expert ids (non-local pairs counted in an extra bucket E);
 //   2. workgroup exclusive scans of the counts (offsets, cursors) and of the non-empty flags
 //      (the ascending active list);
-//   3. a stable scatter in chunks of 1024 consecutive pairs: inside a wave each pair's rank among
-//      equal keys comes from ballots (one pass per distinct key in the wave); across the 16 waves
-//      of a chunk the per-wave key counts kept in LDS give each wave its start; the cursors then
+//   3. a stable scatter in chunks of 512 consecutive pairs. Inside a wave, each lane ORs its bit
+//      into a per-wave 64-bit mask kept in LDS for its key; the mask's population below the lane
+//      is the lane's rank among equal keys (constant time, however many distinct keys). Across
+//      the 8 waves of a chunk the per-wave key counts give each wave its start; the cursors then
 //      advance by the chunk's counts.
 // The result depends only on the ids, so it is bit-exact and run-to-run identical.
 #include "moe_internal.h"
@@ -16,7 +17,7 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 // Exclusive scan of one int per thread over the workgroup; *total gets the sum.
@@ -29,7 +30,7 @@ __device__ int block_exclusive_scan(int v, int *wsum, int *total) {
         if (lane >= d) x += y;
     }
     if (lane == 63) wsum[wave] = x;
-    __syncthreads();
+    lds_barrier();
     if (wave == 0) {
         int s = lane < kWaves ? wsum[lane] : 0;
 #pragma unroll
@@ -39,10 +40,10 @@ __device__ int block_exclusive_scan(int v, int *wsum, int *total) {
         }
         if (lane < kWaves) wsum[lane] = s;
     }
-    __syncthreads();
+    lds_barrier();
     int before = wave ? wsum[wave - 1] : 0;
     *total = wsum[kWaves - 1];
-    __syncthreads();
+    lds_barrier();
     return before + x - v;
 }
 
@@ -50,24 +51,29 @@ __global__ __launch_bounds__(kThreads) void bucket_kernel(
     const int32_t *__restrict__ ids, int32_t P, int32_t E, int32_t expert_base,
     int32_t *__restrict__ offsets, int32_t *__restrict__ pair_ids, int32_t *__restrict__ active,
     int32_t *__restrict__ counts) {
-    extern __shared__ int32_t smem[];
+    extern __shared__ __attribute__((aligned(16))) int32_t smem[];
     const int NB = E + 1;                    // buckets 0..E-1 local experts, E = not local
     int32_t *cnt = smem;                     // [NB] counts, then cursors
     int32_t *wsum = cnt + NB;                // [32] scan scratch
-    uint8_t *wcnt = reinterpret_cast<uint8_t *>(wsum + 32);  // [kWaves][NB] per-wave key counts
+    uint32_t *tbl = reinterpret_cast<uint32_t *>(wsum + 32);  // [kWaves][NB][2] lane masks
+    uint8_t *wcnt = reinterpret_cast<uint8_t *>(tbl + 2 * kWaves * NB);  // [kWaves][NB]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    for (int i = tid; i < NB; i += kThreads) cnt[i] = 0;
-    for (int i = tid; i < kWaves * NB; i += kThreads) wcnt[i] = 0;
-    __syncthreads();
 
     auto key_of = [&](int p) -> int {
         int64_t e = (int64_t)ids[p] - expert_base;
         return (e >= 0 && e < E) ? (int)e : E;
     };
+    const int key0 = tid < P ? key_of(tid) : -1;  // the first chunk's keys stay in registers
 
-    for (int p = tid; p < P; p += kThreads) atomicAdd(&cnt[key_of(p)], 1);
-    __syncthreads();
+    for (int i = tid; i < NB; i += kThreads) cnt[i] = 0;
+    for (int i = tid; i < 2 * kWaves * NB; i += kThreads) tbl[i] = 0;
+    uint32_t *wcnt32 = reinterpret_cast<uint32_t *>(wcnt);   // kWaves*NB is a multiple of 4
+    for (int i = tid; i < kWaves * NB / 4; i += kThreads) wcnt32[i] = 0;
+    lds_barrier();
+
+    if (key0 >= 0) atomicAdd(&cnt[key0], 1);
+    for (int p = tid + kThreads; p < P; p += kThreads) atomicAdd(&cnt[key_of(p)], 1);
+    lds_barrier();
 
     // each thread owns a contiguous run of buckets
     const int per = (NB + kThreads - 1) / kThreads;
@@ -89,37 +95,37 @@ __global__ __launch_bounds__(kThreads) void bucket_kernel(
         run += c;
     }
     if (tid == 0) counts[0] = tot_flags;
-    __syncthreads();
+    lds_barrier();
 
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint32_t *my_tbl = tbl + 2 * wave * NB;
     for (int p0 = 0; p0 < P; p0 += kThreads) {
         const int p = p0 + tid;
-        const int key = p < P ? key_of(p) : -1;
-        uint64_t todo = __ballot(key >= 0);
+        const int key = p0 == 0 ? key0 : (p < P ? key_of(p) : -1);
+        if (key >= 0) atomicOr(&my_tbl[2 * key + (lane >> 5)], 1u << (lane & 31));
+        // the wave's own LDS operations complete in order; wait for them before reading back
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         int rank = 0, gsize = 0;
-        while (todo) {  // wave-uniform: one pass per distinct key in this wave
-            const int leader = __ffsll((unsigned long long)todo) - 1;
-            const int lk = __shfl(key, leader, 64);
-            const uint64_t m = __ballot(key == lk);
-            if (key == lk) {
-                rank = __popcll(m & lanes_below);
-                gsize = __popcll(m);
-            }
-            todo &= ~m;
+        if (key >= 0) {
+            const uint64_t m = (uint64_t)my_tbl[2 * key] | ((uint64_t)my_tbl[2 * key + 1] << 32);
+            rank = __popcll(m & lanes_below);
+            gsize = __popcll(m);
         }
         if (key >= 0 && rank == 0) wcnt[wave * NB + key] = (uint8_t)gsize;
-        __syncthreads();
+        lds_barrier();
         if (key >= 0) {
             int pos = cnt[key] + rank;
             for (int w2 = 0; w2 < wave; w2++) pos += wcnt[w2 * NB + key];
             pair_ids[pos] = p;
         }
-        __syncthreads();
+        lds_barrier();
         if (key >= 0 && rank == 0) {
             atomicAdd(&cnt[key], gsize);
             wcnt[wave * NB + key] = 0;
+            my_tbl[2 * key] = 0;
+            my_tbl[2 * key + 1] = 0;
         }
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -130,7 +136,8 @@ int launch_bucket(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t e
                   hipStream_t s) {
     const int32_t P = T * k;
     const int NB = E + 1;
-    const size_t lds = sizeof(int32_t) * (NB + 32) + (size_t)kWaves * NB;
+    const size_t lds = sizeof(int32_t) * (NB + 32) + sizeof(uint32_t) * 2 * kWaves * NB +
+                       (size_t)kWaves * NB;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(bucket_kernel),
@@ -138,8 +145,10 @@ int launch_bucket(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t e
             return MOE_ELAUNCH;
         attr_set = true;
     }
+    prof_start(MOE_KERNEL_BUCKET, s);
     hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(kThreads), lds, s, ids, P, E, expert_base,
                        offsets, pair_ids, active, counts);
+    prof_stop(MOE_KERNEL_BUCKET, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 

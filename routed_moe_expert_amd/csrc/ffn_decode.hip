@@ -1,24 +1,26 @@
 // Decode path of the routed NVFP4 FFN (few tokens per expert, weight-stream bound).
 //
 // The union gather (moe_union_probe.rs: read each distinct expert's NVFP4 bytes once per call
-// instead of once per routed slot): a workgroup owns one active expert and a tile of its weight
-// rows. It stages the tile's NVFP4 bytes and the bf16 rows of every token routed to that expert
-// in LDS once, then runs all of those tokens against the tile.
+// instead of once per routed slot): work items are (active expert, tile of weight rows); each
+// item's NVFP4 tile is read from HBM once and run against every token routed to that expert,
+// whose rows are staged in LDS once per expert.
 //
-//   gu_decode: 8 gate rows + the 8 matching up rows per workgroup; each thread takes one row and
+//   gu_decode: items of 8 gate rows + the 8 matching up rows. Each thread takes one row and
 //              every 16th scale group of it, decodes E2M1 pairs to bf16 in registers
 //              (v_cvt_scalef32_pk_bf16_fp4, exact), forms 16-weight partial dot products with
 //              v_dot2_f32_bf16 against the staged activations, scales each partial by its
 //              UE4M3 group scale, and the 16 threads of a row reduce with lane shuffles.
 //              The epilogue applies SiLU(g) * u and writes h (fp32) in CSR pair order.
-//   dn_decode: 32 down rows per workgroup, h rows staged in LDS as fp32, E2M1 pairs decoded to
-//              fp32 (v_cvt_scalef32_pk_f32_fp4), fp32 FMAs; writes the per-pair down output
-//              ypair (fp32) in CSR pair order.
-//   combine:   y[t] = sum over t's local slots in ascending j of w[t,j] * ypair[pos(t,j)].
+//   dn_decode: items of 64 down rows, h rows staged in LDS as fp32, E2M1 pairs decoded to fp32
+//              (v_cvt_scalef32_pk_f32_fp4), fp32 FMAs; writes the per-pair down output ypair
+//              (fp32) at row p = t*k + j of its pair.
+//   combine:   y[t] = sum over t's local slots in ascending j of w[t,j] * ypair[t*k + j]; the
+//              pair -> CSR slot map only says which slots are local.
 //
-// Grids are sized from host-known bounds (at most min(E, T*k) active experts); workgroups whose
-// active-slot index is at or past n_active exit at once, so nothing reads the device counts on
-// the host.
+// Both FFN kernels are persistent: a grid of at most two workgroups per CU splits the
+// (expert, tile) items into contiguous ranges, read from the device CSR (nothing is read back on
+// the host). Tiles stream through three LDS buffers with direct-to-LDS loads, two tiles in
+// flight while one is computed.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -27,18 +29,14 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kGuRowsPerSide = 8;      // gate rows (and up rows) per gu workgroup
+constexpr int kGuRowsPerSide = 8;      // gate rows (and up rows) per gu item
 constexpr int kGuRows = 2 * kGuRowsPerSide;
 constexpr int kGuLanesPerRow = kThreads / kGuRows;   // 16
-constexpr int kDnRows = 32;            // down rows per dn workgroup
-constexpr int kDnLanesPerRow = kThreads / kDnRows;   // 8
-
-// Copy `bytes` (a multiple of 16) from 16-byte aligned global memory into LDS.
-__device__ __forceinline__ void stage16(uint8_t *lds, const uint8_t *g, int bytes) {
-    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(g);
-    u32x4_t *dst = reinterpret_cast<u32x4_t *>(lds);
-    for (int u = threadIdx.x; u < bytes / 16; u += kThreads) dst[u] = src[u];
-}
+constexpr int kDnRows = 64;            // down rows per dn item
+constexpr int kDnLanesPerRow = kThreads / kDnRows;   // 4
+constexpr int kNBuf = 3;               // weight tiles in LDS: one computed, two in flight
+constexpr int kWgPerCu = 2;
+constexpr int kCUs = 256;
 
 template <int W>
 __device__ __forceinline__ float group_sum(float v) {
@@ -47,198 +45,367 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-// Writes pos[pair_ids[q]] = q for q in [q_lo, q_hi).
-__device__ __forceinline__ void write_pos(const int32_t *pair_ids, int32_t *pos, int q_lo, int q_hi) {
-    for (int q = q_lo + threadIdx.x; q < q_hi; q += kThreads) pos[pair_ids[q]] = q;
+// One gu item: thread (row, sub) accumulates row `row` of the staged 16-row tile (8 gate rows,
+// then the 8 matching up rows) against the mt staged token rows, over every 16th scale group.
+template <int MT>
+__device__ __forceinline__ void gu_tile_dot(const uint8_t *wrow, const uint16_t *xbuf, int sub,
+                                            int H, int mt, float (&acc)[MT]) {
+    const int iters = H / (kGroup * kGuLanesPerRow);   // H % 256 == 0: same count in every lane
+#pragma unroll
+    for (int i = 0; i < MT; i++) acc[i] = 0.f;
+#pragma unroll 2
+    for (int it = 0; it < iters; it++) {
+        const int g = sub + it * kGuLanesPerRow;
+        const uint8_t *blk = wrow + (g >> 2) * kBlockBytes;
+        const float S = ue4m3_to_f32(blk[g & 3]);
+        const uint32_t *cw = reinterpret_cast<const uint32_t *>(blk + 4 + 8 * (g & 3));
+        const uint32_t c0w = cw[0], c1w = cw[1];
+        uint32_t wv[8];
+        wv[0] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(c0w));
+        wv[1] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(c0w));
+        wv[2] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(c0w));
+        wv[3] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(c0w));
+        wv[4] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(c1w));
+        wv[5] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(c1w));
+        wv[6] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(c1w));
+        wv[7] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(c1w));
+#pragma unroll
+        for (int i = 0; i < MT; i++) {
+            if (i < mt) {
+                const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(xbuf + i * H + g * kGroup);
+                const u32x4_t xa = xr[0], xb = xr[1];
+                float p = 0.f;
+                p = dot2_bf16(wv[0], xa[0], p);
+                p = dot2_bf16(wv[1], xa[1], p);
+                p = dot2_bf16(wv[2], xa[2], p);
+                p = dot2_bf16(wv[3], xa[3], p);
+                p = dot2_bf16(wv[4], xb[0], p);
+                p = dot2_bf16(wv[5], xb[1], p);
+                p = dot2_bf16(wv[6], xb[2], p);
+                p = dot2_bf16(wv[7], xb[3], p);
+                acc[i] = fmaf(S, p, acc[i]);
+            }
+        }
+    }
 }
 
+// One dn item: thread (row, sub) accumulates down row `row` of the 64-row tile against the mt
+// staged fp32 h rows.
+template <int MT>
+__device__ __forceinline__ void dn_tile_dot(const uint8_t *wrow, const float *hbuf, int sub,
+                                            int F, int mt, float (&acc)[MT]) {
+    const int iters = F / (kGroup * kDnLanesPerRow);   // F % 64 == 0: same count in every lane
+#pragma unroll
+    for (int i = 0; i < MT; i++) acc[i] = 0.f;
+#pragma unroll 2
+    for (int it = 0; it < iters; it++) {
+        const int g = sub + it * kDnLanesPerRow;
+        const uint8_t *blk = wrow + (g >> 2) * kBlockBytes;
+        const float S = ue4m3_to_f32(blk[g & 3]);
+        const uint32_t *cw = reinterpret_cast<const uint32_t *>(blk + 4 + 8 * (g & 3));
+        const uint32_t c0w = cw[0], c1w = cw[1];
+        f32x2_t wv[8];
+        wv[0] = e2m1x2_to_f32<0>(c0w);
+        wv[1] = e2m1x2_to_f32<1>(c0w);
+        wv[2] = e2m1x2_to_f32<2>(c0w);
+        wv[3] = e2m1x2_to_f32<3>(c0w);
+        wv[4] = e2m1x2_to_f32<0>(c1w);
+        wv[5] = e2m1x2_to_f32<1>(c1w);
+        wv[6] = e2m1x2_to_f32<2>(c1w);
+        wv[7] = e2m1x2_to_f32<3>(c1w);
+#pragma unroll
+        for (int i = 0; i < MT; i++) {
+            if (i < mt) {
+                const f32x4_t *hr = reinterpret_cast<const f32x4_t *>(hbuf + i * F + g * kGroup);
+                float p = 0.f;
+#pragma unroll
+                for (int v = 0; v < 4; v++) {
+                    const f32x4_t hv = hr[v];
+                    p = fmaf(wv[2 * v][0], hv[0], p);
+                    p = fmaf(wv[2 * v][1], hv[1], p);
+                    p = fmaf(wv[2 * v + 1][0], hv[2], p);
+                    p = fmaf(wv[2 * v + 1][1], hv[3], p);
+                }
+                acc[i] = fmaf(S, p, acc[i]);
+            }
+        }
+    }
+}
+
+// Item range of this workgroup: items are (active expert a, row tile t) in a-major order, split
+// into equal contiguous ranges over the grid, so a workgroup mostly stays on one expert and its
+// token rows are staged once.
+__device__ __forceinline__ void item_range(int total, int &i0, int &i1) {
+    const int per = (total + gridDim.x - 1) / gridDim.x;
+    i0 = min((int)blockIdx.x * per, total);
+    i1 = min(i0 + per, total);
+}
+
+// The CSR entries a workgroup needs (its experts, their first CSR slot, pair count and first MT
+// pair ids), fetched once into LDS at kernel start: reading them per item would put a chain of
+// dependent scalar loads (active -> offsets -> pair_ids), each a round trip to memory the
+// previous kernel just wrote, in front of every tile.
+constexpr int kMaxMeta = 32;   // experts per workgroup range; grids are sized so this holds
+template <int MT>
+struct Meta {
+    int e[kMaxMeta], q0[kMaxMeta], m[kMaxMeta], pid[kMaxMeta][MT];
+};
+
+// Fills meta for active experts [a_first, a_first + na); returns false if na is too large.
+template <int MT>
+__device__ __forceinline__ void load_meta(Meta<MT> &meta, const int32_t *active,
+                                          const int32_t *offsets, const int32_t *pair_ids,
+                                          int a_first, int na) {
+    const int tid = threadIdx.x;
+    if (tid < na) {
+        const int e = active[a_first + tid];
+        const int q0 = offsets[e], m = offsets[e + 1] - q0;
+        meta.e[tid] = e;
+        meta.q0[tid] = q0;
+        meta.m[tid] = m;
+#pragma unroll
+        for (int j = 0; j < MT; j++) meta.pid[tid][j] = j < m ? pair_ids[q0 + j] : 0;
+    }
+}
+
+// Gate/up + SiLU * up over the union of active experts. Persistent workgroups stream their
+// 16-row NVFP4 tiles through kNBuf LDS buffers with direct-to-LDS loads (two tiles in flight
+// while one is computed); h stores of an item are deferred to the next item's start so the
+// in-order vmcnt wait only ever has the newest tile outstanding.
 template <int MT>
 __global__ __launch_bounds__(kThreads) void gu_decode_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const int32_t *__restrict__ active,
     const int32_t *__restrict__ counts, const uint8_t *__restrict__ gate, int64_t gate_stride,
-    const uint8_t *__restrict__ up, int64_t up_stride, int32_t k, int32_t E, int32_t P, int32_t H,
-    int32_t F, float *__restrict__ h, int32_t *__restrict__ pos) {
+    const uint8_t *__restrict__ up, int64_t up_stride, int32_t k, int32_t P, int32_t H, int32_t F,
+    float *__restrict__ h, int32_t *__restrict__ pos) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = H / kBlockWeights * kBlockBytes;
-    uint8_t *wbuf = smem;                                          // [16][rb] NVFP4 rows
-    uint16_t *xbuf = reinterpret_cast<uint16_t *>(smem + kGuRows * rb);  // [MT][H] bf16
-    float *red = reinterpret_cast<float *>(xbuf + MT * H);         // [16][MT]
-
-    const int a = blockIdx.y;
-    if (blockIdx.x == 0 && a == 0) write_pos(pair_ids, pos, offsets[E], P);  // non-local pairs
-    if (a >= counts[0]) return;
-    const int e = active[a];
-    const int q0 = offsets[e], m = offsets[e + 1] - q0;
-    if (blockIdx.x == 0) write_pos(pair_ids, pos, q0, q0 + m);
-
-    const int o0 = blockIdx.x * kGuRowsPerSide;
-    const int span = kGuRowsPerSide * rb;
-    stage16(wbuf, gate + e * gate_stride + (int64_t)o0 * rb, span);
-    stage16(wbuf + span, up + e * up_stride + (int64_t)o0 * rb, span);
-
+    const int side = kGuRowsPerSide * rb, tile_bytes = 2 * side;
+    uint8_t *wb = smem;                                                     // [kNBuf][16 rows]
+    uint16_t *xbuf = reinterpret_cast<uint16_t *>(smem + kNBuf * tile_bytes);  // [MT][H] bf16
+    float *red = reinterpret_cast<float *>(xbuf + MT * H);                  // [16][MT]
+    __shared__ Meta<MT> meta;
     const int tid = threadIdx.x;
+
+    for (int q = blockIdx.x * kThreads + tid; q < P; q += gridDim.x * kThreads) pos[pair_ids[q]] = q;
+
+    const int tiles = F / kGuRowsPerSide;
+    int i0, i1;
+    item_range(counts[0] * tiles, i0, i1);
+    if (i0 >= i1) return;
+    const int a_first = i0 / tiles;
+    load_meta<MT>(meta, active, offsets, pair_ids, a_first,
+                  min((i1 - 1) / tiles - a_first + 1, kMaxMeta));
+    lds_barrier();
     const int row = tid / kGuLanesPerRow, sub = tid % kGuLanesPerRow;
-    const uint8_t *wrow = wbuf + row * rb;
-    const int groups = H / kGroup;
+    const int n_inst = 2 * stage_async_count<kThreads>(side);
 
-    for (int c0 = 0; c0 < m; c0 += MT) {
-        const int mt = min(MT, m - c0);
-        if (c0) __syncthreads();  // previous chunk's x and red are no longer read
-        for (int i = 0; i < mt; i++) {
-            const int t = pair_ids[q0 + c0 + i] / k;
-            stage16(reinterpret_cast<uint8_t *>(xbuf + i * H),
-                    reinterpret_cast<const uint8_t *>(x + (int64_t)t * H), H * 2);
-        }
-        __syncthreads();
-
-        float acc[MT];
-#pragma unroll
-        for (int i = 0; i < MT; i++) acc[i] = 0.f;
-        for (int g = sub; g < groups; g += kGuLanesPerRow) {
-            const uint8_t *blk = wrow + (g >> 2) * kBlockBytes;
-            const float S = ue4m3_to_f32(blk[g & 3]);
-            const uint32_t *cw = reinterpret_cast<const uint32_t *>(blk + 4 + 8 * (g & 3));
-            const uint32_t c0w = cw[0], c1w = cw[1];
-            uint32_t wv[8];
-            wv[0] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(c0w));
-            wv[1] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(c0w));
-            wv[2] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(c0w));
-            wv[3] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(c0w));
-            wv[4] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(c1w));
-            wv[5] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(c1w));
-            wv[6] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(c1w));
-            wv[7] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(c1w));
-#pragma unroll
-            for (int i = 0; i < MT; i++) {
-                if (i < mt) {
-                    const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(xbuf + i * H + g * kGroup);
-                    const u32x4_t xa = xr[0], xb = xr[1];
-                    float p = 0.f;
-                    p = dot2_bf16(wv[0], xa[0], p);
-                    p = dot2_bf16(wv[1], xa[1], p);
-                    p = dot2_bf16(wv[2], xa[2], p);
-                    p = dot2_bf16(wv[3], xa[3], p);
-                    p = dot2_bf16(wv[4], xb[0], p);
-                    p = dot2_bf16(wv[5], xb[1], p);
-                    p = dot2_bf16(wv[6], xb[2], p);
-                    p = dot2_bf16(wv[7], xb[3], p);
-                    acc[i] = fmaf(S, p, acc[i]);
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < MT; i++) {
-            if (i < mt) {
-                const float v = group_sum<kGuLanesPerRow>(acc[i]);
-                if (sub == 0) red[row * MT + i] = v;
-            }
-        }
-        __syncthreads();
+    auto issue = [&](int i) {
+        const int a = i / tiles - a_first, t = i % tiles, e = meta.e[a];
+        uint8_t *dst = wb + ((i - i0) % kNBuf) * tile_bytes;
+        stage_async<kThreads>(dst, gate + e * gate_stride + (int64_t)t * side, side);
+        stage_async<kThreads>(dst + side, up + e * up_stride + (int64_t)t * side, side);
+    };
+    auto store_h = [&](int q0, int o0, int mt) {
         if (tid < kGuRowsPerSide * mt) {
-            const int oi = tid % kGuRowsPerSide, i = tid / kGuRowsPerSide;
-            const float gv = red[oi * MT + i], uv = red[(kGuRowsPerSide + oi) * MT + i];
-            h[(int64_t)(q0 + c0 + i) * F + o0 + oi] = silu(gv) * uv;
+            const int oi = tid % kGuRowsPerSide, j = tid / kGuRowsPerSide;
+            const float gv = red[oi * MT + j], uv = red[(kGuRowsPerSide + oi) * MT + j];
+            h[(int64_t)(q0 + j) * F + o0 + oi] = silu(gv) * uv;
+        }
+    };
+    auto reduce = [&](float (&acc)[MT], int mt) {
+#pragma unroll
+        for (int j = 0; j < MT; j++) {
+            if (j < mt) {
+                const float v = group_sum<kGuLanesPerRow>(acc[j]);
+                if (sub == 0) red[row * MT + j] = v;
+            }
+        }
+    };
+    auto stage_x = [&](int a, int c0, int mt) {   // token rows of CSR pairs c0..c0+mt-1
+        for (int j = 0; j < mt; j++) {
+            const int p = c0 + j < MT ? meta.pid[a][c0 + j] : pair_ids[meta.q0[a] + c0 + j];
+            stage_async<kThreads>(xbuf + j * H, x + (int64_t)(p / k) * H, H * 2);
+        }
+    };
+
+    issue(i0);
+    if (i0 + 1 < i1) issue(i0 + 1);
+    int cur_a = -1, pend_q0 = -1, pend_o0 = 0, pend_mt = 0;
+    for (int i = i0; i < i1; i++) {
+        const int a = i / tiles - a_first, t = i % tiles;
+        const int q0 = meta.q0[a], m = meta.m[a];
+        const uint8_t *wt = wb + ((i - i0) % kNBuf) * tile_bytes;
+        if (a != cur_a && m <= MT) {  // new expert: its token rows (readers of the old ones have
+            stage_x(a, 0, m);         // passed the previous item's pre-reduction barrier)
+            lds_dma_wait();
+            cur_a = a;
+        } else {
+            vm_wait_le(i + 1 < i1 ? n_inst : 0);  // tile i landed; only tile i+1 outstanding
+        }
+        lds_barrier();
+        if (pend_q0 >= 0) store_h(pend_q0, pend_o0, pend_mt);
+        pend_q0 = -1;
+        if (i + 2 < i1) issue(i + 2);
+        float acc[MT];
+        if (m <= MT) {
+            gu_tile_dot<MT>(wt + row * rb, xbuf, sub, H, m, acc);
+            lds_barrier();  // red is free: the deferred stores above have read it
+            reduce(acc, m);
+            pend_q0 = q0;
+            pend_o0 = t * kGuRowsPerSide;
+            pend_mt = m;
+        } else {  // more pairs than MT: token chunks, each restaged (waits on all loads)
+            for (int c0 = 0; c0 < m; c0 += MT) {
+                const int mt = min(MT, m - c0);
+                lds_barrier();
+                stage_x(a, c0, mt);
+                lds_dma_wait();
+                lds_barrier();
+                gu_tile_dot<MT>(wt + row * rb, xbuf, sub, H, mt, acc);
+                lds_barrier();
+                reduce(acc, mt);
+                lds_barrier();
+                store_h(q0 + c0, t * kGuRowsPerSide, mt);
+            }
+            cur_a = -1;
         }
     }
+    lds_barrier();
+    if (pend_q0 >= 0) store_h(pend_q0, pend_o0, pend_mt);
 }
 
+// Down projection over the union of active experts, same streaming scheme with 64-row tiles.
 template <int MT>
 __global__ __launch_bounds__(kThreads) void dn_decode_kernel(
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ active,
-    const int32_t *__restrict__ counts, const uint8_t *__restrict__ down, int64_t down_stride,
-    int32_t H, int32_t F, const float *__restrict__ h, float *__restrict__ ypair) {
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
+    const int32_t *__restrict__ active, const int32_t *__restrict__ counts,
+    const uint8_t *__restrict__ down, int64_t down_stride, int32_t H, int32_t F,
+    const float *__restrict__ h, float *__restrict__ ypair) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = F / kBlockWeights * kBlockBytes;
-    uint8_t *wbuf = smem;                                        // [32][rb]
-    float *hbuf = reinterpret_cast<float *>(smem + kDnRows * rb);  // [MT][F]
-
-    const int a = blockIdx.y;
-    if (a >= counts[0]) return;
-    const int e = active[a];
-    const int q0 = offsets[e], m = offsets[e + 1] - q0;
-    const int r0 = blockIdx.x * kDnRows;
-    stage16(wbuf, down + e * down_stride + (int64_t)r0 * rb, kDnRows * rb);
-
+    const int tile_bytes = kDnRows * rb;
+    uint8_t *wb = smem;                                                     // [kNBuf][64 rows]
+    float *hbuf = reinterpret_cast<float *>(smem + kNBuf * tile_bytes);     // [MT][F]
+    float *red = hbuf + MT * F;                                             // [MT][64]
+    __shared__ Meta<MT> meta;
     const int tid = threadIdx.x;
-    const int row = tid / kDnLanesPerRow, sub = tid % kDnLanesPerRow;
-    const uint8_t *wrow = wbuf + row * rb;
-    const int groups = F / kGroup;
 
-    for (int c0 = 0; c0 < m; c0 += MT) {
-        const int mt = min(MT, m - c0);
-        if (c0) __syncthreads();
-        stage16(reinterpret_cast<uint8_t *>(hbuf),
-                reinterpret_cast<const uint8_t *>(h + (int64_t)(q0 + c0) * F), mt * F * 4);
-        __syncthreads();
-        float acc[MT];
+    const int tiles = H / kDnRows;
+    int i0, i1;
+    item_range(counts[0] * tiles, i0, i1);
+    if (i0 >= i1) return;
+    const int a_first = i0 / tiles;
+    load_meta<MT>(meta, active, offsets, pair_ids, a_first,
+                  min((i1 - 1) / tiles - a_first + 1, kMaxMeta));
+    lds_barrier();
+    const int row = tid / kDnLanesPerRow, sub = tid % kDnLanesPerRow;
+    const int n_inst = stage_async_count<kThreads>(tile_bytes);
+
+    auto issue = [&](int i) {
+        const int a = i / tiles - a_first, t = i % tiles, e = meta.e[a];
+        stage_async<kThreads>(wb + ((i - i0) % kNBuf) * tile_bytes,
+                              down + e * down_stride + (int64_t)t * tile_bytes, tile_bytes);
+    };
+    auto store_y = [&](int a, int c0, int r0, int mt) {   // CSR pairs c0..c0+mt-1 of expert a
+        for (int v = tid; v < kDnRows * mt; v += kThreads) {
+            const int r = v % kDnRows, j = v / kDnRows;
+            const int p = c0 + j < MT ? meta.pid[a][c0 + j] : pair_ids[meta.q0[a] + c0 + j];
+            ypair[(int64_t)p * H + r0 + r] = red[j * kDnRows + r];
+        }
+    };
+    auto reduce = [&](float (&acc)[MT], int mt) {
 #pragma unroll
-        for (int i = 0; i < MT; i++) acc[i] = 0.f;
-        for (int g = sub; g < groups; g += kDnLanesPerRow) {
-            const uint8_t *blk = wrow + (g >> 2) * kBlockBytes;
-            const float S = ue4m3_to_f32(blk[g & 3]);
-            const uint32_t *cw = reinterpret_cast<const uint32_t *>(blk + 4 + 8 * (g & 3));
-            const uint32_t c0w = cw[0], c1w = cw[1];
-            f32x2_t wv[8];
-            wv[0] = e2m1x2_to_f32<0>(c0w);
-            wv[1] = e2m1x2_to_f32<1>(c0w);
-            wv[2] = e2m1x2_to_f32<2>(c0w);
-            wv[3] = e2m1x2_to_f32<3>(c0w);
-            wv[4] = e2m1x2_to_f32<0>(c1w);
-            wv[5] = e2m1x2_to_f32<1>(c1w);
-            wv[6] = e2m1x2_to_f32<2>(c1w);
-            wv[7] = e2m1x2_to_f32<3>(c1w);
-#pragma unroll
-            for (int i = 0; i < MT; i++) {
-                if (i < mt) {
-                    const f32x4_t *hr = reinterpret_cast<const f32x4_t *>(hbuf + i * F + g * kGroup);
-                    float p = 0.f;
-#pragma unroll
-                    for (int v = 0; v < 4; v++) {
-                        const f32x4_t hv = hr[v];
-                        p = fmaf(wv[2 * v][0], hv[0], p);
-                        p = fmaf(wv[2 * v][1], hv[1], p);
-                        p = fmaf(wv[2 * v + 1][0], hv[2], p);
-                        p = fmaf(wv[2 * v + 1][1], hv[3], p);
-                    }
-                    acc[i] = fmaf(S, p, acc[i]);
-                }
+        for (int j = 0; j < MT; j++) {
+            if (j < mt) {
+                const float v = group_sum<kDnLanesPerRow>(acc[j]);
+                if (sub == 0) red[j * kDnRows + row] = v;
             }
         }
-#pragma unroll
-        for (int i = 0; i < MT; i++) {
-            if (i < mt) {
-                const float v = group_sum<kDnLanesPerRow>(acc[i]);
-                if (sub == 0) ypair[(int64_t)(q0 + c0 + i) * H + r0 + row] = v;
+    };
+
+    issue(i0);
+    if (i0 + 1 < i1) issue(i0 + 1);
+    int cur_a = -1, pend_a = -1, pend_r0 = 0, pend_mt = 0;
+    for (int i = i0; i < i1; i++) {
+        const int a = i / tiles - a_first, t = i % tiles;
+        const int q0 = meta.q0[a], m = meta.m[a];
+        const uint8_t *wt = wb + ((i - i0) % kNBuf) * tile_bytes;
+        if (a != cur_a && m <= MT) {
+            stage_async<kThreads>(hbuf, h + (int64_t)q0 * F, m * F * 4);
+            lds_dma_wait();
+            cur_a = a;
+        } else {
+            vm_wait_le(i + 1 < i1 ? n_inst : 0);
+        }
+        lds_barrier();
+        if (pend_a >= 0) store_y(pend_a, 0, pend_r0, pend_mt);
+        pend_a = -1;
+        if (i + 2 < i1) issue(i + 2);
+        float acc[MT];
+        if (m <= MT) {
+            dn_tile_dot<MT>(wt + row * rb, hbuf, sub, F, m, acc);
+            lds_barrier();
+            reduce(acc, m);
+            pend_a = a;
+            pend_r0 = t * kDnRows;
+            pend_mt = m;
+        } else {
+            for (int c0 = 0; c0 < m; c0 += MT) {
+                const int mt = min(MT, m - c0);
+                lds_barrier();
+                stage_async<kThreads>(hbuf, h + (int64_t)(q0 + c0) * F, mt * F * 4);
+                lds_dma_wait();
+                lds_barrier();
+                dn_tile_dot<MT>(wt + row * rb, hbuf, sub, F, mt, acc);
+                lds_barrier();
+                reduce(acc, mt);
+                lds_barrier();
+                store_y(a, c0, t * kDnRows, mt);
             }
+            cur_a = -1;
         }
     }
+    lds_barrier();
+    if (pend_a >= 0) store_y(pend_a, 0, pend_r0, pend_mt);
 }
 
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float *__restrict__ w, const int32_t *__restrict__ pos, const int32_t *__restrict__ offsets,
     int32_t E, const float *__restrict__ ypair, int32_t k, int32_t H, float *__restrict__ y) {
+    constexpr int kJ = 8;  // slots whose loads are issued together
     const int t = blockIdx.y;
     const int r = (blockIdx.x * kThreads + threadIdx.x) * 4;
     if (r >= H) return;
     const int n_local = offsets[E];
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; j++) {
-        const int p = t * k + j;
-        const int q = pos[p];
-        if (q < n_local) {
-            const float wt = w[p];
-            const f32x4_t v = *reinterpret_cast<const f32x4_t *>(ypair + (int64_t)q * H + r);
-            acc[0] = fmaf(wt, v[0], acc[0]);
-            acc[1] = fmaf(wt, v[1], acc[1]);
-            acc[2] = fmaf(wt, v[2], acc[2]);
-            acc[3] = fmaf(wt, v[3], acc[3]);
+    for (int j0 = 0; j0 < k; j0 += kJ) {
+        int q[kJ];
+        float wt[kJ];
+        f32x4_t v[kJ];
+#pragma unroll
+        for (int u = 0; u < kJ; u++) {
+            const int p = t * k + j0 + u;
+            const bool in = j0 + u < k;
+            q[u] = in ? pos[p] : n_local;
+            wt[u] = in ? w[p] : 0.f;
+            // rows of non-local slots hold stale data; they are loaded and then skipped
+            v[u] = in ? *reinterpret_cast<const f32x4_t *>(ypair + (int64_t)p * H + r)
+                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < kJ; u++) {   // ascending slot order
+            if (q[u] < n_local) {
+                acc[0] = fmaf(wt[u], v[u][0], acc[0]);
+                acc[1] = fmaf(wt[u], v[u][1], acc[1]);
+                acc[2] = fmaf(wt[u], v[u][2], acc[2]);
+                acc[3] = fmaf(wt[u], v[u][3], acc[3]);
+            }
         }
     }
     *reinterpret_cast<f32x4_t *>(y + (int64_t)t * H + r) = acc;
 }
-
-constexpr int kMT = 8;
 
 struct DecodeWs {
     int32_t *pos;   // [P]
@@ -259,9 +426,13 @@ DecodeWs carve(void *ws, int32_t P, int32_t H, int32_t F) {
     return d;
 }
 
-bool set_lds_attr(const void *fn, size_t bytes) {
-    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes) ==
-           hipSuccess;
+// Allow up to 160 KB of LDS per workgroup: the dynamic limit is what the kernel's static LDS
+// leaves of it.
+bool set_lds_attr(const void *fn, size_t total) {
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, fn) != hipSuccess || fa.sharedSizeBytes > total) return false;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)(total - fa.sharedSizeBytes)) == hipSuccess;
 }
 
 }  // namespace
@@ -276,37 +447,64 @@ size_t decode_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
 int launch_combine(const float *w, const int32_t *pos, const int32_t *offsets, int32_t E,
                    const float *ypair, int32_t T, int32_t k, int32_t H, float *y, hipStream_t s) {
     dim3 grid((H / 4 + kThreads - 1) / kThreads, T);
+    prof_start(MOE_KERNEL_COMBINE, s);
     hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, w, pos, offsets, E, ypair, k,
                        H, y);
+    prof_stop(MOE_KERNEL_COMBINE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-int launch_decode(const FfnArgs &a, hipStream_t s) {
+template <int MT>
+int launch_decode_mt(const FfnArgs &a, const DecodeWs &d, hipStream_t s) {
     const int32_t P = a.T * a.k;
-    const DecodeWs d = carve(a.ws, P, a.H, a.F);
     const int max_active = (int)std::min<int64_t>(a.E, P);
     const size_t rbh = (size_t)row_bytes(a.H), rbf = (size_t)row_bytes(a.F);
-
-    const size_t gu_lds = kGuRows * rbh + (size_t)kMT * a.H * 2 + kGuRows * kMT * 4;
-    const size_t dn_lds = kDnRows * rbf + (size_t)kMT * a.F * 4;
-    if (gu_lds > 160 * 1024 || dn_lds > 160 * 1024) return MOE_ESHAPE;
+    const size_t gu_lds = kNBuf * kGuRows * rbh + (size_t)MT * a.H * 2 + kGuRows * MT * 4;
+    const size_t dn_lds = kNBuf * kDnRows * rbf + (size_t)MT * a.F * 4 + kDnRows * MT * 4;
+    if (gu_lds + sizeof(Meta<MT>) > 160 * 1024 || dn_lds + sizeof(Meta<MT>) > 160 * 1024)
+        return MOE_ESHAPE;
     static bool attrs = false;
     if (!attrs) {
-        if (!set_lds_attr(reinterpret_cast<const void *>(gu_decode_kernel<kMT>), 160 * 1024) ||
-            !set_lds_attr(reinterpret_cast<const void *>(dn_decode_kernel<kMT>), 160 * 1024))
+        if (!set_lds_attr(reinterpret_cast<const void *>(gu_decode_kernel<MT>), 160 * 1024) ||
+            !set_lds_attr(reinterpret_cast<const void *>(dn_decode_kernel<MT>), 160 * 1024))
             return MOE_ELAUNCH;
         attrs = true;
     }
-    hipLaunchKernelGGL(gu_decode_kernel<kMT>, dim3(a.F / kGuRowsPerSide, max_active),
-                       dim3(kThreads), gu_lds, s, a.x, a.offsets, a.pair_ids, a.active, a.counts,
-                       a.gate.base, a.gate.expert_stride, a.up.base, a.up.expert_stride, a.k, a.E,
-                       P, a.H, a.F, d.h, d.pos);
+    const int grid_cap = kWgPerCu * kCUs;
+    const int gu_tiles = a.F / kGuRowsPerSide, dn_tiles = a.H / kDnRows;
+    const int gu_grid = (int)std::min<int64_t>(grid_cap, (int64_t)max_active * gu_tiles);
+    const int dn_grid = (int)std::min<int64_t>(grid_cap, (int64_t)max_active * dn_tiles);
+    // experts one workgroup's item range can touch must fit its LDS metadata table
+    auto max_experts = [&](int tiles, int grid) {
+        const int64_t per = ((int64_t)max_active * tiles + grid - 1) / grid;
+        return (per - 1) / tiles + 2;
+    };
+    if (max_experts(gu_tiles, gu_grid) > kMaxMeta || max_experts(dn_tiles, dn_grid) > kMaxMeta)
+        return MOE_ESHAPE;
+    prof_start(MOE_KERNEL_GU_DECODE, s);
+    hipLaunchKernelGGL(gu_decode_kernel<MT>, dim3(gu_grid), dim3(kThreads), gu_lds, s, a.x,
+                       a.offsets, a.pair_ids, a.active, a.counts, a.gate.base,
+                       a.gate.expert_stride, a.up.base, a.up.expert_stride, a.k, P, a.H, a.F, d.h,
+                       d.pos);
+    prof_stop(MOE_KERNEL_GU_DECODE, s);
     if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
-    hipLaunchKernelGGL(dn_decode_kernel<kMT>, dim3(a.H / kDnRows, max_active), dim3(kThreads),
-                       dn_lds, s, a.offsets, a.active, a.counts, a.down.base,
-                       a.down.expert_stride, a.H, a.F, d.h, d.ypair);
+    prof_start(MOE_KERNEL_DN_DECODE, s);
+    hipLaunchKernelGGL(dn_decode_kernel<MT>, dim3(dn_grid), dim3(kThreads), dn_lds, s, a.offsets,
+                       a.pair_ids, a.active, a.counts, a.down.base, a.down.expert_stride, a.H, a.F,
+                       d.h, d.ypair);
+    prof_stop(MOE_KERNEL_DN_DECODE, s);
     if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
     return launch_combine(a.w, d.pos, a.offsets, a.E, d.ypair, a.T, a.k, a.H, a.y, s);
+}
+
+int launch_decode(const FfnArgs &a, hipStream_t s) {
+    const DecodeWs d = carve(a.ws, a.T * a.k, a.H, a.F);
+    // Token rows staged per expert. Most experts of a decode batch see one or two pairs; an
+    // expert with more pairs runs its tile once per chunk of MT rows.
+    switch (std::min(a.T, 2)) {
+    case 1: return launch_decode_mt<1>(a, d, s);
+    default: return launch_decode_mt<2>(a, d, s);
+    }
 }
 
 }  // namespace moe

@@ -47,6 +47,80 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Asynchronous copy of `bytes` (a multiple of 16) from 16-byte aligned global memory into
+// 16-byte aligned LDS with the gfx950 direct-to-LDS load (global_load_lds_dwordx4): wave w moves
+// 64 consecutive 16-byte units per instruction, lane i landing at the wave's LDS base + 16*i, so
+// no VGPRs are used and every load of the workgroup is in flight at once. Completion is awaited
+// with lds_dma_wait() followed by a workgroup barrier.
+template <int kThreads>
+__device__ __forceinline__ void stage_async(void *lds, const void *g, int bytes) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int units = bytes >> 4;
+    const uint8_t *src = static_cast<const uint8_t *>(g);
+    uint8_t *dst = static_cast<uint8_t *>(lds);
+    for (int base = wave * 64; base < units; base += kThreads) {
+        const int u = base + lane;
+        if (u < units)
+            __builtin_amdgcn_global_load_lds(src + (size_t)u * 16, (lds_void_t *)(dst + base * 16),
+                                             16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that orders LDS only: it waits for this wave's LDS (and scalar) operations
+// and synchronizes the workgroup, but leaves global loads in flight. __syncthreads() carries a
+// fence over global memory, for which the compiler waits for every outstanding vector-memory
+// operation, and that would drain the prefetched tiles at each barrier. Kernels using this share
+// data between waves through LDS only; data landed by direct-to-LDS loads is awaited first with
+// vm_wait_le / lds_dma_wait by every issuing wave.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Number of global_load_lds instructions one wave issues in stage_async for `bytes`.
+template <int kThreads>
+__device__ __forceinline__ int stage_async_count(int bytes) {
+    const int units = bytes >> 4, first = (threadIdx.x >> 6) * 64;
+    return units > first ? (units - first + kThreads - 1) / kThreads : 0;
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding (n wave-uniform).
+// Vector memory operations complete in issue order, so this waits for everything issued before
+// the n most recent ones. Counts above 15 fall back to waiting for all.
+__device__ __forceinline__ void vm_wait_le(int n) {
+    switch (n) {
+#define MOE_VMW(i) case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
+        MOE_VMW(1) MOE_VMW(2) MOE_VMW(3) MOE_VMW(4) MOE_VMW(5) MOE_VMW(6) MOE_VMW(7) MOE_VMW(8)
+        MOE_VMW(9) MOE_VMW(10) MOE_VMW(11) MOE_VMW(12) MOE_VMW(13) MOE_VMW(14) MOE_VMW(15)
+#undef MOE_VMW
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// ------------------------------------------------------------------- optional kernel timing
+struct KernelProfile {
+    int kernel = MOE_KERNEL_NONE;
+    hipEvent_t *starts = nullptr;
+    hipEvent_t *stops = nullptr;
+    int n = 0;
+    int next = 0;
+};
+extern KernelProfile g_profile;
+
+inline void prof_start(int id, hipStream_t s) {
+    if (g_profile.kernel == id && g_profile.next < g_profile.n)
+        (void)hipEventRecord(g_profile.starts[g_profile.next], s);
+}
+inline void prof_stop(int id, hipStream_t s) {
+    if (g_profile.kernel == id && g_profile.next < g_profile.n) {
+        (void)hipEventRecord(g_profile.stops[g_profile.next], s);
+        g_profile.next++;
+    }
+}
+
 // ----------------------------------------------------------------------------- host launchers
 // Each returns a MOE_* status; arguments have been validated by the ABI layer.
 

@@ -87,3 +87,11 @@ def test_streams_are_independent_and_reproducible():
     assert np.array_equal(a["x"], b["x"]) and np.array_equal(a["ids"], b["ids"])
     c = gen.make_workload("tiny_decode", 1, seed=9, with_banks=False)
     assert not np.array_equal(a["x"], c["x"])
+
+
+def test_route_union_rotated_disjoint_windows():
+    a = gen.route_union_rotated(2, 6, 10, 512, 60, 0)
+    b = gen.route_union_rotated(2, 6, 10, 512, 60, 1)
+    assert np.unique(a).size == 60 and np.unique(b).size == 60
+    assert np.intersect1d(a, b).size == 0
+    assert all(np.unique(r).size == 10 for r in a)

@@ -159,3 +159,56 @@ def test_zero_tokens_is_noop():
     assert np.all(off == 0) and np.all(cnt == 0)
     assert moe.moe_ffn_nvfp4(dc.x, dc.w, dc.offsets, dc.pair_ids, dc.active, dc.counts, dc.gate,
                              dc.up, dc.down, 0, 2, 3, 256, 64, dc.y, 0, dc.ws, dc.ws_bytes) == moe.MOE_OK
+
+
+# ---------------------------------------------------------------------------- FFN: prefill path
+
+PREFILL_SMALL = [
+    # seed, T, k, E, H, F, scales, nonlocal fraction, expert base, fused
+    (11, 3, 2, 4, 256, 64, "all", 0.0, 0, False),
+    (12, 150, 2, 2, 256, 128, "all", 0.0, 0, True),      # > 128 pairs per expert: several M tiles
+    (13, 70, 4, 9, 512, 192, "all", 0.3, 2, False),
+    (14, 40, 8, 5, 768, 64, "pow2", 0.0, 0, False),      # duplicates within tokens
+    (15, 300, 1, 1, 256, 320, "all", 0.0, 0, False),     # one expert, 300 pairs: ragged last tile
+]
+
+
+@pytest.mark.parametrize("seed,T,k,E,H,F,scales,frac,base,fused", PREFILL_SMALL)
+def test_prefill_small(seed, T, k, E, H, F, scales, frac, base, fused):
+    _print_case("prefill_small", seed=seed, T=T, k=k, E=E, H=H, F=F, frac=frac)
+    case = gen.make_random_case(seed, T, k, E, H, F, scales=scales, nonlocal_frac=frac,
+                                expert_base=base, fused=fused)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_PREFILL)
+    assert_parity(y, oracle.ffn_union(case), "prefill_small")
+
+
+@pytest.mark.parametrize("name,T,n_check", [("skewed_prefill", 512, 24),
+                                            ("skewed_prefill", 4096, 16),
+                                            ("full_prefill", 4096, 12),
+                                            ("e256_plateau", 128, 12)])
+def test_prefill_workloads(name, T, n_check):
+    """Full-size prefill workloads (and the E256 decode shape forced through the GEMM path),
+    compared on sampled tokens, always including the last token."""
+    _print_case("prefill_workload", name=name, T=T)
+    case = _workload(name, T)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_PREFILL)
+    tok = np.random.default_rng(T + 1).choice(T, size=n_check, replace=False)
+    tok[0] = T - 1
+    ref = oracle.ffn_per_slot(case, tokens=tok)
+    assert_parity(y[tok], ref, name)
+
+
+def test_prefill_deterministic_and_matches_decode():
+    case = gen.make_random_case(41, 64, 4, 6, 512, 128, nonlocal_frac=0.1)
+    dc = DeviceCase(case)
+    hashes = set()
+    for _ in range(5):
+        y = dc.run(moe.MOE_PATH_PREFILL)
+        hashes.add(hashlib.sha256(y.tobytes()).hexdigest())
+    assert len(hashes) == 1
+    yd = dc.run(moe.MOE_PATH_DECODE)
+    ref = oracle.ffn_union(case)
+    assert_parity(y, ref, "prefill")
+    assert_parity(yd, ref, "decode")
