@@ -49,6 +49,29 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// DPP lane moves (VALU, no LDS round trip). CTRL is the dpp_ctrl encoding: 0xB1 / 0x4E swap
+// lanes 1-apart / 2-apart inside each quad, 0x141 mirrors each 8-lane half row, 0x140 mirrors
+// each 16-lane row, 0x142 broadcasts lane 15 of a row into the next row (rows in ROW_MASK).
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, ROW_MASK, 0xf, false));
+}
+// Sum over each aligned group of 8 lanes; every lane of the group receives the sum.
+__device__ __forceinline__ float sum8_dpp(float v) {
+    v += dpp_mov<0xB1>(v);
+    v += dpp_mov<0x4E>(v);
+    v += dpp_mov<0x141>(v);
+    return v;
+}
+// Sum over each 32-lane half wave; lanes 16..31 and 48..63 receive their half's sum.
+__device__ __forceinline__ float sum32_dpp(float v) {
+    v = sum8_dpp(v);
+    v += dpp_mov<0x140>(v);          // 16-lane rows
+    v += dpp_mov<0x142, 0xA>(v);     // row 0 into row 1, row 2 into row 3
+    return v;
+}
+
 // Asynchronous copy of `bytes` (a multiple of 16) from 16-byte aligned global memory into
 // 16-byte aligned LDS with the gfx950 direct-to-LDS load (global_load_lds_dwordx4): wave w moves
 // 64 consecutive 16-byte units per instruction, lane i landing at the wave's LDS base + 16*i, so
