@@ -26,6 +26,41 @@ sys.path.insert(0, ROOT)
 METRIC = "routed-MoE layer µs + HBM GB/s (% of 8 TB/s) at T=1..128; TFLOP/s at T=4096"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+COPY_BYTES = 1 << 30
+
+# HBM traffic of the dominant kernel, per launch, from two rocprofv3 --pmc passes over
+# `bench.py --steps 20 --warmup 5 --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch, mean over the dispatches). Each counter is scaled by what it reads for
+# `bench.py --copy-calib` (a 1 GiB copy): FETCH_SIZE read 524301 KiB for 1048576 KiB moved, so x2.0;
+# WRITE_SIZE read 1048576 KiB, so x1.0. Keyed by the SHA-256 of the kernel's sources: once they
+# change, the entry no longer applies and traffic is reported as null until measured again.
+FETCH_SCALE = 1048576.0 / 524301.2
+WRITE_SCALE = 1.0
+TRAFFIC = {
+    ("gu_decode_kernel", "verify_chunk", 6, 60): {
+        "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
+                    "routed_moe_expert_amd/csrc/moe_internal.h"],
+        "sha256": "013e0503fa19c6b9c0ca8fac3d9dd8c2b8551bbe73632c0ce43b7651a6cec9db",
+        "fetch_kib": 54186.4, "write_kib": 161.9,
+    },
+}
+
+
+def measured_traffic(kname, workload, T, U):
+    """Calibrated HBM bytes per launch of `kname`, or None if not measured for these sources."""
+    import hashlib
+    ent = TRAFFIC.get((kname, workload, T, U))
+    if ent is None:
+        return None
+    h = hashlib.sha256()
+    for f in ent["sources"]:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != ent["sha256"]:
+        return None
+    fetch = ent["fetch_kib"] * 1024 * FETCH_SCALE
+    write = ent["write_kib"] * 1024 * WRITE_SCALE
+    return {"bytes": fetch + write, "fetch_bytes": fetch, "write_bytes": write}
 
 
 def _hip():
@@ -51,7 +86,20 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="reuse one routing (cache-warm numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scale for HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration(torch):
+    """A plain copy of known size: it reads and writes COPY_BYTES per launch, so what a
+    FETCH_SIZE / WRITE_SIZE counter reads for it converts that counter to bytes."""
+    src = torch.full((COPY_BYTES,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": COPY_BYTES, "launches": 5}), flush=True)
 
 
 DEFAULT_T = {"verify_chunk": 6, "tiny_decode": 1, "e256_plateau": 128, "skewed_prefill": 4096,
@@ -118,6 +166,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calib:
+        copy_calibration(torch)
+        return
 
     import gen
     import routed_moe_expert_amd as moe
@@ -223,7 +275,11 @@ def main():
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": gu_flops,
                 "avg_launch_us": k_avg_s * 1e6, "launches": len(kms)}
         roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    tr = measured_traffic(kname, D["name"], T, D["U"] if D["name"] == "verify_chunk" else None)
+    roof["traffic"] = tr["bytes"] if tr else None
+    if tr:
+        roof["traffic_detail"] = tr
+        roof["traffic_over_algorithmic"] = tr["bytes"] / (gu_bytes if decode else float("nan"))
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -73,7 +73,9 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
     FfnArgs a{x, topk_w, offsets, pair_ids, active, counts, gate, up, down, T, k, E, H, F, y,
               ws, ws_bytes};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (path == MOE_PATH_AUTO) path = (T <= 128) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    // AUTO: the decode path for up to 128 tokens where its slices fit, else the GEMM path
+    if (path == MOE_PATH_AUTO)
+        path = (T <= 128 && decode_supported(a)) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
     return path == MOE_PATH_DECODE ? launch_decode(a, s) : launch_prefill(a, s);
 }
 

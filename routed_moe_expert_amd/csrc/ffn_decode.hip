@@ -2,25 +2,38 @@
 //
 // The union gather (moe_union_probe.rs: read each distinct expert's NVFP4 bytes once per call
 // instead of once per routed slot): work items are (active expert, tile of weight rows); each
-// item's NVFP4 tile is read from HBM once and run against every token routed to that expert,
-// whose rows are staged in LDS once per expert.
+// item's NVFP4 tile is read from HBM once and contracted against every token routed to that
+// expert on the matrix cores, 16 tokens per MFMA column tile, so the cost of an item does not
+// grow with the expert's token count up to 16.
 //
-//   gu_decode: items of 8 gate rows + the 8 matching up rows. Each thread takes one row and
-//              every 16th scale group of it, decodes E2M1 pairs to bf16 in registers
-//              (v_cvt_scalef32_pk_bf16_fp4, exact), forms 16-weight partial dot products with
-//              v_dot2_f32_bf16 against the staged activations, scales each partial by its
-//              UE4M3 group scale, and the 16 threads of a row reduce with lane shuffles.
-//              The epilogue applies SiLU(g) * u and writes h (fp32) in CSR pair order.
-//   dn_decode: items of 64 down rows, h rows staged in LDS as fp32, E2M1 pairs decoded to fp32
-//              (v_cvt_scalef32_pk_f32_fp4), fp32 FMAs; writes the per-pair down output ypair
-//              (fp32) at row p = t*k + j of its pair.
+//   gu_decode: items of 8 gate rows + the 8 matching up rows = one 16-row MFMA A tile. The
+//              eight waves split K = hidden into eight slices. Each lane decodes the E2M1 codes
+//              of one row and one 16-weight scale group to f16 (v_cvt_scalef32_pk_f16_fp4) and
+//              multiplies in the UE4M3 group scale (v_pk_mul_f16); both steps are exact, since
+//              every E2M1 x UE4M3 product is an f16 value. The B operand is the expert's token
+//              rows of x, held in registers as f16 for the whole expert: bf16 -> f16 is exact
+//              once each (token, K slice) is scaled by a power of two that brings its largest
+//              magnitude into [2^14, 2^15). v_mfma_f32_16x16x32_f16 accumulates in fp32; the
+//              slices are unscaled, summed across the waves through LDS, and the epilogue
+//              writes h = SiLU(g) * u (fp32) in CSR pair order.
+//   dn_decode: items of 16*RT down rows; RT row tiles x (8/RT) K slices of ff over the eight
+//              waves. B is the expert's h rows, scaled per (pair, K slice) and split into
+//              f16 hi + lo (about 22 significant bits), two MFMAs per step. Slices are summed
+//              through LDS into the per-pair rows ypair (row = pair id).
 //   combine:   y[t] = sum over t's local slots in ascending j of w[t,j] * ypair[t*k + j]; the
 //              pair -> CSR slot map only says which slots are local.
 //
-// Both FFN kernels are persistent: a grid of at most two 512-thread workgroups per CU splits the
+// MFMA operand layout (v_mfma_f32_16x16x32_*): lane l supplies row l%16 of A and column l%16 of
+// B, each with 8 consecutive reduction indices of group l/16; it receives rows 4*(l/16)..+3 of
+// column l%16 of the result. The reduction order is free, so K step s of NVFP4 block b gives
+// lane group q the weights 16q + 8s .. 16q + 8s + 7 of the block: one scale group per lane and
+// two steps per block.
+//
+// Both FFN kernels are persistent: a grid of one or two 512-thread workgroups per CU splits the
 // (expert, tile) items into contiguous ranges, read from the device CSR (nothing is read back on
-// the host). Tiles stream through three LDS buffers with direct-to-LDS loads, two tiles in
-// flight while one is computed.
+// the host). Tiles stream through a ring of LDS buffers with direct-to-LDS loads (three per
+// workgroup with two workgroups per CU, up to six with one), all but one in flight while one is
+// computed.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -28,335 +41,424 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 512;          // 8 waves: 4 per SIMD with two workgroups per CU
+constexpr int kThreads = 256;          // 4 waves; two workgroups per CU
+constexpr int kWaves = kThreads / 64;
+constexpr int kCols = 16;              // token columns per MFMA tile
 constexpr int kGuO = 8;                // output features per gu item: 8 gate rows + 8 up rows
-constexpr int kGuLanes = 32;           // lanes per weight row: wave o holds feature o, its gate
-                                       // row in lanes 0..31 and its up row in lanes 32..63
-constexpr int kDnRows = 64;            // down rows per dn item
-constexpr int kDnLanes = kThreads / kDnRows;         // 8 lanes per down row
-constexpr int kNBuf = 3;               // weight tiles in LDS: one computed, two in flight
-constexpr int kWgPerCu = 2;
 constexpr int kCUs = 256;
+constexpr int kMaxGuBlocks = 16;       // NVFP4 blocks per wave slice: hidden <= 4 * 16 * 64
+constexpr int kMaxDnBlocks = 10;       // ... ff <= 4 * 10 * 64
+constexpr int kRedFloats = kWaves * kCols * 16;      // one set of per-wave 16x16 fp32 partials
+constexpr int kRedBytes = 2 * kRedFloats * 4;        // two sets (double-buffered)
 
-// 16 E2M1 codes (two code dwords) -> 8 bf16 pairs, exact.
-__device__ __forceinline__ void e2m1x16_to_bf16(uint32_t c0, uint32_t c1, uint32_t (&w)[8]) {
-    w[0] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(c0));
-    w[1] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(c0));
-    w[2] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(c0));
-    w[3] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(c0));
-    w[4] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<0>(c1));
-    w[5] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<1>(c1));
-    w[6] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<2>(c1));
-    w[7] = __builtin_bit_cast(uint32_t, e2m1x2_to_bf16<3>(c1));
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+
+// 8 E2M1 codes (one code dword, low nibble first) times the group scale S -> 8 f16, exact.
+__device__ __forceinline__ f16x8_t dequant8(uint32_t c, f16x2_t S) {
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * S;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * S;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * S;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * S;
+    return __builtin_bit_cast(f16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, p0),
+                                               __builtin_bit_cast(uint32_t, p1),
+                                               __builtin_bit_cast(uint32_t, p2),
+                                               __builtin_bit_cast(uint32_t, p3)});
 }
 
-__device__ __forceinline__ float dot16(const uint32_t (&w)[8], const u32x4_t &xa, const u32x4_t &xb) {
-    float p = 0.f;
-    p = dot2_bf16(w[0], xa[0], p);
-    p = dot2_bf16(w[1], xa[1], p);
-    p = dot2_bf16(w[2], xa[2], p);
-    p = dot2_bf16(w[3], xa[3], p);
-    p = dot2_bf16(w[4], xb[0], p);
-    p = dot2_bf16(w[5], xb[1], p);
-    p = dot2_bf16(w[6], xb[2], p);
-    p = dot2_bf16(w[7], xb[3], p);
-    return p;
+// UE4M3 scale byte -> f16 pair (exact: every finite UE4M3 value is a normal f16).
+__device__ __forceinline__ f16x2_t scale_f16x2(uint32_t byte) {
+    const _Float16 s = (_Float16)ue4m3_to_f32(byte);
+    return f16x2_t{s, s};
 }
 
-// One gu item: thread (o, sub) accumulates the gate row and the up row of feature o over scale
-// groups sub, sub+32, ... against the mt staged token rows; each x load serves both rows.
-// GPL > 0: every lane has exactly GPL groups (H = 512*GPL) and the loop is fully unrolled, so
-// all of an item's LDS reads issue before the first wait; GPL = 0: any H, runtime loop.
-// One weight row (this lane's) against the mt staged token rows over scale groups sub, sub+32,
-// ... GPL > 0: every lane has exactly GPL groups (H = 512*GPL) and the loop is fully unrolled,
-// so all of an item's LDS reads issue before the first wait; GPL = 0: any H, runtime loop.
-template <int MT, int GPL>
-__device__ __forceinline__ void gu_row_dot(const uint8_t *row, const uint16_t *xbuf, int sub,
-                                           int H, int mt, float (&acc)[MT]) {
+__device__ __forceinline__ f32x4_t mfma16(f16x8_t a, f16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Lane-group (q) part of one NVFP4 block of one row, as the A operands of the block's two K
+// steps.
+__device__ __forceinline__ void load_a(const uint8_t *blk, int q, f16x8_t &a0, f16x8_t &a1) {
+    const f16x2_t S = scale_f16x2(blk[q]);
+    const uint32_t *c = reinterpret_cast<const uint32_t *>(blk + 4 + 8 * q);
+    a0 = dequant8(c[0], S);
+    a1 = dequant8(c[1], S);
+}
+
+// Max over the four lanes of a column (lanes n, n+16, n+32, n+48).
+__device__ __forceinline__ float colmax(float v) {
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+
+// Power-of-two exponent s such that mx * 2^-s lies in [2^14, 2^15) (0 for mx = 0).
+__device__ __forceinline__ int pick_scale(float mx) {
+    int e = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e);   // mx = f * 2^e, f in [0.5, 1)
+    return mx > 0.f ? e - 15 : 0;
+}
+
+// B operands of one token column for a K slice of NB blocks starting at blk0: lane (n, q) holds
+// x[64 b + 16 q .. +15] of its token for every block b of the slice, as f16 scaled by 2^-s with
+// s chosen per (token, slice); returns s. Absent tokens (row == nullptr) and blocks past the row
+// give zeros. The raw bf16 words are converted in place (same register footprint).
+template <int NB>
+__device__ __forceinline__ int load_x_operands(u32x4_t (&xb)[NB][2], const uint16_t *row, int blk0,
+                                               int nblk, int q) {
 #pragma unroll
-    for (int i = 0; i < MT; i++) acc[i] = 0.f;
-    auto group = [&](int g) {
-        const int boff = (g >> 2) * kBlockBytes, j = g & 3;
-        const float S = ue4m3_to_f32(row[boff + j]);
-        const uint32_t *c = reinterpret_cast<const uint32_t *>(row + boff + 4 + 8 * j);
-        uint32_t w[8];
-        e2m1x16_to_bf16(c[0], c[1], w);
-#pragma unroll
-        for (int i = 0; i < MT; i++) {
-            if (i < mt) {
-                const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(xbuf + i * H + g * kGroup);
-                acc[i] = fmaf(S, dot16(w, xr[0], xr[1]), acc[i]);
-            }
-        }
-    };
-    if constexpr (GPL > 0 && MT == 1) {
-#pragma unroll
-        for (int it = 0; it < GPL; it++) group(sub + it * kGuLanes);
-    } else if constexpr (GPL > 0) {   // two token rows: unroll less to stay within 128 VGPRs
-#pragma unroll 2
-        for (int it = 0; it < GPL; it++) group(sub + it * kGuLanes);
-    } else {
-        const int groups = H / kGroup;
-#pragma nounroll
-        for (int g = sub; g < groups; g += kGuLanes) group(g);
+    for (int j = 0; j < NB; j++) {
+        const bool in = row != nullptr && blk0 + j < nblk;
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(row + 64 * (blk0 + j) + 16 * q);
+        xb[j][0] = in ? src[0] : u32x4_t{0, 0, 0, 0};
+        xb[j][1] = in ? src[1] : u32x4_t{0, 0, 0, 0};
     }
+    uint32_t amax = 0;   // |x| as bf16 bits: ordered like the magnitudes for finite values
+#pragma unroll
+    for (int j = 0; j < NB; j++)
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                amax = max(amax, max(xb[j][h][i] & 0x7fffu, (xb[j][h][i] >> 16) & 0x7fffu));
+    const int s = pick_scale(colmax(__uint_as_float(amax << 16)));
+    const float inv = ldexpf(1.0f, -s);
+#pragma unroll
+    for (int j = 0; j < NB; j++)
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t w = xb[j][h][i];
+                const f16x2_t v = {(_Float16)(__uint_as_float(w << 16) * inv),
+                                   (_Float16)(__uint_as_float(w & 0xffff0000u) * inv)};
+                xb[j][h][i] = __builtin_bit_cast(uint32_t, v);
+            }
+    return s;
 }
 
-// One down row (this lane's) against the mt staged fp32 h rows over scale groups sub, sub+8, ...
-template <int MT, int GPL>
-__device__ __forceinline__ void dn_row_dot(const uint8_t *row, const float *hbuf, int sub, int F,
-                                           int mt, float (&acc)[MT]) {
+// B operands of one h column (fp32, CSR row of a pair) for a K slice of ff: hi + lo f16 pairs,
+// scaled by 2^-s per (pair, slice); returns s. The fp32 words land in the hi/lo registers
+// (hi[j] = values 0..7 of block j, lo[j] = values 8..15) and are converted one block at a time.
+template <int NB>
+__device__ __forceinline__ int load_h_operands(u32x4_t (&hi)[NB][2], u32x4_t (&lo)[NB][2],
+                                               const float *row, int blk0, int nblk, int q) {
 #pragma unroll
-    for (int i = 0; i < MT; i++) acc[i] = 0.f;
-    auto group = [&](int g) {
-        const int boff = (g >> 2) * kBlockBytes, j = g & 3;
-        const float S = ue4m3_to_f32(row[boff + j]);
-        const uint32_t *c = reinterpret_cast<const uint32_t *>(row + boff + 4 + 8 * j);
-        f32x2_t w[8];
-        w[0] = e2m1x2_to_f32<0>(c[0]); w[1] = e2m1x2_to_f32<1>(c[0]);
-        w[2] = e2m1x2_to_f32<2>(c[0]); w[3] = e2m1x2_to_f32<3>(c[0]);
-        w[4] = e2m1x2_to_f32<0>(c[1]); w[5] = e2m1x2_to_f32<1>(c[1]);
-        w[6] = e2m1x2_to_f32<2>(c[1]); w[7] = e2m1x2_to_f32<3>(c[1]);
-#pragma unroll
-        for (int i = 0; i < MT; i++) {
-            if (i < mt) {
-                const f32x4_t *hr = reinterpret_cast<const f32x4_t *>(hbuf + i * F + g * kGroup);
-                float p = 0.f;
-#pragma unroll
-                for (int v = 0; v < 4; v++) {
-                    const f32x4_t hv = hr[v];
-                    p = fmaf(w[2 * v][0], hv[0], p);
-                    p = fmaf(w[2 * v][1], hv[1], p);
-                    p = fmaf(w[2 * v + 1][0], hv[2], p);
-                    p = fmaf(w[2 * v + 1][1], hv[3], p);
-                }
-                acc[i] = fmaf(S, p, acc[i]);
-            }
-        }
-    };
-    if constexpr (GPL > 0 && MT == 1) {
-#pragma unroll
-        for (int it = 0; it < GPL; it++) group(sub + it * kDnLanes);
-    } else if constexpr (GPL > 0) {   // two fp32 h rows: unroll less to stay within 128 VGPRs
-#pragma unroll 2
-        for (int it = 0; it < GPL; it++) group(sub + it * kDnLanes);
-    } else {
-        const int groups = F / kGroup;
-#pragma nounroll
-        for (int g = sub; g < groups; g += kDnLanes) group(g);
+    for (int j = 0; j < NB; j++) {
+        const bool in = row != nullptr && blk0 + j < nblk;
+        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(row + 64 * (blk0 + j) + 16 * q);
+        hi[j][0] = in ? src[0] : u32x4_t{0, 0, 0, 0};
+        hi[j][1] = in ? src[1] : u32x4_t{0, 0, 0, 0};
+        lo[j][0] = in ? src[2] : u32x4_t{0, 0, 0, 0};
+        lo[j][1] = in ? src[3] : u32x4_t{0, 0, 0, 0};
     }
+    float mx = 0.f;
+#pragma unroll
+    for (int j = 0; j < NB; j++)
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(hi[j][h][i])),
+                                     fabsf(__uint_as_float(lo[j][h][i]))));
+    const int s = pick_scale(colmax(mx));
+    const float inv = ldexpf(1.0f, -s);
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            v[i] = __uint_as_float(hi[j][0][i]) * inv;
+            v[4 + i] = __uint_as_float(hi[j][1][i]) * inv;
+            v[8 + i] = __uint_as_float(lo[j][0][i]) * inv;
+            v[12 + i] = __uint_as_float(lo[j][1][i]) * inv;
+        }
+#pragma unroll
+        for (int st = 0; st < 2; st++)      // K step st: values 8 st .. 8 st + 7
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float f0 = v[8 * st + 2 * i], f1 = v[8 * st + 2 * i + 1];
+                const _Float16 h0 = (_Float16)f0, h1 = (_Float16)f1;
+                hi[j][st][i] = __builtin_bit_cast(uint32_t, f16x2_t{h0, h1});
+                lo[j][st][i] = __builtin_bit_cast(uint32_t, f16x2_t{(_Float16)(f0 - (float)h0),
+                                                                    (_Float16)(f1 - (float)h1)});
+            }
+    }
+    return s;
+}
+
+__device__ __forceinline__ f32x4_t unscale(f32x4_t acc, int s) {
+    return f32x4_t{ldexpf(acc[0], s), ldexpf(acc[1], s), ldexpf(acc[2], s), ldexpf(acc[3], s)};
 }
 
 // Item range of this workgroup: items are (active expert a, row tile t) in a-major order, split
 // into equal contiguous ranges over the grid, so a workgroup mostly stays on one expert and its
-// token rows are staged once.
+// token rows are loaded once.
 __device__ __forceinline__ void item_range(int total, int &i0, int &i1) {
     const int per = (total + gridDim.x - 1) / gridDim.x;
     i0 = min((int)blockIdx.x * per, total);
     i1 = min(i0 + per, total);
 }
 
-// The CSR entries a workgroup needs (its experts, their first CSR slot, pair count and first MT
-// pair ids), fetched once into LDS at kernel start: reading them per item would put a chain of
-// dependent scalar loads (active -> offsets -> pair_ids), each a round trip to memory the
-// previous kernel just wrote, in front of every tile.
+// The CSR entries a workgroup needs: its experts, their first CSR slot, pair count and first 16
+// pair ids.
 constexpr int kMaxMeta = 32;   // experts per workgroup range; grids are sized so this holds
-template <int MT>
 struct Meta {
-    int e[kMaxMeta], q0[kMaxMeta], m[kMaxMeta], pid[kMaxMeta][MT];
+    int n_active;
+    int e[kMaxMeta], q0[kMaxMeta], m[kMaxMeta], pid[kMaxMeta][kCols];
 };
 
-template <int MT>
-__device__ __forceinline__ void load_meta(Meta<MT> &meta, const int32_t *active,
-                                          const int32_t *offsets, const int32_t *pair_ids,
-                                          int a_first, int na) {
+constexpr int kPairCap = 4096;   // pair ids read whole at start up to this many
+
+// LDS scratch of load_plan: the active list, the offsets and (up to kPairCap) the pair ids.
+inline size_t plan_scratch_bytes(int E, int P) {
+    return 4 * (2 * (size_t)E + 1 + (P <= kPairCap ? P : 0));
+}
+
+// This workgroup's item range and CSR entries. The counts, the whole active list, the whole
+// offsets array and (when short) all pair ids are fetched at once into LDS scratch, so start up
+// costs one round trip to memory instead of the chain counts -> active -> offsets -> pair ids.
+__device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restrict__ counts,
+                          const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
+                          const int32_t *__restrict__ pair_ids, int E, int P, int tiles, int &i0,
+                          int &i1, int &a_first) {
     const int tid = threadIdx.x;
+    int32_t *s_act = scratch, *s_off = scratch + E, *s_pair = scratch + 2 * E + 1;
+    const bool pairs_in_lds = P <= kPairCap;
+    if (tid == 0) meta.n_active = counts[0];
+    for (int j = tid; j < E; j += kThreads) s_act[j] = active[j];
+    for (int j = tid; j <= E; j += kThreads) s_off[j] = offsets[j];
+    if (pairs_in_lds)
+        for (int j = tid; j < P; j += kThreads) s_pair[j] = pair_ids[j];
+    lds_barrier();
+    item_range(meta.n_active * tiles, i0, i1);
+    a_first = i0 / tiles;
+    const int na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
     if (tid < na) {
-        const int e = active[a_first + tid];
-        const int q0 = offsets[e], m = offsets[e + 1] - q0;
+        const int e = s_act[a_first + tid];
+        const int q0 = s_off[e], m = s_off[e + 1] - q0;
         meta.e[tid] = e;
         meta.q0[tid] = q0;
         meta.m[tid] = m;
 #pragma unroll
-        for (int j = 0; j < MT; j++) meta.pid[tid][j] = j < m ? pair_ids[q0 + j] : 0;
+        for (int j = 0; j < kCols; j++)
+            meta.pid[tid][j] = j < m ? (pairs_in_lds ? s_pair[q0 + j] : pair_ids[q0 + j]) : 0;
     }
+    lds_barrier();
 }
 
-// Gate/up + SiLU * up over the union of active experts. Persistent workgroups stream their
-// 16-row NVFP4 tiles through kNBuf LDS buffers with direct-to-LDS loads: two tiles in flight
-// while one is computed. Tile i is awaited with "at most the next tile's loads outstanding";
-// vector-memory loads complete in issue order, so that wait also covers tile i whatever stores
-// were issued in between.
-template <int MT, int GPL>
-__global__ __launch_bounds__(kThreads, 4) void gu_decode_kernel(
+// Pair id of column n of token chunk c of expert a (chunks beyond the first read the CSR).
+__device__ __forceinline__ int chunk_pid(const Meta &meta, const int32_t *pair_ids, int a, int c,
+                                         int n) {
+    return c == 0 ? meta.pid[a][n] : pair_ids[meta.q0[a] + c * kCols + n];
+}
+
+// Gate/up + SiLU * up over the union of active experts; the four waves split K = hidden. A unit
+// of work is one item (or, past 16 tokens of an expert, one token chunk of it). Each unit has a
+// single barrier: it publishes the previous unit's partial tiles (double-buffered) and hands back
+// the previous tile's buffer; one wave (rotating) then sums the previous unit while the others
+// go on. Tile i is awaited with "at most the tiles behind it outstanding": loads complete in
+// issue order, so that wait covers tile i.
+template <int NB>
+__global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const int32_t *__restrict__ active,
     const int32_t *__restrict__ counts, const uint8_t *__restrict__ gate, int64_t gate_stride,
-    const uint8_t *__restrict__ up, int64_t up_stride, int32_t k, int32_t P, int32_t H, int32_t F,
-    float *__restrict__ h, int32_t *__restrict__ pos) {
+    const uint8_t *__restrict__ up, int64_t up_stride, int32_t k, int32_t P, int32_t E, int32_t H,
+    int32_t F, int32_t nbuf, int32_t ring_bytes, float *__restrict__ h, int32_t *__restrict__ pos) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = H / kBlockWeights * kBlockBytes;
     const int side = kGuO * rb, tile_bytes = 2 * side;
-    uint8_t *wb = smem;                                                     // [kNBuf][16 rows]
-    uint16_t *xbuf = reinterpret_cast<uint16_t *>(smem + kNBuf * tile_bytes);  // [MT][H] bf16
-    __shared__ Meta<MT> meta;
-    const int tid = threadIdx.x;
-
+    uint8_t *wb = smem;                                                // [nbuf][16 rows]
+    float *red = reinterpret_cast<float *>(smem + ring_bytes);         // [2][wave][col][16 rows]
+    __shared__ Meta meta;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, q = lane >> 4;   // A row / B column, and K group
+    const int nblk = H / kBlockWeights, blk0 = wave * NB;   // slices are whole: nblk = 4 NB
     const int tiles = F / kGuO;
-    int i0, i1;
-    item_range(counts[0] * tiles, i0, i1);
-    const int o = tid >> 6, lane = tid & 63, sub = lane & 31;
-    const int wrow = (lane < 32 ? 0 : side) + o * rb;   // this lane's row within a tile
+
+    int i0, i1, a_first;
+    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, E, P,
+              tiles, i0, i1, a_first);
     const int n_inst = 2 * stage_async_count<kThreads>(side);
-    const int a_first = i0 / tiles;
+    const int depth = nbuf - 1;   // tiles in flight while one is computed
+    // stream cursor: the next item to load (expert index, row tile, ring slot)
+    int ia = 0, it = i0 - a_first * tiles, is = 0;
+    auto issue_next = [&]() {
+        const int e = meta.e[ia];
+        uint8_t *dst = wb + is * tile_bytes;
+        stage_async<kThreads>(dst, gate + e * gate_stride + (int64_t)it * side, side);
+        stage_async<kThreads>(dst + side, up + e * up_stride + (int64_t)it * side, side);
+        if (++it == tiles) { it = 0; ++ia; }
+        if (++is == nbuf) is = 0;
+    };
+    for (int i = i0; i < min(i0 + depth, i1); i++) issue_next();
 
-    auto issue_e = [&](int i, int e) {
-        const int t = i % tiles;
-        uint8_t *dst = wb + ((i - i0) % kNBuf) * tile_bytes;
-        stage_async<kThreads>(dst, gate + e * gate_stride + (int64_t)t * side, side);
-        stage_async<kThreads>(dst + side, up + e * up_stride + (int64_t)t * side, side);
-    };
-    auto issue = [&](int i) { issue_e(i, meta.e[i / tiles - a_first]); };
-    if (i0 < i1) {
-        // the first two tiles go out before the rest of the CSR metadata is fetched
-        issue_e(i0, active[i0 / tiles]);
-        if (i0 + 1 < i1) issue_e(i0 + 1, active[(i0 + 1) / tiles]);
-        load_meta<MT>(meta, active, offsets, pair_ids, a_first,
-                      min((i1 - 1) / tiles - a_first + 1, kMaxMeta));
-        lds_barrier();
-    }
-    auto stage_x = [&](int a, int c0, int mt) {   // token rows of CSR pairs c0..c0+mt-1
-        for (int j = 0; j < mt; j++) {
-            const int p = c0 + j < MT ? meta.pid[a][c0 + j] : pair_ids[meta.q0[a] + c0 + j];
-            stage_async<kThreads>(xbuf + j * H, x + (int64_t)(p / k) * H, H * 2);
-        }
-    };
-    auto finish = [&](float (&acc)[MT], int q0, int o0, int mt) {
+    // reduction of a unit by one wave: lane -> (feature f, token column nn)
+    auto reduce = [&](const float *rp, int q0, int c, int t, int mt) {
+        for (int o = lane; o < kGuO * mt; o += 64) {
+            const int f = o & (kGuO - 1), nn = o / kGuO;
+            float g = 0.f, u = 0.f;
 #pragma unroll
-        for (int j = 0; j < MT; j++) {
-            if (j < mt) {
-                const float v = sum32_dpp(acc[j]);   // gate sum in lanes 16..31, up in 48..63
-                const float gv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                     __builtin_bit_cast(int, v), 31));
-                const float uv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
-                                     __builtin_bit_cast(int, v), 63));
-                if (lane == 0) h[(int64_t)(q0 + j) * F + o0 + o] = silu(gv) * uv;
+            for (int w = 0; w < kWaves; w++) {
+                g += rp[(w * kCols + nn) * 16 + f];
+                u += rp[(w * kCols + nn) * 16 + f + kGuO];
             }
+            h[(int64_t)(q0 + c * kCols + nn) * F + t * kGuO + f] = silu(g) * u;
         }
     };
 
-    int cur_a = -1;
+    u32x4_t xb[NB][2];
+    int xs = 0, cur_a = -1, cur_c = -1;
+    int unit = 0, p_q0 = 0, p_c = 0, p_t = 0, p_mt = 0;
+    int a = 0, t = i0 - a_first * tiles, slot = 0;   // item i: expert index, row tile, ring slot
     for (int i = i0; i < i1; i++) {
-        const int a = i / tiles - a_first, t = i % tiles;
         const int q0 = meta.q0[a], m = meta.m[a];
-        const uint8_t *wt = wb + ((i - i0) % kNBuf) * tile_bytes;
-        if (a != cur_a && m <= MT) {  // new expert: stage its token rows once xbuf is free
-            lds_barrier();
-            stage_x(a, 0, m);
-            lds_dma_wait();
-            cur_a = a;
-        } else {
-            vm_wait_le(i + 1 < i1 ? n_inst : 0);  // tile i landed; only tile i+1 outstanding
-        }
-        lds_barrier();   // tile i visible to all; everyone is done with item i-1's buffer
-        if (i + 2 < i1) issue(i + 2);
-        // one pass when the expert's rows are staged; otherwise token chunks, each restaged
-        // (which waits on all loads)
-        const bool chunked = m > MT;
-        for (int c0 = 0; c0 < m; c0 += MT) {
-            const int mt = min(MT, m - c0);
-            if (chunked) {
-                lds_barrier();
-                stage_x(a, c0, mt);
-                lds_dma_wait();
-                lds_barrier();
+        // this lane's row, at its wave's K slice
+        const uint8_t *wt = wb + slot * tile_bytes + n * rb + blk0 * kBlockBytes;
+        for (int c = 0; c * kCols < m; c++, unit++) {
+            const int mt = min(kCols, m - c * kCols);
+            if (a != cur_a || c != cur_c) {   // token rows of this chunk into registers
+                const uint16_t *row = nullptr;
+                if (n < mt) row = x + (int64_t)(chunk_pid(meta, pair_ids, a, c, n) / k) * H;
+                xs = load_x_operands<NB>(xb, row, blk0, nblk, q);
+                cur_a = a;
+                cur_c = c;
             }
-            float acc[MT];
-            gu_row_dot<MT, GPL>(wt + wrow, xbuf, sub, H, mt, acc);
-            finish(acc, q0 + c0, t * kGuO, mt);
+            if (c == 0) vm_wait_le(min(depth - 1, i1 - 1 - i) * n_inst);   // tile i landed
+            lds_barrier();   // tile i and the previous unit's partials visible to all
+            if (c == 0 && i + depth < i1) issue_next();   // into item i-1's buffer
+            if (unit > 0 && wave == (unit - 1) % kWaves)
+                reduce(red + ((unit - 1) & 1) * kRedFloats, p_q0, p_c, p_t, p_mt);
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NB; j++) {
+                f16x8_t a0, a1;
+                load_a(wt + j * kBlockBytes, q, a0, a1);
+                acc = mfma16(a0, __builtin_bit_cast(f16x8_t, xb[j][0]), acc);
+                acc = mfma16(a1, __builtin_bit_cast(f16x8_t, xb[j][1]), acc);
+            }
+            *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats + (wave * kCols + n) * 16 +
+                                         4 * q) = unscale(acc, xs);
+            p_q0 = q0;
+            p_c = c;
+            p_t = t;
+            p_mt = mt;
         }
-        if (chunked) cur_a = -1;
+        if (++t == tiles) { t = 0; ++a; }
+        if (++slot == nbuf) slot = 0;
+    }
+    if (unit > 0) {
+        lds_barrier();
+        if (wave == (unit - 1) % kWaves)
+            reduce(red + ((unit - 1) & 1) * kRedFloats, p_q0, p_c, p_t, p_mt);
     }
     // pair -> CSR slot map for the combine (not needed before it)
-    for (int q = blockIdx.x * kThreads + tid; q < P; q += gridDim.x * kThreads) pos[pair_ids[q]] = q;
+    for (int q2 = blockIdx.x * kThreads + tid; q2 < P; q2 += gridDim.x * kThreads)
+        pos[pair_ids[q2]] = q2;
 }
 
-// Down projection over the union of active experts, same streaming scheme with 64-row tiles;
-// the per-pair rows go to ypair at the pair id.
-template <int MT, int GPL>
-__global__ __launch_bounds__(kThreads, 4) void dn_decode_kernel(
+// Down projection over the union of active experts, same streaming scheme; an item is 16*RT
+// down rows, wave w takes row tile w % RT and K slice w / RT of ff. With one K slice (RT = 4,
+// ff up to 640) every wave owns whole rows and stores them from registers; otherwise the slices
+// are summed through LDS like gate/up, by all waves.
+template <int NB>
+__global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
     const int32_t *__restrict__ active, const int32_t *__restrict__ counts,
-    const uint8_t *__restrict__ down, int64_t down_stride, int32_t H, int32_t F,
-    const float *__restrict__ h, float *__restrict__ ypair) {
+    const uint8_t *__restrict__ down, int64_t down_stride, int32_t P, int32_t E, int32_t H,
+    int32_t F, int32_t RT, int32_t nbuf, int32_t ring_bytes, const float *__restrict__ h,
+    float *__restrict__ ypair) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = F / kBlockWeights * kBlockBytes;
-    const int tile_bytes = kDnRows * rb;
-    uint8_t *wb = smem;                                                     // [kNBuf][64 rows]
-    float *hbuf = reinterpret_cast<float *>(smem + kNBuf * tile_bytes);     // [MT][F]
-    __shared__ Meta<MT> meta;
-    const int tid = threadIdx.x;
+    const int rows = 16 * RT, tile_bytes = rows * rb;
+    uint8_t *wb = smem;                                                // [nbuf][rows]
+    float *red = reinterpret_cast<float *>(smem + ring_bytes);         // [2][wave][col][16 rows]
+    __shared__ Meta meta;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, q = lane >> 4;
+    const int rt = wave % RT, ks = wave / RT, KS = kWaves / RT;
+    const int nblk = F / kBlockWeights, blk0 = ks * NB;
+    const int tiles = H / rows;
 
-    const int tiles = H / kDnRows;
-    int i0, i1;
-    item_range(counts[0] * tiles, i0, i1);
+    int i0, i1, a_first;
+    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, E, P,
+              tiles, i0, i1, a_first);
     if (i0 >= i1) return;
-    const int a_first = i0 / tiles;
-    const int row = tid / kDnLanes, sub = tid % kDnLanes;   // this lane's row of the tile
     const int n_inst = stage_async_count<kThreads>(tile_bytes);
-
-    auto issue_e = [&](int i, int e) {
-        stage_async<kThreads>(wb + ((i - i0) % kNBuf) * tile_bytes,
-                              down + e * down_stride + (int64_t)(i % tiles) * tile_bytes, tile_bytes);
+    const int depth = nbuf - 1;
+    int ia = 0, it = i0 - a_first * tiles, is = 0;   // stream cursor
+    auto issue_next = [&]() {
+        const int e = meta.e[ia];
+        stage_async<kThreads>(wb + is * tile_bytes,
+                              down + e * down_stride + (int64_t)it * tile_bytes, tile_bytes);
+        if (++it == tiles) { it = 0; ++ia; }
+        if (++is == nbuf) is = 0;
     };
-    auto issue = [&](int i) { issue_e(i, meta.e[i / tiles - a_first]); };
-    issue_e(i0, active[i0 / tiles]);
-    if (i0 + 1 < i1) issue_e(i0 + 1, active[(i0 + 1) / tiles]);
-    load_meta<MT>(meta, active, offsets, pair_ids, a_first,
-                  min((i1 - 1) / tiles - a_first + 1, kMaxMeta));
-    lds_barrier();
-    auto finish = [&](float (&acc)[MT], int a, int c0, int r0, int mt) {
-#pragma unroll
-        for (int j = 0; j < MT; j++) {
-            if (j < mt) {
-                const float v = sum8_dpp(acc[j]);
-                if (sub == 0) {
-                    const int p = c0 + j < MT ? meta.pid[a][c0 + j] : pair_ids[meta.q0[a] + c0 + j];
-                    ypair[(int64_t)p * H + r0 + row] = v;
-                }
-            }
+    for (int i = i0; i < min(i0 + depth, i1); i++) issue_next();
+
+    // (row r of the item, token column nn) sums the KS slices of r's row tile
+    auto reduce = [&](const float *rp, int a, int c, int t, int mt) {
+        for (int u = tid; u < rows * mt; u += kThreads) {
+            const int r = u % rows, nn = u / rows;
+            float v = 0.f;
+            for (int s2 = 0; s2 < KS; s2++) v += rp[((s2 * RT + r / 16) * kCols + nn) * 16 + r % 16];
+            ypair[(int64_t)chunk_pid(meta, pair_ids, a, c, nn) * H + t * rows + r] = v;
         }
     };
 
-    int cur_a = -1;
+    u32x4_t hh[NB][2], hl[NB][2];
+    int hs = 0, cur_a = -1, cur_c = -1;
+    int unit = 0, p_a = 0, p_c = 0, p_t = 0, p_mt = 0;
+    int a = 0, t = i0 - a_first * tiles, slot = 0;
     for (int i = i0; i < i1; i++) {
-        const int a = i / tiles - a_first, t = i % tiles;
         const int q0 = meta.q0[a], m = meta.m[a];
-        const uint8_t *wt = wb + ((i - i0) % kNBuf) * tile_bytes;
-        if (a != cur_a && m <= MT) {
-            lds_barrier();
-            stage_async<kThreads>(hbuf, h + (int64_t)q0 * F, m * F * 4);
-            lds_dma_wait();
-            cur_a = a;
-        } else {
-            vm_wait_le(i + 1 < i1 ? n_inst : 0);
-        }
-        lds_barrier();
-        if (i + 2 < i1) issue(i + 2);
-        const bool chunked = m > MT;
-        for (int c0 = 0; c0 < m; c0 += MT) {
-            const int mt = min(MT, m - c0);
-            if (chunked) {
-                lds_barrier();
-                stage_async<kThreads>(hbuf, h + (int64_t)(q0 + c0) * F, mt * F * 4);
-                lds_dma_wait();
-                lds_barrier();
+        const uint8_t *wt = wb + slot * tile_bytes + (rt * 16 + n) * rb;
+        for (int c = 0; c * kCols < m; c++, unit++) {
+            const int mt = min(kCols, m - c * kCols);
+            if (a != cur_a || c != cur_c) {
+                const float *row = n < mt ? h + (int64_t)(q0 + c * kCols + n) * F : nullptr;
+                hs = load_h_operands<NB>(hh, hl, row, blk0, nblk, q);
+                cur_a = a;
+                cur_c = c;
             }
-            float acc[MT];
-            dn_row_dot<MT, GPL>(wt + row * rb, hbuf, sub, F, mt, acc);
-            finish(acc, a, c0, t * kDnRows, mt);
+            if (c == 0) vm_wait_le(min(depth - 1, i1 - 1 - i) * n_inst);
+            lds_barrier();
+            if (c == 0 && i + depth < i1) issue_next();
+            if (KS > 1 && unit > 0) reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < NB; j++) {
+                f16x8_t a0, a1;   // blocks past the row (last slice): zero B, any valid A
+                load_a(wt + min(blk0 + j, nblk - 1) * kBlockBytes, q, a0, a1);
+                acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hh[j][0]), acc);
+                acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hl[j][0]), acc);
+                acc = mfma16(a1, __builtin_bit_cast(f16x8_t, hh[j][1]), acc);
+                acc = mfma16(a1, __builtin_bit_cast(f16x8_t, hl[j][1]), acc);
+            }
+            acc = unscale(acc, hs);
+            if (KS == 1) {   // whole rows: lane holds rows 4q..4q+3 of token column n
+                if (n < mt) {
+                    const int p = chunk_pid(meta, pair_ids, a, c, n);
+                    *reinterpret_cast<f32x4_t *>(ypair + (int64_t)p * H + t * rows + rt * 16 +
+                                                 4 * q) = acc;
+                }
+            } else {
+                *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats +
+                                             (wave * kCols + n) * 16 + 4 * q) = acc;
+            }
+            p_a = a;
+            p_c = c;
+            p_t = t;
+            p_mt = mt;
         }
-        if (chunked) cur_a = -1;
+        if (++t == tiles) { t = 0; ++a; }
+        if (++slot == nbuf) slot = 0;
+    }
+    if (KS > 1) {
+        lds_barrier();
+        reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
     }
 }
 
@@ -443,73 +545,136 @@ int launch_combine(const float *w, const int32_t *pos, const int32_t *offsets, i
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-template <int MT, int GG, int GD>
-int launch_decode_mt(const FfnArgs &a, const DecodeWs &d, hipStream_t s) {
-    const int32_t P = a.T * a.k;
-    const int max_active = (int)std::min<int64_t>(a.E, P);
-    const size_t rbh = (size_t)row_bytes(a.H), rbf = (size_t)row_bytes(a.F);
-    const size_t gu_lds = kNBuf * 2 * kGuO * rbh + (size_t)MT * a.H * 2;
-    const size_t dn_lds = kNBuf * kDnRows * rbf + (size_t)MT * a.F * 4;
-    if (gu_lds + sizeof(Meta<MT>) > 160 * 1024 || dn_lds + sizeof(Meta<MT>) > 160 * 1024)
-        return MOE_ESHAPE;
-    static bool attrs = false;
-    if (!attrs) {
-        if (!set_lds_attr(reinterpret_cast<const void *>(gu_decode_kernel<MT, GG>), 160 * 1024) ||
-            !set_lds_attr(reinterpret_cast<const void *>(dn_decode_kernel<MT, GD>), 160 * 1024))
-            return MOE_ELAUNCH;
-        attrs = true;
-    }
-    const int grid_cap = kWgPerCu * kCUs;
-    const int gu_tiles = a.F / kGuO, dn_tiles = a.H / kDnRows;
-    const int gu_grid = (int)std::min<int64_t>(grid_cap, (int64_t)max_active * gu_tiles);
-    const int dn_grid = (int)std::min<int64_t>(grid_cap, (int64_t)max_active * dn_tiles);
-    // experts one workgroup's item range can touch must fit its LDS metadata table
-    auto max_experts = [&](int tiles, int grid) {
-        const int64_t per = ((int64_t)max_active * tiles + grid - 1) / grid;
-        return (per - 1) / tiles + 2;
-    };
-    if (max_experts(gu_tiles, gu_grid) > kMaxMeta || max_experts(dn_tiles, dn_grid) > kMaxMeta)
-        return MOE_ESHAPE;
-    prof_start(MOE_KERNEL_GU_DECODE, s);
-    hipLaunchKernelGGL((gu_decode_kernel<MT, GG>), dim3(gu_grid), dim3(kThreads), gu_lds, s, a.x,
-                       a.offsets, a.pair_ids, a.active, a.counts, a.gate.base,
-                       a.gate.expert_stride, a.up.base, a.up.expert_stride, a.k, P, a.H, a.F, d.h,
-                       d.pos);
-    prof_stop(MOE_KERNEL_GU_DECODE, s);
-    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
-    prof_start(MOE_KERNEL_DN_DECODE, s);
-    hipLaunchKernelGGL((dn_decode_kernel<MT, GD>), dim3(dn_grid), dim3(kThreads), dn_lds, s,
-                       a.offsets, a.pair_ids, a.active, a.counts, a.down.base,
-                       a.down.expert_stride, a.H, a.F, d.h, d.ypair);
-    prof_stop(MOE_KERNEL_DN_DECODE, s);
-    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
-    return launch_combine(a.w, d.pos, a.offsets, a.E, d.ypair, a.T, a.k, a.H, a.y, s);
+namespace {
+
+constexpr size_t kLds = 160 * 1024;
+constexpr int kMaxBuf = 6;
+
+// Experts that one workgroup's contiguous item range can touch.
+int64_t max_experts(int64_t n_items, int64_t tiles, int grid) {
+    const int64_t per = (n_items + grid - 1) / grid;
+    return (per - 1) / tiles + 2;
 }
 
-// Compile-time groups per lane for the common widths (gate/up: H/512 in {5, 8}, down: F/128 in
-// {5, 10}), else 0 (runtime loop). Two staged token rows per expert only where the unrolled
-// kernels stay within 256 VGPRs (two waves per SIMD); elsewhere one.
-template <int GG, int GD>
-int launch_decode_shape(const FfnArgs &a, const DecodeWs &d, hipStream_t s) {
-    if (a.T >= 2) return launch_decode_mt<2, GG, GD>(a, d, s);
-    return launch_decode_mt<1, GG, GD>(a, d, s);
-}
-template <int GG>
-int launch_decode_gd(const FfnArgs &a, const DecodeWs &d, hipStream_t s) {
-    switch (a.F % 128 ? 0 : a.F / 128) {
-    case 5: return launch_decode_shape<GG, 5>(a, d, s);
-    case 10: return launch_decode_shape<GG, 10>(a, d, s);
-    default: return launch_decode_shape<GG, 0>(a, d, s);
+// Two workgroups per CU with three tile buffers each when the LDS holds them, else one with as
+// many as fit (at most kMaxBuf). The ring region also holds the start-up scratch, so it is at
+// least that large. Returns the dynamic LDS bytes (0: does not fit).
+size_t ring_plan(size_t tile, size_t scratch, int &nbuf, int &ring_bytes, int &wgs) {
+    const size_t fixed = kRedBytes + sizeof(Meta);
+    const size_t scr = (scratch + 15) & ~size_t(15);
+    if (2 * (std::max(3 * tile, scr) + fixed) <= kLds) {
+        nbuf = 3;
+        wgs = 2;
+    } else {
+        if (kLds < fixed + 2 * tile) return 0;
+        nbuf = (int)std::min<size_t>(kMaxBuf, (kLds - fixed) / tile);
+        wgs = 1;
     }
+    const size_t ring = std::max(nbuf * tile, scr);
+    if (ring + fixed > kLds) return 0;
+    ring_bytes = (int)ring;
+    return ring + kRedBytes;
+}
+
+template <int NB>
+int launch_gu(const FfnArgs &a, const DecodeWs &d, int max_active, hipStream_t s) {
+    auto kern = gu_decode_kernel<NB>;
+    const int32_t P = a.T * a.k;
+    int nbuf, ring_bytes, wgs;
+    const size_t lds = ring_plan(2 * kGuO * (size_t)row_bytes(a.H), plan_scratch_bytes(a.E, P),
+                                 nbuf, ring_bytes, wgs);
+    if (!lds) return MOE_ESHAPE;
+    static bool attr = false;
+    if (!attr) {
+        if (!set_lds_attr(reinterpret_cast<const void *>(kern), kLds)) return MOE_ELAUNCH;
+        attr = true;
+    }
+    const int tiles = a.F / kGuO;
+    const int grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * tiles);
+    if (max_experts((int64_t)max_active * tiles, tiles, grid) > kMaxMeta) return MOE_ESHAPE;
+    prof_start(MOE_KERNEL_GU_DECODE, s);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.x, a.offsets, a.pair_ids,
+                       a.active, a.counts, a.gate.base, a.gate.expert_stride, a.up.base,
+                       a.up.expert_stride, a.k, P, a.E, a.H, a.F, nbuf, ring_bytes, d.h, d.pos);
+    prof_stop(MOE_KERNEL_GU_DECODE, s);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+template <int NB>
+int launch_dn(const FfnArgs &a, const DecodeWs &d, int max_active, int RT, hipStream_t s) {
+    auto kern = dn_decode_kernel<NB>;
+    const int32_t P = a.T * a.k;
+    const int rows = 16 * RT;
+    int nbuf, ring_bytes, wgs;
+    const size_t lds = ring_plan(rows * (size_t)row_bytes(a.F), plan_scratch_bytes(a.E, P), nbuf,
+                                 ring_bytes, wgs);
+    if (!lds) return MOE_ESHAPE;
+    static bool attr = false;
+    if (!attr) {
+        if (!set_lds_attr(reinterpret_cast<const void *>(kern), kLds)) return MOE_ELAUNCH;
+        attr = true;
+    }
+    const int tiles = a.H / rows;
+    const int grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * tiles);
+    if (max_experts((int64_t)max_active * tiles, tiles, grid) > kMaxMeta) return MOE_ESHAPE;
+    prof_start(MOE_KERNEL_DN_DECODE, s);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.offsets, a.pair_ids, a.active,
+                       a.counts, a.down.base, a.down.expert_stride, P, a.E, a.H, a.F, RT, nbuf,
+                       ring_bytes, d.h, d.ypair);
+    prof_stop(MOE_KERNEL_DN_DECODE, s);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+// Gate/up: the four waves split hidden into slices of NB = ceil(blocks / 4) NVFP4 blocks.
+// Down: the smallest K split KS in {1, 2, 4} with at most kMaxDnBlocks blocks per slice, and
+// RT = 4 / KS row tiles per item; H must hold whole items, and two tiles plus the start-up
+// scratch must fit in LDS.
+int decode_plan(const FfnArgs &a, int &nb_gu, int &nb_dn, int &rt) {
+    const int bh = a.H / kBlockWeights, bf = a.F / kBlockWeights;
+    nb_gu = (bh + kWaves - 1) / kWaves;
+    int ks = 1;
+    while (ks < kWaves && (bf + ks - 1) / ks > kMaxDnBlocks) ks *= 2;
+    nb_dn = (bf + ks - 1) / ks;
+    rt = kWaves / ks;
+    if (nb_gu > kMaxGuBlocks || nb_dn > kMaxDnBlocks || a.H % (16 * rt)) return MOE_ESHAPE;
+    const int32_t P = a.T * a.k;
+    int nbuf, ring, wgs;
+    if (!ring_plan(2 * kGuO * (size_t)row_bytes(a.H), plan_scratch_bytes(a.E, P), nbuf, ring, wgs) ||
+        !ring_plan(16 * rt * (size_t)row_bytes(a.F), plan_scratch_bytes(a.E, P), nbuf, ring, wgs))
+        return MOE_ESHAPE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+bool decode_supported(const FfnArgs &a) {
+    int g, d, r;
+    return decode_plan(a, g, d, r) == MOE_OK;
 }
 
 int launch_decode(const FfnArgs &a, hipStream_t s) {
+    int nb_gu, nb_dn, rt;
+    if (int st = decode_plan(a, nb_gu, nb_dn, rt)) return st;
     const DecodeWs d = carve(a.ws, a.T * a.k, a.H, a.F);
-    switch (a.H % 512 ? 0 : a.H / 512) {
-    case 5: return launch_decode_gd<5>(a, d, s);
-    case 8: return launch_decode_gd<8>(a, d, s);
-    default: return launch_decode_gd<0>(a, d, s);
+    const int max_active = (int)std::min<int64_t>(a.E, (int64_t)a.T * a.k);
+    int st = MOE_OK;
+    switch (nb_gu) {
+#define MOE_GU(nb) case nb: st = launch_gu<nb>(a, d, max_active, s); break;
+        MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) MOE_GU(7) MOE_GU(8)
+        MOE_GU(9) MOE_GU(10) MOE_GU(11) MOE_GU(12) MOE_GU(13) MOE_GU(14) MOE_GU(15) MOE_GU(16)
+#undef MOE_GU
+    default: return MOE_ESHAPE;
     }
+    if (st != MOE_OK) return st;
+    switch (nb_dn) {
+#define MOE_DN(nb) case nb: st = launch_dn<nb>(a, d, max_active, rt, s); break;
+        MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5)
+        MOE_DN(6) MOE_DN(7) MOE_DN(8) MOE_DN(9) MOE_DN(10)
+#undef MOE_DN
+    default: return MOE_ESHAPE;
+    }
+    if (st != MOE_OK) return st;
+    return launch_combine(a.w, d.pos, a.offsets, a.E, d.ypair, a.T, a.k, a.H, a.y, s);
 }
 
 }  // namespace moe

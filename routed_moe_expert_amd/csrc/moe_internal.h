@@ -45,7 +45,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(va, vb, c, false);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU(z) = z * sigmoid(z), with the hardware reciprocal (about 1 ulp) in place of a division.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -79,7 +80,8 @@ __device__ __forceinline__ float sum32_dpp(float v) {
 // with lds_dma_wait() followed by a workgroup barrier.
 template <int kThreads>
 __device__ __forceinline__ void stage_async(void *lds, const void *g, int bytes) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is uniform: as a scalar, each instruction's LDS base is set up in SGPRs
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int units = bytes >> 4;
     const uint8_t *src = static_cast<const uint8_t *>(g);
     uint8_t *dst = static_cast<uint8_t *>(lds);
@@ -111,15 +113,22 @@ __device__ __forceinline__ int stage_async_count(int bytes) {
 }
 
 // Wait until at most n vector-memory operations of this wave are outstanding (n wave-uniform).
-// Vector memory operations complete in issue order, so this waits for everything issued before
-// the n most recent ones. Counts above 15 fall back to waiting for all.
+// Vector memory loads complete in issue order, so this waits for everything issued before the n
+// most recent ones. The counter holds 6 bits; larger n waits for all.
 __device__ __forceinline__ void vm_wait_le(int n) {
     switch (n) {
 #define MOE_VMW(i) case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
         MOE_VMW(1) MOE_VMW(2) MOE_VMW(3) MOE_VMW(4) MOE_VMW(5) MOE_VMW(6) MOE_VMW(7) MOE_VMW(8)
         MOE_VMW(9) MOE_VMW(10) MOE_VMW(11) MOE_VMW(12) MOE_VMW(13) MOE_VMW(14) MOE_VMW(15)
+        MOE_VMW(16) MOE_VMW(17) MOE_VMW(18) MOE_VMW(19) MOE_VMW(20) MOE_VMW(21) MOE_VMW(22)
+        MOE_VMW(23) MOE_VMW(24) MOE_VMW(25) MOE_VMW(26) MOE_VMW(27) MOE_VMW(28) MOE_VMW(29)
+        MOE_VMW(30) MOE_VMW(31) MOE_VMW(32) MOE_VMW(33) MOE_VMW(34) MOE_VMW(35) MOE_VMW(36)
+        MOE_VMW(37) MOE_VMW(38) MOE_VMW(39) MOE_VMW(40) MOE_VMW(41) MOE_VMW(42) MOE_VMW(43)
+        MOE_VMW(44) MOE_VMW(45) MOE_VMW(46) MOE_VMW(47) MOE_VMW(48) MOE_VMW(49) MOE_VMW(50)
+        MOE_VMW(51) MOE_VMW(52) MOE_VMW(53) MOE_VMW(54) MOE_VMW(55) MOE_VMW(56) MOE_VMW(57)
+        MOE_VMW(58) MOE_VMW(59) MOE_VMW(60) MOE_VMW(61) MOE_VMW(62) MOE_VMW(63)
 #undef MOE_VMW
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
 }
 
@@ -164,6 +173,7 @@ struct FfnArgs {
 
 size_t decode_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
 size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
+bool decode_supported(const FfnArgs &a);   // shape within the decode kernels' limits
 int launch_decode(const FfnArgs &a, hipStream_t s);
 int launch_prefill(const FfnArgs &a, hipStream_t s);
 

@@ -110,7 +110,8 @@ def _workload(name, T, U=None):
 @pytest.mark.parametrize("name,T,U,n_check", [
     ("tiny_decode", 1, None, None), ("verify_chunk", 6, 10, None), ("verify_chunk", 6, 30, None),
     ("verify_chunk", 6, 60, None), ("e256_plateau", 16, None, None),
-    ("e256_plateau", 128, None, 12)])
+    ("e256_plateau", 128, None, 12), ("skewed_prefill", 16, None, None),
+    ("full_prefill", 8, None, None)])
 def test_decode_workloads(name, T, U, n_check):
     """Full-size decode workloads; the largest compares a sample of tokens one by one."""
     _print_case("decode_workload", name=name, T=T, U=U)
@@ -126,6 +127,20 @@ def test_decode_workloads(name, T, U, n_check):
         tok[0] = T - 1
         ref = oracle.ffn_per_slot(case, tokens=tok)
         assert_parity(y[tok], ref, name)
+
+
+def test_decode_beyond_slice_width_uses_gemm_path():
+    """hidden = 5376 is wider than the decode kernels' K slices: forcing decode is refused with
+    MOE_ESHAPE, and AUTO computes the layer on the GEMM path."""
+    case = gen.make_random_case(34, 3, 2, 3, 5376, 64)
+    dc = DeviceCase(case)
+    dc.bucket()
+    st = moe.moe_ffn_nvfp4(dc.x, dc.w, dc.offsets, dc.pair_ids, dc.active, dc.counts, dc.gate,
+                           dc.up, dc.down, dc.T, dc.k, dc.E, dc.H, dc.F, dc.y,
+                           moe.MOE_PATH_DECODE, dc.ws, dc.ws_bytes, raise_on_error=False)
+    assert st == moe.MOE_ESHAPE
+    y = dc.run(moe.MOE_PATH_AUTO)
+    assert_parity(y, oracle.ffn_union(case), "auto wide hidden")
 
 
 def test_decode_deterministic():
