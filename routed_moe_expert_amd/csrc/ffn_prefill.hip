@@ -1,22 +1,30 @@
-// Prefill path of the routed NVFP4 FFN: bf16-MFMA grouped GEMM over expert-first CSR tiles.
+// Prefill path of the routed NVFP4 FFN: grouped GEMMs over expert-first CSR tiles on bf16 MFMA.
 //
 // moe_sk_repro.rs times a prefill MoE layer as three grouped GEMMs (gate, up, down) over the
 // expert buckets, in 128-row M tiles; here gate and up share one kernel so the SiLU(g) * u
 // epilogue runs on registers, and down is the second kernel.
 //
-//   schedule:   M tiles of at most kBM consecutive CSR pairs of one expert, listed from the
-//               device CSR (no host read-back); also the pair -> CSR slot map for the combine.
-//   gu_prefill: one workgroup per (64 output features, M tile). The MFMA A operand is the
-//               weights: 64 gate rows and the 64 matching up rows, staged as raw NVFP4 in LDS
-//               (four 36-byte blocks per row at a time) and dequantized once per workgroup into
-//               a bf16 LDS tile -- exact, since every E2M1 x UE4M3 product is a bf16 value. The
-//               B operand is the tile's token rows of x gathered by CSR pair. v_mfma_f32_16x16x32
-//               _bf16 with fp32 accumulation; the epilogue forms h = SiLU(g) * u and stores it as
-//               a bf16 pair h_hi + h_lo (h_hi = bf16(h), h_lo = bf16(h - h_hi)), which carries
-//               h to about 16 significant bits.
-//   dn_prefill: one workgroup per (64 down rows, M tile): dequantized W_d tile times h_hi, plus
-//               the same tile times h_lo, into the fp32 per-pair rows ypair (row = pair id).
-//   combine:    the decode path's ordered fp32 combine.
+//   schedule: M tiles of at most kBM consecutive CSR pairs of one expert, listed from the
+//             device CSR (no host read-back); also the pair -> CSR slot map for the combine.
+//   gemm:     one 8-wave workgroup per (N tile of 256 weight rows, M tile). The A operand is the
+//             weights, staged raw in LDS one NVFP4 block per row per K step; every wave
+//             decodes its own 32 rows straight into bf16 MFMA fragments in registers -- exact,
+//             since every E2M1 x UE4M3 product is a bf16 value. The B operand is the M tile's
+//             token rows (x gathered by token for gate/up, the h_hi / h_lo rows of the CSR
+//             slots for down) with an XOR swizzle of their 16-byte parts so that fragment reads
+//             are free of bank conflicts. Five LDS stages keep four K steps in flight.
+//             v_mfma_f32_16x16x32_bf16 with fp32 accumulation; a wave owns 32 rows x 128
+//             tokens (gate/up) or 32 rows x 64 tokens (down, whose workgroups take half an M
+//             tile so that h_hi and h_lo fit the stages) and skips the second half of its token
+//             columns when the tile does not reach them.
+//             Gate/up: rows are 128 gate rows and the matching up rows; the epilogue forms
+//             h = SiLU(g) * u and stores it as a bf16 pair h_hi + h_lo (h_hi = bf16(h),
+//             h_lo = bf16(h - h_hi)), which carries h to about 16 significant bits. Down: the
+//             same tile times h_hi plus times h_lo, into the fp32 per-pair rows ypair.
+//   combine:  the decode path's ordered fp32 combine.
+//
+// Workgroups are mapped XCD-aware (hardware workgroup b runs on XCD b mod 8): M tile t runs on
+// XCD t mod 8, the N tiles of an M tile -- which share its token rows -- back to back there.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -24,15 +32,13 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreadsSched = 256;
 constexpr int kBM = 128;               // pairs per M tile
-constexpr int kBK = 64;                // K per MFMA sub-step (one NVFP4 block)
-constexpr int kPitch = kBK + 8;        // bf16 elements per LDS tile row (144 bytes)
-constexpr int kChunkBlocks = 4;        // NVFP4 blocks per raw staging chunk
-constexpr int kRawRow = kChunkBlocks * kBlockBytes;  // 144 bytes
-constexpr int kGuO = 64;               // output features per gu tile (gate + up = 128 rows)
-constexpr int kGuRows = 2 * kGuO;
-constexpr int kDnR = 64;               // down rows per dn tile
+constexpr int kCF = kBM / 16;          // token column tiles per M tile
+constexpr int kBRow = 64 * 2;          // bytes of one token row per K step (64 bf16)
+constexpr int kBBytes = kBM * kBRow;   // 16 KB per B operand per stage (128 tokens)
+constexpr int kStages = 5;            // LDS stages: four K steps in flight
+constexpr int kGemmThreads = 512;      // 8 waves, one workgroup per CU
 
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2_t;
 
@@ -49,7 +55,7 @@ __device__ int scan256(int v, int *wsum, int *total) {
     if (lane == 63) wsum[wave] = x;
     lds_barrier();
     int before = 0, tot = 0;
-    for (int w = 0; w < kThreads / 64; w++) {
+    for (int w = 0; w < kThreadsSched / 64; w++) {
         if (w < wave) before += wsum[w];
         tot += wsum[w];
     }
@@ -58,17 +64,17 @@ __device__ int scan256(int v, int *wsum, int *total) {
     return before + x - v;
 }
 
-__global__ __launch_bounds__(kThreads) void schedule_kernel(
+__global__ __launch_bounds__(kThreadsSched) void schedule_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
     const int32_t *__restrict__ active, const int32_t *__restrict__ counts, int32_t P,
     int32_t max_tiles, i32x2_t *__restrict__ tiles, int32_t *__restrict__ n_tiles,
     int32_t *__restrict__ pos) {
-    for (int q = blockIdx.x * kThreads + threadIdx.x; q < P; q += gridDim.x * kThreads)
+    for (int q = blockIdx.x * kThreadsSched + threadIdx.x; q < P; q += gridDim.x * kThreadsSched)
         pos[pair_ids[q]] = q;
     if (blockIdx.x != 0) return;
-    __shared__ int wsum[kThreads / 64];
+    __shared__ int wsum[kThreadsSched / 64];
     const int n_act = counts[0];
-    const int per = (n_act + kThreads - 1) / kThreads;
+    const int per = (n_act + kThreadsSched - 1) / kThreadsSched;
     const int lo = min((int)threadIdx.x * per, n_act), hi = min(lo + per, n_act);
     int mine = 0;
     for (int a = lo; a < hi; a++) {
@@ -88,316 +94,253 @@ __global__ __launch_bounds__(kThreads) void schedule_kernel(
     if (threadIdx.x == 0) n_tiles[0] = min(total, max_tiles);
 }
 
-// ------------------------------------------------------------------------ shared helpers
-
-__device__ __forceinline__ bf16x8_t frag(const uint16_t *tile, int row0, int k0) {
-    const int l = threadIdx.x & 63;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(tile + (row0 + (l & 15)) * kPitch + k0 +
-                                                         (l >> 4) * 8);
-    return __builtin_bit_cast(bf16x8_t, v);
-}
+// ------------------------------------------------------------------------------- gemm
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     bf16x2_t v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Dequantize one 16-weight scale group (scale byte `sb`, 8 code bytes c0,c1) to 16 bf16 and store
-// them as two 16-byte LDS writes at dst. Exact: each product is a bf16 value.
-__device__ __forceinline__ void dequant_group(uint32_t sb, uint32_t c0, uint32_t c1, uint16_t *dst) {
-    const float S = ue4m3_to_f32(sb);
-    u32x4_t lo, hi;
-    f32x2_t v;
-    v = e2m1x2_to_f32<0>(c0); lo[0] = pack_bf16(v[0] * S, v[1] * S);
-    v = e2m1x2_to_f32<1>(c0); lo[1] = pack_bf16(v[0] * S, v[1] * S);
-    v = e2m1x2_to_f32<2>(c0); lo[2] = pack_bf16(v[0] * S, v[1] * S);
-    v = e2m1x2_to_f32<3>(c0); lo[3] = pack_bf16(v[0] * S, v[1] * S);
-    v = e2m1x2_to_f32<0>(c1); hi[0] = pack_bf16(v[0] * S, v[1] * S);
-    v = e2m1x2_to_f32<1>(c1); hi[1] = pack_bf16(v[0] * S, v[1] * S);
-    v = e2m1x2_to_f32<2>(c1); hi[2] = pack_bf16(v[0] * S, v[1] * S);
-    v = e2m1x2_to_f32<3>(c1); hi[3] = pack_bf16(v[0] * S, v[1] * S);
-    reinterpret_cast<u32x4_t *>(dst)[0] = lo;
-    reinterpret_cast<u32x4_t *>(dst)[1] = hi;
+// 8 E2M1 codes (one code dword) times the group scale S -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t c, float S) {
+    f32x2_t v0 = e2m1x2_to_f32<0>(c), v1 = e2m1x2_to_f32<1>(c);
+    f32x2_t v2 = e2m1x2_to_f32<2>(c), v3 = e2m1x2_to_f32<3>(c);
+    return __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16(v0[0] * S, v0[1] * S),
+                                                pack_bf16(v1[0] * S, v1[1] * S),
+                                                pack_bf16(v2[0] * S, v2[1] * S),
+                                                pack_bf16(v3[0] * S, v3[1] * S)});
 }
 
-// ----------------------------------------------------------------------------- gate / up
+// Target builtins stay inside __device__ helpers: used directly in a kernel template they make
+// its host-side instantiation fail, and the launch stub goes missing.
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 4, 0, 0);
+}
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
+}
+// 12 bytes per lane; lane i lands at LDS + 16 i (the last 4 bytes of its slot are untouched)
+__device__ __forceinline__ void dma12(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 12, 0, 0);
+}
 
-constexpr int kGuRawUnits = kGuRows * kRawRow / 16;            // 1152 16-byte units per chunk
-constexpr int kGuRawPerThread = (kGuRawUnits + kThreads - 1) / kThreads;  // 5
-constexpr int kActUnits = kBM * kBK * 2 / 16;                  // 1024 units per sub-step
-constexpr int kActPerThread = kActUnits / kThreads;            // 4
+// LDS offset of byte b (0..35) of an NVFP4 block staged as three 12-byte loads in 16-byte slots
+__host__ __device__ constexpr int blk_lds(int b) { return 16 * (b / 12) + b % 12; }
 
-__global__ __launch_bounds__(kThreads) void gu_prefill_kernel(
-    const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
+
+// LDS slot (16-byte unit) of part p (8 bf16) of token row r of a B stage: parts are XOR-swizzled
+// by the row so that the 8 lanes of a fragment read group hit 8 different bank groups.
+__device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ (r & 7)); }
+
+// One workgroup: N tile nt (256 weight rows) of M tile ti (gate/up: all of its up to 128 pairs;
+// down: the half hf of 64 pairs). DOWN = false: gate/up (A rows are 128 gate rows then the
+// matching up rows; K = H; B = x rows by token); DOWN = true: down (A rows are 256 rows of W_d;
+// K = F; B = h_hi and h_lo rows by CSR slot). N tiles may run past the matrix: rows beyond it
+// read the last row and are not stored.
+//
+// Each K step of 64 stages one NVFP4 block of every A row (three 12-byte direct-to-LDS loads per
+// row, lane i of a load landing at +16 i, so a row takes 48 bytes of LDS) and the B rows, in one
+// of kStages LDS stages: kStages - 1 steps are in flight while one is computed, which is what
+// covers the latency of these scattered loads. Each wave issues a fixed number of loads per step,
+// so its count of outstanding loads is exact and the waits are partial.
+template <bool DOWN>
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ hin_hi,
+    const uint16_t *__restrict__ hin_lo, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const i32x2_t *__restrict__ tiles,
-    const int32_t *__restrict__ n_tiles, const uint8_t *__restrict__ gate, int64_t gate_stride,
-    const uint8_t *__restrict__ up, int64_t up_stride, int32_t k, int32_t H, int32_t F,
-    uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo) {
-    __shared__ __attribute__((aligned(16))) uint16_t wbf[kGuRows * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t act[kBM * kPitch];
-    __shared__ __attribute__((aligned(16))) uint8_t raw[kGuRows * kRawRow];
-    __shared__ int tok[kBM];
+    const int32_t *__restrict__ n_tiles, int32_t max_tiles, int32_t n_ntiles,
+    const uint8_t *__restrict__ w0, int64_t s0, const uint8_t *__restrict__ w1, int64_t s1,
+    int32_t k, int32_t K, int32_t F, int32_t H, uint16_t *__restrict__ h_hi,
+    uint16_t *__restrict__ h_lo, float *__restrict__ ypair) {
+    constexpr int kThreads = kGemmThreads;
+    constexpr int kWaves = kThreads / 64;
+    constexpr int kRows = 32 * kWaves;              // A rows per workgroup
+    constexpr int kAUnits = kRows * 3;              // 12-byte A loads per step (3 per row)
+    constexpr int kABytes = kAUnits * 16;           // 48 bytes per row
+    constexpr int kNB = DOWN ? 2 : 1;               // B operands (h_hi, h_lo) or (x)
+    constexpr int kBM2 = DOWN ? kBM / 2 : kBM;      // token columns per workgroup
+    constexpr int kCols = kBM2 / 16;
+    constexpr int kBBytesW = kBM2 * kBRow;
+    constexpr int kStageBytes = kABytes + kNB * kBBytesW;
+    constexpr int kBUnits = kBBytesW / 16 / kThreads;    // 16-byte B loads per lane per operand
+    constexpr int kALoadsMax = (kAUnits + kThreads - 1) / kThreads;   // 2
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ int rowid[kBM2];               // token (gate/up) or CSR slot (down) of each column
 
-    const int ti = blockIdx.y;
+    // M tile ti runs on XCD ti mod 8 (hardware workgroup b runs on XCD b mod 8), its N tiles (and
+    // halves) in consecutive slots there: they share its token rows in that XCD's L2, and the
+    // tiles that exist (the schedule's count is only known on the device) spread evenly over the
+    // XCDs whatever the count
+    const int nh = DOWN ? 2 : 1;
+    const int pos = blockIdx.x >> 3;
+    const int ti = (pos / (n_ntiles * nh)) * 8 + (blockIdx.x & 7), rem = pos % (n_ntiles * nh);
+    const int nt = rem / nh, hf = rem % nh;
     if (ti >= n_tiles[0]) return;
     const i32x2_t tl = tiles[ti];
-    const int e = tl[0], m0 = tl[1];
+    const int e = tl[0], m0 = tl[1] + hf * kBM2;
     const int q0 = offsets[e] + m0;
-    const int mt = min(kBM, offsets[e + 1] - q0);
-    const int o0 = blockIdx.x * kGuO;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rb = H / kBlockWeights * kBlockBytes;
+    const int mt = min(kBM2, offsets[e + 1] - q0);
+    if (mt <= 0) return;
+    const int ncol = (mt + 15) >> 4;
 
-    for (int r = tid; r < kBM; r += kThreads) tok[r] = r < mt ? pair_ids[q0 + r] / k : -1;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 15, q = lane >> 4;
+    const int nblk = K / kBlockWeights;
+    const int rb = nblk * kBlockBytes;
+    const int n_out = DOWN ? H : F;                  // rows (down) or features (gate/up)
 
-    const uint8_t *gsrc = gate + e * gate_stride + (int64_t)o0 * rb;
-    const uint8_t *usrc = up + e * up_stride + (int64_t)o0 * rb;
+    for (int r = tid; r < kBM2; r += kThreads) {
+        const int c = r < mt ? r : 0;
+        rowid[r] = DOWN ? q0 + c : pair_ids[q0 + c] / k;
+    }
+    lds_barrier();
 
-    u32x4_t rawr[kGuRawPerThread];
-    auto load_raw = [&](int chunk) {
+    // A: load i of a wave covers units (i*kWaves + wave)*64 + lane (unit j = u % 3 of row
+    // u / 3); loads whose units all lie past kAUnits are skipped by the whole wave
+    const uint8_t *asrc[kALoadsMax];
 #pragma unroll
-        for (int i = 0; i < kGuRawPerThread; i++) {
-            const int u = tid + i * kThreads;
-            if (u < kGuRawUnits) {
-                const int row = u / 9, part = u % 9;
-                const uint8_t *src = (row < kGuO ? gsrc + (int64_t)row * rb
-                                                 : usrc + (int64_t)(row - kGuO) * rb) +
-                                     chunk * kRawRow + part * 16;
-                rawr[i] = *reinterpret_cast<const u32x4_t *>(src);
-            }
+    for (int i = 0; i < kALoadsMax; i++) {
+        const int u = min((i * kWaves + wave) * 64 + lane, kAUnits - 1);
+        const int row = u / 3;
+        const uint8_t *base;
+        if (DOWN) {
+            base = w0 + e * s0 + (int64_t)min(nt * kRows + row, n_out - 1) * rb;
+        } else {
+            const int half = kRows / 2;   // gate rows, then the matching up rows
+            const int f = min(nt * half + (row < half ? row : row - half), n_out - 1);
+            base = (row < half ? w0 + e * s0 : w1 + e * s1) + (int64_t)f * rb;
         }
-    };
-    auto store_raw = [&]() {
+        asrc[i] = base + 12 * (u % 3);
+    }
+    const int a_loads = ((kALoadsMax - 1) * kWaves + wave) * 64 < kAUnits ? kALoadsMax : kALoadsMax - 1;
+    // B: lane loads 16-byte units u = (i*kWaves + wave)*64 + lane of each operand
+    const uint16_t *bsrc[kNB][kBUnits];
 #pragma unroll
-        for (int i = 0; i < kGuRawPerThread; i++) {
-            const int u = tid + i * kThreads;
-            if (u < kGuRawUnits) reinterpret_cast<u32x4_t *>(raw)[u] = rawr[i];
-        }
-    };
-    lds_barrier();  // tok visible
-    u32x4_t actr[kActPerThread];
-    auto load_act = [&](int sub) {
-#pragma unroll
-        for (int i = 0; i < kActPerThread; i++) {
-            const int u = tid + i * kThreads;
-            const int row = u >> 3, part = u & 7;
-            const int t = tok[row];
-            actr[i] = t >= 0 ? *reinterpret_cast<const u32x4_t *>(x + (int64_t)t * H + sub * kBK + part * 8)
-                             : u32x4_t{0, 0, 0, 0};
-        }
-    };
-    auto store_act = [&]() {
-#pragma unroll
-        for (int i = 0; i < kActPerThread; i++) {
-            const int u = tid + i * kThreads;
-            const int row = u >> 3, part = u & 7;
-            *reinterpret_cast<u32x4_t *>(act + row * kPitch + part * 8) = actr[i];
-        }
-    };
-
-    f32x4_t acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; a++)
-#pragma unroll
-        for (int b = 0; b < 4; b++) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int wa = wave & 1, wb = wave >> 1;
-    const int nsub = H / kBK;
-    load_raw(0);
-    load_act(0);
-    for (int s = 0; s < nsub; s++) {
-        lds_barrier();
-        if ((s & 3) == 0) store_raw();
-        store_act();
-        lds_barrier();
-        {   // dequantize block (s & 3) of the chunk: thread -> (row, two scale groups)
-            const int row = tid >> 1, half = tid & 1;
-            const uint8_t *blk = raw + row * kRawRow + (s & 3) * kBlockBytes;
-            const uint32_t *b32 = reinterpret_cast<const uint32_t *>(blk);
-            const uint32_t scw = b32[0];
-            uint16_t *dst = wbf + row * kPitch + half * 32;
-            dequant_group((scw >> (16 * half)) & 0xff, b32[1 + 4 * half], b32[2 + 4 * half], dst);
-            dequant_group((scw >> (16 * half + 8)) & 0xff, b32[3 + 4 * half], b32[4 + 4 * half],
-                          dst + 16);
-        }
-        if (s + 1 < nsub) load_act(s + 1);
-        if ((s & 3) == 3 && s + 1 < nsub) load_raw((s + 1) >> 2);
-        lds_barrier();
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            bf16x8_t af[4], bfr[4];
-            af[0] = frag(wbf, 32 * wa, kk);
-            af[1] = frag(wbf, 32 * wa + 16, kk);
-            af[2] = frag(wbf, kGuO + 32 * wa, kk);
-            af[3] = frag(wbf, kGuO + 32 * wa + 16, kk);
-#pragma unroll
-            for (int b = 0; b < 4; b++) bfr[b] = frag(act, 64 * wb + 16 * b, kk);
-#pragma unroll
-            for (int a = 0; a < 4; a++)
-#pragma unroll
-                for (int b = 0; b < 4; b++)
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bfr[b], acc[a][b], 0, 0, 0);
+    for (int i = 0; i < kBUnits; i++) {
+        const int u = (i * kWaves + wave) * 64 + lane;
+        const int r = u >> 3, p = (u & 7) ^ (r & 7);
+        const int64_t off = (int64_t)rowid[r] * (DOWN ? F : H) + 8 * p;
+        if (DOWN) {
+            bsrc[0][i] = hin_hi + off;
+            bsrc[kNB - 1][i] = hin_lo + off;
+        } else {
+            bsrc[0][i] = x + off;
         }
     }
+    auto issue = [&](int kb) {
+        uint8_t *st = smem + (kb % kStages) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < kALoadsMax; i++)
+            if (i < a_loads)
+                dma12(asrc[i] + kb * kBlockBytes, st + (i * kWaves + wave) * 1024);
+#pragma unroll
+        for (int o = 0; o < kNB; o++)
+#pragma unroll
+            for (int i = 0; i < kBUnits; i++)
+                dma16(bsrc[o][i] + kb * 64, st + kABytes + o * kBBytesW + (i * kWaves + wave) * 1024);
+    };
+    const int ops = a_loads + kNB * kBUnits;   // loads per step of this wave
 
-    // epilogue: lane holds C[4*(lane/16)+v][lane%16] of each 16x16 tile (rows = features,
-    // columns = pairs); gate tile a pairs with up tile a+2.
+    f32x4_t acc[2][kCols];
 #pragma unroll
-    for (int a = 0; a < 2; a++) {
+    for (int f = 0; f < 2; f++)
 #pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int col = 64 * wb + 16 * b + (lane & 15);
-            if (col < mt) {
-                const int o = o0 + 32 * wa + 16 * a + 4 * (lane >> 4);
-                uint32_t hi2[2], lo2[2];
+        for (int c = 0; c < kCols; c++) acc[f][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // this wave's two 16-row A tiles: DOWN: rows 32*wave + 16f; gate/up: gate rows 16*wave
+    // (f = 0) and the matching up rows (f = 1)
+    const int arow0 = DOWN ? 32 * wave : 16 * wave;
+    const int arow1 = DOWN ? 32 * wave + 16 : kRows / 2 + 16 * wave;
+    // this lane's scale byte and code dwords within a staged block (12-byte loads, 16 apart)
+    const int c0_off = blk_lds(4 + 8 * q), c1_off = blk_lds(8 + 8 * q);
+
+    const int nsteps = nblk;
+    for (int kb = 0; kb < min(kStages - 1, nsteps); kb++) issue(kb);
+    for (int kb = 0; kb < nsteps; kb++) {
+        vm_wait_le(min(kStages - 2, nsteps - 1 - kb) * ops);   // step kb landed
+        lds_barrier();   // visible to all; the stage of step kb-1 is free
+        if (kb + kStages - 1 < nsteps) issue(kb + kStages - 1);
+        const uint8_t *st = smem + (kb % kStages) * kStageBytes;
+        // A: lane (n, q) takes scale group q of its row: K step s = weights 16q+8s .. +7
+        float S[2];
+        uint32_t cw[2][2];
 #pragma unroll
-                for (int v = 0; v < 4; v += 2) {
-                    const float h0 = silu(acc[a][b][v]) * acc[a + 2][b][v];
-                    const float h1 = silu(acc[a][b][v + 1]) * acc[a + 2][b][v + 1];
-                    const __bf16 g0 = (__bf16)h0, g1 = (__bf16)h1;
-                    hi2[v / 2] = pack_bf16((float)g0, (float)g1);
-                    lo2[v / 2] = pack_bf16(h0 - (float)g0, h1 - (float)g1);
+        for (int f = 0; f < 2; f++) {
+            const uint8_t *blk = st + ((f ? arow1 : arow0) + n) * 48;
+            S[f] = ue4m3_to_f32(blk[q]);
+            cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
+            cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            bf16x8_t af[2];
+#pragma unroll
+            for (int f = 0; f < 2; f++) af[f] = dequant8_bf16(cw[f][s], S[f]);
+            // token columns in two halves: the second only when the tile reaches it (one uniform
+            // branch, so each half schedules freely)
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+                if (hh == 1 && ncol <= kCols / 2) break;
+#pragma unroll
+                for (int o = 0; o < kNB; o++) {
+                    bf16x8_t bfr[kCols / 2];
+#pragma unroll
+                    for (int c = 0; c < kCols / 2; c++)
+                        bfr[c] = *reinterpret_cast<const bf16x8_t *>(
+                            st + kABytes + o * kBBytesW +
+                            16 * b_slot(16 * (hh * kCols / 2 + c) + n, 2 * q + s));
+#pragma unroll
+                    for (int f = 0; f < 2; f++)
+#pragma unroll
+                        for (int c = 0; c < kCols / 2; c++)
+                            acc[f][hh * kCols / 2 + c] =
+                                mfma_bf16(af[f], bfr[c], acc[f][hh * kCols / 2 + c]);
                 }
-                const int64_t off = (int64_t)(q0 + col) * F + o;
-                *reinterpret_cast<i32x2_t *>(h_hi + off) = i32x2_t{(int)hi2[0], (int)hi2[1]};
-                *reinterpret_cast<i32x2_t *>(h_lo + off) = i32x2_t{(int)lo2[0], (int)lo2[1]};
             }
         }
     }
-}
 
-// ---------------------------------------------------------------------------------- down
-
-constexpr int kDnRawDwords = kDnR * kRawRow / 4;                 // 2304 dwords per full chunk
-constexpr int kDnRawPerThread = kDnRawDwords / kThreads;          // 9
-constexpr int kDnActPerThread = 2 * kActUnits / kThreads;         // 8 (hi and lo)
-
-__global__ __launch_bounds__(kThreads) void dn_prefill_kernel(
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
-    const i32x2_t *__restrict__ tiles,
-    const int32_t *__restrict__ n_tiles, const uint8_t *__restrict__ down, int64_t down_stride,
-    int32_t H, int32_t F, const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
-    float *__restrict__ ypair) {
-    __shared__ __attribute__((aligned(16))) uint16_t wbf[kDnR * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t ahi[kBM * kPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t alo[kBM * kPitch];
-    __shared__ __attribute__((aligned(16))) uint8_t raw[kDnR * kRawRow];
-    __shared__ int pid[kBM];
-
-    const int ti = blockIdx.y;
-    if (ti >= n_tiles[0]) return;
-    const i32x2_t tl = tiles[ti];
-    const int e = tl[0], m0 = tl[1];
-    const int q0 = offsets[e] + m0;
-    const int mt = min(kBM, offsets[e + 1] - q0);
-    const int r0 = blockIdx.x * kDnR;
-    for (int r = threadIdx.x; r < kBM; r += kThreads) pid[r] = r < mt ? pair_ids[q0 + r] : 0;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rb = F / kBlockWeights * kBlockBytes;
-    const int nblk = F / kBlockWeights;
-    const uint8_t *wsrc = down + e * down_stride + (int64_t)r0 * rb;
-
-    uint32_t rawr[kDnRawPerThread];
-    auto load_raw = [&](int chunk) {
-        const int cb = min(kChunkBlocks, nblk - chunk * kChunkBlocks);
-        const int dw_row = cb * 9;
+    // epilogue: lane holds rows 4q..4q+3 of each 16-row A tile for token column 16c + n
+    if (DOWN) {
 #pragma unroll
-        for (int i = 0; i < kDnRawPerThread; i++) {
-            const int u = tid + i * kThreads;
-            if (u < kDnR * dw_row) {
-                const int row = u / dw_row, d = u % dw_row;
-                rawr[i] = *reinterpret_cast<const uint32_t *>(wsrc + (int64_t)row * rb +
-                                                              chunk * kRawRow + 4 * d);
-            }
-        }
-    };
-    auto store_raw = [&](int chunk) {
-        const int cb = min(kChunkBlocks, nblk - chunk * kChunkBlocks);
-        const int dw_row = cb * 9;
-#pragma unroll
-        for (int i = 0; i < kDnRawPerThread; i++) {
-            const int u = tid + i * kThreads;
-            if (u < kDnR * dw_row) {
-                const int row = u / dw_row, d = u % dw_row;
-                reinterpret_cast<uint32_t *>(raw + row * kRawRow)[d] = rawr[i];
-            }
-        }
-    };
-    u32x4_t actr[kDnActPerThread];
-    auto load_act = [&](int sub) {
-#pragma unroll
-        for (int i = 0; i < kDnActPerThread; i++) {
-            const int u = tid + (i >> 1) * kThreads;
-            const int row = u >> 3, part = u & 7;
-            const uint16_t *src = (i & 1) ? h_lo : h_hi;
-            actr[i] = row < mt ? *reinterpret_cast<const u32x4_t *>(src + (int64_t)(q0 + row) * F +
-                                                                   sub * kBK + part * 8)
-                               : u32x4_t{0, 0, 0, 0};
-        }
-    };
-    auto store_act = [&]() {
-#pragma unroll
-        for (int i = 0; i < kDnActPerThread; i++) {
-            const int u = tid + (i >> 1) * kThreads;
-            const int row = u >> 3, part = u & 7;
-            *reinterpret_cast<u32x4_t *>(((i & 1) ? alo : ahi) + row * kPitch + part * 8) = actr[i];
-        }
-    };
-
-    f32x4_t acc[2][4];
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-        for (int b = 0; b < 4; b++) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    const int wa = wave & 1, wb = wave >> 1;
-    const int nsub = nblk;
-    load_raw(0);
-    load_act(0);
-    for (int s = 0; s < nsub; s++) {
-        lds_barrier();
-        if ((s & 3) == 0) store_raw(s >> 2);
-        store_act();
-        lds_barrier();
-        {   // dequantize block (s & 3) of the chunk: thread -> (row, scale group)
-            const int row = tid >> 2, g = tid & 3;
-            const uint8_t *blk = raw + row * kRawRow + (s & 3) * kBlockBytes;
-            const uint32_t *b32 = reinterpret_cast<const uint32_t *>(blk);
-            dequant_group((b32[0] >> (8 * g)) & 0xff, b32[1 + 2 * g], b32[2 + 2 * g],
-                          wbf + row * kPitch + 16 * g);
-        }
-        if (s + 1 < nsub) load_act(s + 1);
-        if ((s & 3) == 3 && s + 1 < nsub) load_raw((s + 1) >> 2);
-        lds_barrier();
-#pragma unroll
-        for (int kk = 0; kk < kBK; kk += 32) {
-            bf16x8_t af[2], bh[4], bl[4];
-            af[0] = frag(wbf, 32 * wa, kk);
-            af[1] = frag(wbf, 32 * wa + 16, kk);
-#pragma unroll
-            for (int b = 0; b < 4; b++) {
-                bh[b] = frag(ahi, 64 * wb + 16 * b, kk);
-                bl[b] = frag(alo, 64 * wb + 16 * b, kk);
-            }
-#pragma unroll
-            for (int a = 0; a < 2; a++)
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bh[b], acc[a][b], 0, 0, 0);
-                    acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[a], bl[b], acc[a][b], 0, 0, 0);
-                }
-        }
-    }
-#pragma unroll
-    for (int a = 0; a < 2; a++)
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int col = 64 * wb + 16 * b + (lane & 15);
+        for (int c = 0; c < kCols; c++) {
+            const int col = 16 * c + n;
             if (col < mt) {
-                const int r = r0 + 32 * wa + 16 * a + 4 * (lane >> 4);
-                *reinterpret_cast<f32x4_t *>(ypair + (int64_t)pid[col] * H + r) = acc[a][b];
+                const int64_t prow = (int64_t)pair_ids[q0 + col] * H;
+#pragma unroll
+                for (int f = 0; f < 2; f++) {
+                    const int r = nt * kRows + (f ? arow1 : arow0) + 4 * q;
+                    if (r < H) *reinterpret_cast<f32x4_t *>(ypair + prow + r) = acc[f][c];
+                }
             }
         }
+    } else {
+        const int o = nt * (kRows / 2) + 16 * wave + 4 * q;   // features o..o+3
+        if (o < F) {
+#pragma unroll
+            for (int c = 0; c < kCols; c++) {
+                const int col = 16 * c + n;
+                if (col < mt) {
+                    uint32_t hi2[2], lo2[2];
+#pragma unroll
+                    for (int v = 0; v < 4; v += 2) {
+                        const float h0 = silu(acc[0][c][v]) * acc[1][c][v];
+                        const float h1 = silu(acc[0][c][v + 1]) * acc[1][c][v + 1];
+                        const __bf16 g0 = (__bf16)h0, g1 = (__bf16)h1;
+                        hi2[v / 2] = pack_bf16((float)g0, (float)g1);
+                        lo2[v / 2] = pack_bf16(h0 - (float)g0, h1 - (float)g1);
+                    }
+                    const int64_t off = (int64_t)(q0 + col) * F + o;
+                    *reinterpret_cast<i32x2_t *>(h_hi + off) = i32x2_t{(int)hi2[0], (int)hi2[1]};
+                    *reinterpret_cast<i32x2_t *>(h_lo + off) = i32x2_t{(int)lo2[0], (int)lo2[1]};
+                }
+            }
+        }
+    }
 }
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -412,7 +355,7 @@ struct PrefillWs {
 
 int max_tiles(int32_t P, int32_t E) { return P / kBM + std::min(E, P) + 1; }
 
-PrefillWs carve(void *ws, int32_t P, int32_t E, int32_t H, int32_t F) {
+PrefillWs carve(void *ws, int32_t P, int32_t E, int32_t F) {
     uint8_t *b = static_cast<uint8_t *>(ws);
     PrefillWs w;
     w.pos = reinterpret_cast<int32_t *>(b);
@@ -429,6 +372,37 @@ PrefillWs carve(void *ws, int32_t P, int32_t E, int32_t H, int32_t F) {
     return w;
 }
 
+template <bool DOWN>
+int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
+    constexpr int kRows = 32 * (kGemmThreads / 64);
+    constexpr size_t lds = kStages * (kRows * 48 + kBBytes);   // B: 128 x1 or 64 x2 rows
+    static bool attr = false;
+    if (!attr) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_kernel<DOWN>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return MOE_ELAUNCH;
+        attr = true;
+    }
+    const int per_nt = DOWN ? kRows : kRows / 2;
+    const int n_out = DOWN ? a.H : a.F;
+    const int n_ntiles = (n_out + per_nt - 1) / per_nt;
+    const int grid = 8 * ((mt + 7) / 8) * n_ntiles * (DOWN ? 2 : 1);
+    const int id = DOWN ? MOE_KERNEL_DN_PREFILL : MOE_KERNEL_GU_PREFILL;
+    prof_start(id, s);
+    if constexpr (DOWN)
+        hipLaunchKernelGGL((gemm_kernel<true>), dim3(grid), dim3(kGemmThreads), lds, s, nullptr,
+                           w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt, n_ntiles,
+                           a.down.base, a.down.expert_stride, nullptr, (int64_t)0, a.k, a.F, a.F,
+                           a.H, nullptr, nullptr, w.ypair);
+    else
+        hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kGemmThreads), lds, s, a.x,
+                           nullptr, nullptr, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt,
+                           n_ntiles, a.gate.base, a.gate.expert_stride, a.up.base,
+                           a.up.expert_stride, a.k, a.H, a.F, a.H, w.h_hi, w.h_lo, nullptr);
+    prof_stop(id, s);
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
 }  // namespace
 
 size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
@@ -439,28 +413,18 @@ size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
 
 int launch_prefill(const FfnArgs &a, hipStream_t s) {
     const int32_t P = a.T * a.k;
-    const PrefillWs w = carve(a.ws, P, a.E, a.H, a.F);
+    const PrefillWs w = carve(a.ws, P, a.E, a.F);
     const int mt = max_tiles(P, a.E);
-    const int sched_blocks = std::max(1, std::min(256, (P + kThreads - 1) / kThreads));
+    const int sched_blocks = std::max(1, std::min(256, (P + kThreadsSched - 1) / kThreadsSched));
     prof_start(MOE_KERNEL_SCHEDULE, s);
-    hipLaunchKernelGGL(schedule_kernel, dim3(sched_blocks), dim3(kThreads), 0, s, a.offsets,
+    hipLaunchKernelGGL(schedule_kernel, dim3(sched_blocks), dim3(kThreadsSched), 0, s, a.offsets,
                        a.pair_ids, a.active, a.counts, P, mt, w.tiles, w.n_tiles, w.pos);
     prof_stop(MOE_KERNEL_SCHEDULE, s);
     if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
-    if (a.F % kGuO || a.H % kDnR) return MOE_ESHAPE;
-    prof_start(MOE_KERNEL_GU_PREFILL, s);
-    hipLaunchKernelGGL(gu_prefill_kernel, dim3(a.F / kGuO, mt), dim3(kThreads), 0, s, a.x,
-                       a.offsets, a.pair_ids, w.tiles, w.n_tiles, a.gate.base,
-                       a.gate.expert_stride, a.up.base, a.up.expert_stride, a.k, a.H, a.F, w.h_hi,
-                       w.h_lo);
-    prof_stop(MOE_KERNEL_GU_PREFILL, s);
-    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
-    prof_start(MOE_KERNEL_DN_PREFILL, s);
-    hipLaunchKernelGGL(dn_prefill_kernel, dim3(a.H / kDnR, mt), dim3(kThreads), 0, s, a.offsets,
-                       a.pair_ids, w.tiles, w.n_tiles, a.down.base, a.down.expert_stride, a.H, a.F, w.h_hi,
-                       w.h_lo, w.ypair);
-    prof_stop(MOE_KERNEL_DN_PREFILL, s);
-    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+    int st = launch_gemm<false>(a, w, mt, s);
+    if (st != MOE_OK) return st;
+    st = launch_gemm<true>(a, w, mt, s);
+    if (st != MOE_OK) return st;
     return launch_combine(a.w, w.pos, a.offsets, a.E, w.ypair, a.T, a.k, a.H, a.y, s);
 }
 
