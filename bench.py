@@ -40,8 +40,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "013e0503fa19c6b9c0ca8fac3d9dd8c2b8551bbe73632c0ce43b7651a6cec9db",
-        "fetch_kib": 54186.4, "write_kib": 161.9,
+        "sha256": "3de1908eff825a0a5a160d27bc49928a970a1806260cca0996d756e98fb902ca",
+        "fetch_kib": 54265.8, "write_kib": 165.7,
     },
 }
 
@@ -227,7 +227,7 @@ def main():
     # second pass of the same K steps
     hip = _hip()
     kid = moe.MOE_KERNEL_GU_DECODE if decode else moe.MOE_KERNEL_GU_PREFILL
-    kname = "gu_decode_kernel" if decode else "gu_prefill_kernel"
+    kname = "gu_decode_kernel" if decode else "gemm_kernel<false>"   # gate/up + SiLU
     starts, stops = [], []
     for _ in range(K):
         a, b = ctypes.c_void_p(), ctypes.c_void_p()
