@@ -7,7 +7,7 @@
 // grow with the expert's token count up to 16.
 //
 //   gu_decode: items of 8 gate rows + the 8 matching up rows = one 16-row MFMA A tile. The
-//              eight waves split K = hidden into eight slices. Each lane decodes the E2M1 codes
+//              four waves split K = hidden into four slices. Each lane decodes the E2M1 codes
 //              of one row and one 16-weight scale group to f16 (v_cvt_scalef32_pk_f16_fp4) and
 //              multiplies in the UE4M3 group scale (v_pk_mul_f16); both steps are exact, since
 //              every E2M1 x UE4M3 product is an f16 value. The B operand is the expert's token
@@ -16,7 +16,7 @@
 //              magnitude into [2^14, 2^15). v_mfma_f32_16x16x32_f16 accumulates in fp32; the
 //              slices are unscaled, summed across the waves through LDS, and the epilogue
 //              writes h = SiLU(g) * u (fp32) in CSR pair order.
-//   dn_decode: items of 16*RT down rows; RT row tiles x (8/RT) K slices of ff over the eight
+//   dn_decode: items of 16*RT down rows; RT row tiles x (4/RT) K slices of ff over the four
 //              waves. B is the expert's h rows, scaled per (pair, K slice) and split into
 //              f16 hi + lo (about 22 significant bits), two MFMAs per step. Slices are summed
 //              through LDS into the per-pair rows ypair (row = pair id).
@@ -29,11 +29,12 @@
 // lane group q the weights 16q + 8s .. 16q + 8s + 7 of the block: one scale group per lane and
 // two steps per block.
 //
-// Both FFN kernels are persistent: a grid of one or two 512-thread workgroups per CU splits the
+// Both FFN kernels are persistent: a grid of one or two 256-thread workgroups per CU splits the
 // (expert, tile) items into contiguous ranges, read from the device CSR (nothing is read back on
 // the host). Tiles stream through a ring of LDS buffers with direct-to-LDS loads (three per
-// workgroup with two workgroups per CU, up to six with one), all but one in flight while one is
-// computed.
+// workgroup with two workgroups per CU, up to six with one). Each wave copies its share of a
+// tile into registers first thing, and the buffer is refilled as soon as every wave has done
+// so, so all buffers are in flight while a tile is computed.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -54,21 +55,26 @@ constexpr int kRedBytes = 2 * kRedFloats * 4;        // two sets (double-buffere
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 
-// 8 E2M1 codes (one code dword, low nibble first) times the group scale S -> 8 f16, exact.
+// 8 E2M1 codes (one code dword, low nibble first) times the group scale -> 8 f16, exact. The
+// converts scale by 2^8 (their scale operand contributes its exponent only) and S holds the
+// group scale times 2^-8 (scale_f16x2), so the products are the plain E2M1 x UE4M3 values.
 __device__ __forceinline__ f16x8_t dequant8(uint32_t c, f16x2_t S) {
-    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 0) * S;
-    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 1) * S;
-    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 2) * S;
-    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 1.0f, 3) * S;
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 0) * S;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 1) * S;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 2) * S;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 3) * S;
     return __builtin_bit_cast(f16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, p0),
                                                __builtin_bit_cast(uint32_t, p1),
                                                __builtin_bit_cast(uint32_t, p2),
                                                __builtin_bit_cast(uint32_t, p3)});
 }
 
-// UE4M3 scale byte -> f16 pair (exact: every finite UE4M3 value is a normal f16).
+// UE4M3 scale byte (0x00..0x7E) -> f16 pair holding 2^-8 times its value, exactly: the byte's
+// 4 exponent and 3 mantissa bits shifted into the f16 exponent and top mantissa bits read as
+// 2^(e-15) (1 + m/8) for e > 0 and as the subnormal m 2^-17 for e = 0, i.e. 2^-8 times the
+// UE4M3 values 2^(e-7) (1 + m/8) and m 2^-9. One shift instead of a decode and a conversion.
 __device__ __forceinline__ f16x2_t scale_f16x2(uint32_t byte) {
-    const _Float16 s = (_Float16)ue4m3_to_f32(byte);
+    const _Float16 s = __builtin_bit_cast(f16x2_t, byte << 7)[0];
     return f16x2_t{s, s};
 }
 
@@ -76,13 +82,39 @@ __device__ __forceinline__ f32x4_t mfma16(f16x8_t a, f16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// Lane-group (q) part of one NVFP4 block of one row, as the A operands of the block's two K
-// steps.
-__device__ __forceinline__ void load_a(const uint8_t *blk, int q, f16x8_t &a0, f16x8_t &a1) {
-    const f16x2_t S = scale_f16x2(blk[q]);
-    const uint32_t *c = reinterpret_cast<const uint32_t *>(blk + 4 + 8 * q);
-    a0 = dequant8(c[0], S);
-    a1 = dequant8(c[1], S);
+// One lane's share of a row's K slice in an LDS tile: for each of NB blocks, the UE4M3 scale
+// byte of its group q and the group's 16 E2M1 codes (two dwords). All reads are issued before
+// any is used, so their LDS latencies overlap instead of adding up block by block.
+template <int NB>
+struct SliceA {
+    uint32_t s[NB];
+    uint32_t c[NB][2];
+};
+
+// Block j of the slice is block min(j0 + j, jlast) of the row: the clamp only bites for a last
+// slice that runs past the row, whose extra blocks meet zero B operands (re-reading a block of
+// the row keeps them finite). Whole slices take the unclamped form, with constant offsets.
+template <int NB>
+__device__ __forceinline__ void read_slice_at(const uint8_t *row, int j0, int jlast, int q,
+                                              SliceA<NB> &a) {
+#pragma unroll
+    for (int j = 0; j < NB; j++) {
+        const uint8_t *blk = row + min(j0 + j, jlast) * kBlockBytes;
+        a.s[j] = blk[q];
+        const uint32_t *c = reinterpret_cast<const uint32_t *>(blk + 4 + 8 * q);
+        a.c[j][0] = c[0];
+        a.c[j][1] = c[1];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the code that uses them
+}
+
+template <int NB>
+__device__ __forceinline__ void read_slice(const uint8_t *row, int j0, int nblk, int q,
+                                           SliceA<NB> &a) {
+    if (j0 + NB <= nblk)
+        read_slice_at<NB>(row + j0 * kBlockBytes, 0, NB - 1, q, a);
+    else
+        read_slice_at<NB>(row, j0, nblk - 1, q, a);
 }
 
 // Max over the four lanes of a column (lanes n, n+16, n+32, n+48).
@@ -190,13 +222,43 @@ __device__ __forceinline__ f32x4_t unscale(f32x4_t acc, int s) {
     return f32x4_t{ldexpf(acc[0], s), ldexpf(acc[1], s), ldexpf(acc[2], s), ldexpf(acc[3], s)};
 }
 
-// Item range of this workgroup: items are (active expert a, row tile t) in a-major order, split
-// into equal contiguous ranges over the grid, so a workgroup mostly stays on one expert and its
-// token rows are loaded once.
-__device__ __forceinline__ void item_range(int total, int &i0, int &i1) {
-    const int per = (total + gridDim.x - 1) / gridDim.x;
-    i0 = min((int)blockIdx.x * per, total);
+// Item range of this workgroup: items are (active expert a, row tile t) in a-major order. When
+// the grid holds g >= 1 workgroups per active expert without costing balance, each expert's tiles
+// are split over g workgroups and no workgroup changes expert: its token rows are loaded once,
+// before its stream of tiles starts, instead of at an expert change, where the load (vector
+// memory completes in issue order) would wait for every tile in flight. Otherwise the items are
+// split into equal contiguous ranges.
+__device__ __forceinline__ void item_range(int n_active, int tiles, int &i0, int &i1) {
+    const int G = gridDim.x, b = blockIdx.x, total = n_active * tiles;
+    const int per = (total + G - 1) / G;
+    if (n_active > 0 && n_active <= G) {
+        const int g = G / n_active, per_g = (tiles + g - 1) / g;
+        if (per_g <= per + 1) {
+            const int a = b / g, r = b % g;
+            i0 = i1 = 0;
+            if (a < n_active) {
+                i0 = a * tiles + r * tiles / g;
+                i1 = a * tiles + (r + 1) * tiles / g;
+            }
+            return;
+        }
+    }
+    i0 = min(b * per, total);
     i1 = min(i0 + per, total);
+}
+
+// Gate/up tile layout in LDS: 16 rows (8 gate, then the 8 matching up rows), one per lane row of
+// the MFMA tile, each lane reading its own row. Rows are whole 16-byte chunks (hidden is a
+// multiple of 256) and sit one chunk further apart than their length. For hidden 2560 (1440-byte
+// rows, 360 dwords: 8 past a multiple of the 32 LDS banks) the same byte of rows n and n + 4
+// would fall in one bank; at a 1456-byte pitch only rows n and n + 8 share one, which halves the
+// bank conflicts of the reads. The pad chunk is filled with a copy of the row's first chunk, so
+// each direct-to-LDS load still moves 64 whole chunks.
+__host__ __device__ inline int gu_pitch(int rb) { return rb + 16; }
+constexpr int kMaxTileInst = 10;   // loads per wave for one padded tile (hidden <= 4096)
+
+__device__ __forceinline__ void dma16(const void *g, void *lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
 }
 
 // The CSR entries a workgroup needs: its experts, their first CSR slot, pair count and first 16
@@ -230,7 +292,7 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
     if (pairs_in_lds)
         for (int j = tid; j < P; j += kThreads) s_pair[j] = pair_ids[j];
     lds_barrier();
-    item_range(meta.n_active * tiles, i0, i1);
+    item_range(meta.n_active, tiles, i0, i1);
     a_first = i0 / tiles;
     const int na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
     if (tid < na) {
@@ -267,7 +329,8 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     int32_t F, int32_t nbuf, int32_t ring_bytes, float *__restrict__ h, int32_t *__restrict__ pos) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = H / kBlockWeights * kBlockBytes;
-    const int side = kGuO * rb, tile_bytes = 2 * side;
+    const int side = kGuO * rb;
+    const int pitch = gu_pitch(rb), tile_bytes = 2 * kGuO * pitch;
     uint8_t *wb = smem;                                                // [nbuf][16 rows]
     float *red = reinterpret_cast<float *>(smem + ring_bytes);         // [2][wave][col][16 rows]
     __shared__ Meta meta;
@@ -280,19 +343,36 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     int i0, i1, a_first;
     load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, E, P,
               tiles, i0, i1, a_first);
-    const int n_inst = 2 * stage_async_count<kThreads>(side);
-    const int depth = nbuf - 1;   // tiles in flight while one is computed
+    // load k of this wave moves LDS chunk p = 64 wave + 256 k + lane of the tile,
+    // row p / cpr, chunk p % cpr of it (the last one a copy of chunk 0); its source offset within
+    // the gate or up rows of the tile (sign bit: up) is the same for every tile
+    const int cpr = rb / 16 + 1, units = 2 * kGuO * cpr;
+    int32_t src_off[kMaxTileInst];
+#pragma unroll
+    for (int kk = 0; kk < kMaxTileInst; kk++) {
+        const int p = wave * 64 + kk * kThreads + lane, r = p / cpr, c = p - r * cpr;
+        src_off[kk] = ((r & (kGuO - 1)) * rb + (c == cpr - 1 ? 0 : c) * 16) |
+                      (r >= kGuO ? (int32_t)0x80000000 : 0);
+    }
+    const int n_inst = stage_async_count<kThreads>(units * 16);
     // stream cursor: the next item to load (expert index, row tile, ring slot)
     int ia = 0, it = i0 - a_first * tiles, is = 0;
     auto issue_next = [&]() {
         const int e = meta.e[ia];
         uint8_t *dst = wb + is * tile_bytes;
-        stage_async<kThreads>(dst, gate + e * gate_stride + (int64_t)it * side, side);
-        stage_async<kThreads>(dst + side, up + e * up_stride + (int64_t)it * side, side);
+        const uint8_t *gt = gate + e * gate_stride + (int64_t)it * side;
+        const uint8_t *ut = up + e * up_stride + (int64_t)it * side;
+#pragma unroll
+        for (int kk = 0; kk < kMaxTileInst; kk++) {
+            const int base = wave * 64 + kk * kThreads;
+            if (base < units && base + lane < units) {
+                const int32_t o = src_off[kk];
+                dma16((o < 0 ? ut : gt) + (o & 0x7fffffff), dst + base * 16);
+            }
+        }
         if (++it == tiles) { it = 0; ++ia; }
         if (++is == nbuf) is = 0;
     };
-    for (int i = i0; i < min(i0 + depth, i1); i++) issue_next();
 
     // reduction of a unit by one wave: lane -> (feature f, token column nn)
     auto reduce = [&](const float *rp, int q0, int c, int t, int mt) {
@@ -310,33 +390,46 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
 
     u32x4_t xb[NB][2];
     int xs = 0, cur_a = -1, cur_c = -1;
+    // the token rows of the first unit are loaded right after the first tile, before the rest of
+    // the ring: waiting for them then waits for one tile, not for every buffer in flight
+    auto load_x = [&](int a_, int c_) {
+        const int mt = min(kCols, meta.m[a_] - c_ * kCols);
+        const uint16_t *row = nullptr;
+        if (n < mt) row = x + (int64_t)(chunk_pid(meta, pair_ids, a_, c_, n) / k) * H;
+        xs = load_x_operands<NB>(xb, row, blk0, nblk, q);
+        cur_a = a_;
+        cur_c = c_;
+    };
+    if (i0 < i1) {
+        issue_next();
+        load_x(0, 0);
+    }
+    for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
+
     int unit = 0, p_q0 = 0, p_c = 0, p_t = 0, p_mt = 0;
     int a = 0, t = i0 - a_first * tiles, slot = 0;   // item i: expert index, row tile, ring slot
     for (int i = i0; i < i1; i++) {
         const int q0 = meta.q0[a], m = meta.m[a];
-        // this lane's row, at its wave's K slice
-        const uint8_t *wt = wb + slot * tile_bytes + n * rb + blk0 * kBlockBytes;
+        const uint8_t *wt = wb + slot * tile_bytes + n * pitch;   // this lane's row of the tile
         for (int c = 0; c * kCols < m; c++, unit++) {
             const int mt = min(kCols, m - c * kCols);
-            if (a != cur_a || c != cur_c) {   // token rows of this chunk into registers
-                const uint16_t *row = nullptr;
-                if (n < mt) row = x + (int64_t)(chunk_pid(meta, pair_ids, a, c, n) / k) * H;
-                xs = load_x_operands<NB>(xb, row, blk0, nblk, q);
-                cur_a = a;
-                cur_c = c;
-            }
-            if (c == 0) vm_wait_le(min(depth - 1, i1 - 1 - i) * n_inst);   // tile i landed
+            if (a != cur_a || c != cur_c) load_x(a, c);   // token rows of this chunk
+            if (c == 0) vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst);   // tile i landed
             lds_barrier();   // tile i and the previous unit's partials visible to all
-            if (c == 0 && i + depth < i1) issue_next();   // into item i-1's buffer
+            SliceA<NB> sa;
+            read_slice<NB>(wt, blk0, nblk, q, sa);
+            if ((c + 1) * kCols >= m && i + nbuf < i1) {
+                lds_barrier();   // tile i is in every wave's registers: refill its buffer
+                issue_next();
+            }
             if (unit > 0 && wave == (unit - 1) % kWaves)
                 reduce(red + ((unit - 1) & 1) * kRedFloats, p_q0, p_c, p_t, p_mt);
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NB; j++) {
-                f16x8_t a0, a1;
-                load_a(wt + j * kBlockBytes, q, a0, a1);
-                acc = mfma16(a0, __builtin_bit_cast(f16x8_t, xb[j][0]), acc);
-                acc = mfma16(a1, __builtin_bit_cast(f16x8_t, xb[j][1]), acc);
+                const f16x2_t S = scale_f16x2(sa.s[j]);
+                acc = mfma16(dequant8(sa.c[j][0], S), __builtin_bit_cast(f16x8_t, xb[j][0]), acc);
+                acc = mfma16(dequant8(sa.c[j][1], S), __builtin_bit_cast(f16x8_t, xb[j][1]), acc);
             }
             *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats + (wave * kCols + n) * 16 +
                                          4 * q) = unscale(acc, xs);
@@ -387,7 +480,6 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
               tiles, i0, i1, a_first);
     if (i0 >= i1) return;
     const int n_inst = stage_async_count<kThreads>(tile_bytes);
-    const int depth = nbuf - 1;
     int ia = 0, it = i0 - a_first * tiles, is = 0;   // stream cursor
     auto issue_next = [&]() {
         const int e = meta.e[ia];
@@ -396,8 +488,6 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
         if (++it == tiles) { it = 0; ++ia; }
         if (++is == nbuf) is = 0;
     };
-    for (int i = i0; i < min(i0 + depth, i1); i++) issue_next();
-
     // (row r of the item, token column nn) sums the KS slices of r's row tile
     auto reduce = [&](const float *rp, int a, int c, int t, int mt) {
         for (int u = tid; u < rows * mt; u += kThreads) {
@@ -410,28 +500,40 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
 
     u32x4_t hh[NB][2], hl[NB][2];
     int hs = 0, cur_a = -1, cur_c = -1;
+    auto load_h = [&](int a_, int c_) {
+        const int mt = min(kCols, meta.m[a_] - c_ * kCols);
+        const float *row = n < mt ? h + (int64_t)(meta.q0[a_] + c_ * kCols + n) * F : nullptr;
+        hs = load_h_operands<NB>(hh, hl, row, blk0, nblk, q);
+        cur_a = a_;
+        cur_c = c_;
+    };
+    // the h rows of the first unit come right after the first tile, before the rest of the ring
+    issue_next();
+    load_h(0, 0);
+    for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
+
     int unit = 0, p_a = 0, p_c = 0, p_t = 0, p_mt = 0;
     int a = 0, t = i0 - a_first * tiles, slot = 0;
     for (int i = i0; i < i1; i++) {
-        const int q0 = meta.q0[a], m = meta.m[a];
+        const int m = meta.m[a];
         const uint8_t *wt = wb + slot * tile_bytes + (rt * 16 + n) * rb;
         for (int c = 0; c * kCols < m; c++, unit++) {
             const int mt = min(kCols, m - c * kCols);
-            if (a != cur_a || c != cur_c) {
-                const float *row = n < mt ? h + (int64_t)(q0 + c * kCols + n) * F : nullptr;
-                hs = load_h_operands<NB>(hh, hl, row, blk0, nblk, q);
-                cur_a = a;
-                cur_c = c;
-            }
-            if (c == 0) vm_wait_le(min(depth - 1, i1 - 1 - i) * n_inst);
+            if (a != cur_a || c != cur_c) load_h(a, c);
+            if (c == 0) vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst);   // tile i landed
             lds_barrier();
-            if (c == 0 && i + depth < i1) issue_next();
+            SliceA<NB> sa;
+            read_slice<NB>(wt, blk0, nblk, q, sa);
+            if ((c + 1) * kCols >= m && i + nbuf < i1) {
+                lds_barrier();   // tile i is in every wave's registers: refill its buffer
+                issue_next();
+            }
             if (KS > 1 && unit > 0) reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int j = 0; j < NB; j++) {
-                f16x8_t a0, a1;   // blocks past the row (last slice): zero B, any valid A
-                load_a(wt + min(blk0 + j, nblk - 1) * kBlockBytes, q, a0, a1);
+                const f16x2_t S = scale_f16x2(sa.s[j]);
+                const f16x8_t a0 = dequant8(sa.c[j][0], S), a1 = dequant8(sa.c[j][1], S);
                 acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hh[j][0]), acc);
                 acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hl[j][0]), acc);
                 acc = mfma16(a1, __builtin_bit_cast(f16x8_t, hh[j][1]), acc);
@@ -581,8 +683,8 @@ int launch_gu(const FfnArgs &a, const DecodeWs &d, int max_active, hipStream_t s
     auto kern = gu_decode_kernel<NB>;
     const int32_t P = a.T * a.k;
     int nbuf, ring_bytes, wgs;
-    const size_t lds = ring_plan(2 * kGuO * (size_t)row_bytes(a.H), plan_scratch_bytes(a.E, P),
-                                 nbuf, ring_bytes, wgs);
+    const size_t lds = ring_plan(2 * kGuO * (size_t)gu_pitch((int)row_bytes(a.H)),
+                                 plan_scratch_bytes(a.E, P), nbuf, ring_bytes, wgs);
     if (!lds) return MOE_ESHAPE;
     static bool attr = false;
     if (!attr) {
@@ -639,7 +741,8 @@ int decode_plan(const FfnArgs &a, int &nb_gu, int &nb_dn, int &rt) {
     if (nb_gu > kMaxGuBlocks || nb_dn > kMaxDnBlocks || a.H % (16 * rt)) return MOE_ESHAPE;
     const int32_t P = a.T * a.k;
     int nbuf, ring, wgs;
-    if (!ring_plan(2 * kGuO * (size_t)row_bytes(a.H), plan_scratch_bytes(a.E, P), nbuf, ring, wgs) ||
+    if (!ring_plan(2 * kGuO * (size_t)gu_pitch((int)row_bytes(a.H)), plan_scratch_bytes(a.E, P), nbuf,
+                   ring, wgs) ||
         !ring_plan(16 * rt * (size_t)row_bytes(a.F), plan_scratch_bytes(a.E, P), nbuf, ring, wgs))
         return MOE_ESHAPE;
     return MOE_OK;

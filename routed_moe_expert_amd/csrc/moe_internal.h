@@ -116,7 +116,7 @@ __device__ __forceinline__ int stage_async_count(int bytes) {
 // Vector memory loads complete in issue order, so this waits for everything issued before the n
 // most recent ones. The counter holds 6 bits; larger n waits for all.
 __device__ __forceinline__ void vm_wait_le(int n) {
-    switch (n) {
+    switch (__builtin_amdgcn_readfirstlane(n)) {   // a scalar branch, not per-lane compares
 #define MOE_VMW(i) case i: asm volatile("s_waitcnt vmcnt(" #i ")" ::: "memory"); break;
         MOE_VMW(1) MOE_VMW(2) MOE_VMW(3) MOE_VMW(4) MOE_VMW(5) MOE_VMW(6) MOE_VMW(7) MOE_VMW(8)
         MOE_VMW(9) MOE_VMW(10) MOE_VMW(11) MOE_VMW(12) MOE_VMW(13) MOE_VMW(14) MOE_VMW(15)
