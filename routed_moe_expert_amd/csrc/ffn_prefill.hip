@@ -6,18 +6,21 @@
 //
 //   schedule: M tiles of at most kBM consecutive CSR pairs of one expert, listed from the
 //             device CSR (no host read-back); also the pair -> CSR slot map for the combine.
-//   gemm:     one 8-wave workgroup per (N tile of 256 weight rows, M tile). The A operand is the
+//   gemm:     one 8-wave workgroup per (N tile of 512 weight rows, M tile). The A operand is the
 //             weights, staged raw in LDS one NVFP4 block per row per K step; every wave
-//             decodes its own 32 rows straight into bf16 MFMA fragments in registers -- exact,
+//             decodes its own 64 rows straight into bf16 MFMA fragments in registers -- exact,
 //             since every E2M1 x UE4M3 product is a bf16 value. The B operand is the M tile's
 //             token rows (x gathered by token for gate/up, the h_hi / h_lo rows of the CSR
 //             slots for down) with an XOR swizzle of their 16-byte parts so that fragment reads
-//             are free of bank conflicts. Five LDS stages keep four K steps in flight.
-//             v_mfma_f32_16x16x32_bf16 with fp32 accumulation; a wave owns 32 rows x 128
-//             tokens (gate/up) or 32 rows x 64 tokens (down, whose workgroups take half an M
+//             are free of bank conflicts. Three LDS stages keep two K steps in flight.
+//             v_mfma_f32_16x16x32_bf16 with fp32 accumulation; a wave owns 64 rows x 128
+//             tokens (gate/up) or 64 rows x 64 tokens (down, whose workgroups take half an M
 //             tile so that h_hi and h_lo fit the stages) and skips the second half of its token
-//             columns when the tile does not reach them.
-//             Gate/up: rows are 128 gate rows and the matching up rows; the epilogue forms
+//             columns when the tile does not reach them. Each weight row is decoded by one wave
+//             only, and each B fragment read from LDS feeds four MFMAs: per K step the LDS
+//             reads of a workgroup (the B tile once per wave) stay below what the matrix cores
+//             take to consume them, which at 32 rows per wave they did not.
+//             Gate/up: rows are 256 gate rows and the matching up rows; the epilogue forms
 //             h = SiLU(g) * u and stores it as a bf16 pair h_hi + h_lo (h_hi = bf16(h),
 //             h_lo = bf16(h - h_hi)), which carries h to about 16 significant bits. Down: the
 //             same tile times h_hi plus times h_lo, into the fp32 per-pair rows ypair.
@@ -26,6 +29,7 @@
 // Workgroups are mapped XCD-aware (hardware workgroup b runs on XCD b mod 8): M tile t runs on
 // XCD t mod 8, the N tiles of an M tile -- which share its token rows -- back to back there.
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_internal.h"
 
@@ -37,7 +41,8 @@ constexpr int kBM = 128;               // pairs per M tile
 constexpr int kCF = kBM / 16;          // token column tiles per M tile
 constexpr int kBRow = 64 * 2;          // bytes of one token row per K step (64 bf16)
 constexpr int kBBytes = kBM * kBRow;   // 16 KB per B operand per stage (128 tokens)
-constexpr int kStages = 5;            // LDS stages: four K steps in flight
+constexpr int kStages = 3;            // LDS stages: two K steps in flight
+constexpr int kRowsW = 64;            // A rows per wave
 constexpr int kGemmThreads = 512;      // 8 waves, one workgroup per CU
 
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2_t;
@@ -135,19 +140,19 @@ __host__ __device__ constexpr int blk_lds(int b) { return 16 * (b / 12) + b % 12
 // by the row so that the 8 lanes of a fragment read group hit 8 different bank groups.
 __device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ (r & 7)); }
 
-// One workgroup: N tile nt (256 weight rows) of M tile ti (gate/up: all of its up to 128 pairs;
-// down: the half hf of 64 pairs). DOWN = false: gate/up (A rows are 128 gate rows then the
-// matching up rows; K = H; B = x rows by token); DOWN = true: down (A rows are 256 rows of W_d;
+// One workgroup: N tile nt (512 weight rows) of M tile ti (gate/up: all of its up to 128 pairs;
+// down: the half hf of 64 pairs). DOWN = false: gate/up (A rows are 256 gate rows then the
+// matching up rows; K = H; B = x rows by token); DOWN = true: down (A rows are 512 rows of W_d;
 // K = F; B = h_hi and h_lo rows by CSR slot). N tiles may run past the matrix: rows beyond it
 // read the last row and are not stored.
 //
 // Each K step of 64 stages one NVFP4 block of every A row (three 12-byte direct-to-LDS loads per
 // row, lane i of a load landing at +16 i, so a row takes 48 bytes of LDS) and the B rows, in one
-// of kStages LDS stages: kStages - 1 steps are in flight while one is computed, which is what
-// covers the latency of these scattered loads. Each wave issues a fixed number of loads per step,
+// of kStages LDS stages: kStages - 1 steps are in flight while one is computed, which (at two
+// waves per SIMD and 64 MFMAs per wave per step) covers the latency of these scattered loads. Each wave issues a fixed number of loads per step,
 // so its count of outstanding loads is exact and the waits are partial.
 template <bool DOWN>
-__global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ hin_hi,
     const uint16_t *__restrict__ hin_lo, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const i32x2_t *__restrict__ tiles,
@@ -157,7 +162,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
     uint16_t *__restrict__ h_lo, float *__restrict__ ypair) {
     constexpr int kThreads = kGemmThreads;
     constexpr int kWaves = kThreads / 64;
-    constexpr int kRows = 32 * kWaves;              // A rows per workgroup
+    constexpr int kRows = kRowsW * kWaves;          // A rows per workgroup
     constexpr int kAUnits = kRows * 3;              // 12-byte A loads per step (3 per row)
     constexpr int kABytes = kAUnits * 16;           // 48 bytes per row
     constexpr int kNB = DOWN ? 2 : 1;               // B operands (h_hi, h_lo) or (x)
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
     constexpr int kBBytesW = kBM2 * kBRow;
     constexpr int kStageBytes = kABytes + kNB * kBBytesW;
     constexpr int kBUnits = kBBytesW / 16 / kThreads;    // 16-byte B loads per lane per operand
-    constexpr int kALoadsMax = (kAUnits + kThreads - 1) / kThreads;   // 2
+    constexpr int kALoadsMax = (kAUnits + kThreads - 1) / kThreads;   // 3
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int rowid[kBM2];               // token (gate/up) or CSR slot (down) of each column
 
@@ -245,16 +250,23 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
     };
     const int ops = a_loads + kNB * kBUnits;   // loads per step of this wave
 
-    f32x4_t acc[2][kCols];
+    constexpr int kAT0 = kRowsW / 16;
+    f32x4_t acc[kAT0][kCols];
 #pragma unroll
-    for (int f = 0; f < 2; f++)
+    for (int f = 0; f < kAT0; f++)
 #pragma unroll
         for (int c = 0; c < kCols; c++) acc[f][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // this wave's two 16-row A tiles: DOWN: rows 32*wave + 16f; gate/up: gate rows 16*wave
     // (f = 0) and the matching up rows (f = 1)
-    const int arow0 = DOWN ? 32 * wave : 16 * wave;
-    const int arow1 = DOWN ? 32 * wave + 16 : kRows / 2 + 16 * wave;
+    // this wave's four 16-row A tiles: DOWN: rows 64 wave + 16 f; gate/up: gate rows
+    // 32 wave + 16 f (f = 0, 1) and the matching up rows (f = 2, 3)
+    constexpr int kAT = kRowsW / 16;
+    int arow[kAT];
+#pragma unroll
+    for (int f = 0; f < kAT; f++)
+        arow[f] = DOWN ? kRowsW * wave + 16 * f
+                       : (f >= 2 ? kRows / 2 : 0) + (kRowsW / 2) * wave + 16 * (f & 1);
     // this lane's scale byte and code dwords within a staged block (12-byte loads, 16 apart)
     const int c0_off = blk_lds(4 + 8 * q), c1_off = blk_lds(8 + 8 * q);
 
@@ -265,43 +277,44 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
         lds_barrier();   // visible to all; the stage of step kb-1 is free
         if (kb + kStages - 1 < nsteps) issue(kb + kStages - 1);
         const uint8_t *st = smem + (kb % kStages) * kStageBytes;
-        // A: lane (n, q) takes scale group q of its row: K step s = weights 16q+8s .. +7
-        float S[2];
-        uint32_t cw[2][2];
+        // One K step in two sub-steps of 32. The second half of the token columns is read and
+        // multiplied only when the tile reaches it (one uniform branch).
+        auto step = [&](auto full) {
+            constexpr int kC = decltype(full)::value ? kCols : kCols / 2;
+            uint32_t sb[kAT], cw[kAT][2];
 #pragma unroll
-        for (int f = 0; f < 2; f++) {
-            const uint8_t *blk = st + ((f ? arow1 : arow0) + n) * 48;
-            S[f] = ue4m3_to_f32(blk[q]);
-            cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
-            cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
-        }
+            for (int f = 0; f < kAT; f++) {
+                const uint8_t *blk = st + (arow[f] + n) * 48;
+                sb[f] = blk[q];
+                cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
+                cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
+            }
 #pragma unroll
-        for (int s = 0; s < 2; s++) {
-            bf16x8_t af[2];
+            for (int s2 = 0; s2 < 2; s2++) {
+                bf16x8_t bfr[kNB][kC];
 #pragma unroll
-            for (int f = 0; f < 2; f++) af[f] = dequant8_bf16(cw[f][s], S[f]);
-            // token columns in two halves: the second only when the tile reaches it (one uniform
-            // branch, so each half schedules freely)
+                for (int o = 0; o < kNB; o++)
 #pragma unroll
-            for (int hh = 0; hh < 2; hh++) {
-                if (hh == 1 && ncol <= kCols / 2) break;
+                    for (int c = 0; c < kC; c++)
+                        bfr[o][c] = *reinterpret_cast<const bf16x8_t *>(
+                            st + kABytes + o * kBBytesW + 16 * b_slot(16 * c + n, 2 * q + s2));
+                // A: lane (n, q) takes scale group q of its row: sub-step s2 = weights
+                // 16q + 8 s2 .. +7
 #pragma unroll
-                for (int o = 0; o < kNB; o++) {
-                    bf16x8_t bfr[kCols / 2];
+                for (int f = 0; f < kAT; f++) {
+                    const bf16x8_t af = dequant8_bf16(cw[f][s2], ue4m3_to_f32(sb[f]));
 #pragma unroll
-                    for (int c = 0; c < kCols / 2; c++)
-                        bfr[c] = *reinterpret_cast<const bf16x8_t *>(
-                            st + kABytes + o * kBBytesW +
-                            16 * b_slot(16 * (hh * kCols / 2 + c) + n, 2 * q + s));
+                    for (int o = 0; o < kNB; o++)
 #pragma unroll
-                    for (int f = 0; f < 2; f++)
-#pragma unroll
-                        for (int c = 0; c < kCols / 2; c++)
-                            acc[f][hh * kCols / 2 + c] =
-                                mfma_bf16(af[f], bfr[c], acc[f][hh * kCols / 2 + c]);
+                        for (int c = 0; c < kC; c++)
+                            acc[f][c] = mfma_bf16(af, bfr[o][c], acc[f][c]);
                 }
             }
-        }
+        };
+        if (ncol > kCols / 2)
+            step(std::true_type{});
+        else
+            step(std::false_type{});
     }
 
     // epilogue: lane holds rows 4q..4q+3 of each 16-row A tile for token column 16c + n
@@ -312,15 +325,17 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
             if (col < mt) {
                 const int64_t prow = (int64_t)pair_ids[q0 + col] * H;
 #pragma unroll
-                for (int f = 0; f < 2; f++) {
-                    const int r = nt * kRows + (f ? arow1 : arow0) + 4 * q;
+                for (int f = 0; f < kAT; f++) {
+                    const int r = nt * kRows + arow[f] + 4 * q;
                     if (r < H) *reinterpret_cast<f32x4_t *>(ypair + prow + r) = acc[f][c];
                 }
             }
         }
     } else {
-        const int o = nt * (kRows / 2) + 16 * wave + 4 * q;   // features o..o+3
-        if (o < F) {
+#pragma unroll
+        for (int t = 0; t < 2; t++) {   // gate tile t and the matching up tile 2 + t
+            const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q;   // o..o+3
+            if (o >= F) continue;
 #pragma unroll
             for (int c = 0; c < kCols; c++) {
                 const int col = 16 * c + n;
@@ -328,8 +343,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_kernel(
                     uint32_t hi2[2], lo2[2];
 #pragma unroll
                     for (int v = 0; v < 4; v += 2) {
-                        const float h0 = silu(acc[0][c][v]) * acc[1][c][v];
-                        const float h1 = silu(acc[0][c][v + 1]) * acc[1][c][v + 1];
+                        const float h0 = silu(acc[t][c][v]) * acc[2 + t][c][v];
+                        const float h1 = silu(acc[t][c][v + 1]) * acc[2 + t][c][v + 1];
                         const __bf16 g0 = (__bf16)h0, g1 = (__bf16)h1;
                         hi2[v / 2] = pack_bf16((float)g0, (float)g1);
                         lo2[v / 2] = pack_bf16(h0 - (float)g0, h1 - (float)g1);
@@ -374,7 +389,7 @@ PrefillWs carve(void *ws, int32_t P, int32_t E, int32_t F) {
 
 template <bool DOWN>
 int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
-    constexpr int kRows = 32 * (kGemmThreads / 64);
+    constexpr int kRows = kRowsW * (kGemmThreads / 64);
     constexpr size_t lds = kStages * (kRows * 48 + kBBytes);   // B: 128 x1 or 64 x2 rows
     static bool attr = false;
     if (!attr) {
