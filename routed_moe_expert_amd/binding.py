@@ -7,6 +7,7 @@ when the library has not been built.
 from __future__ import annotations
 
 import ctypes
+import importlib.util
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +33,11 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python routed_moe_expert_amd/build.py` (hipcc, gfx950)")
+    # One HIP runtime per process: PyTorch ships its own libamdhip64 (same soname, loaded under
+    # another file name). Loaded after ours, it would be a second runtime that knows nothing of
+    # our kernels' module or of the other's allocations; loaded first, ours binds to it.
+    if importlib.util.find_spec("torch") is not None:
+        import torch  # noqa: F401
     l = ctypes.CDLL(LIB_PATH)
     i32, sz, vp = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
     l.moe_route_bucket_ws.restype = sz

@@ -98,3 +98,19 @@ def test_bucket_host_checks(over, status):
 def test_errors_raise_by_default():
     with pytest.raises(moe.MoeError):
         moe.moe_route_bucket(0, 4, 2, 8, 0, 0, 0, 0, 0, stream=0)
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """The package imported before torch must still leave a single HIP runtime mapped."""
+    import subprocess
+    import sys
+    code = ("import routed_moe_expert_amd, torch\n"
+            "paths = set()\n"
+            "for line in open('/proc/self/maps'):\n"
+            "    p = line.split()[-1]\n"
+            "    if 'libamdhip64' in p: paths.add(p)\n"
+            "print(len(paths))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
