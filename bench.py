@@ -40,8 +40,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "3de1908eff825a0a5a160d27bc49928a970a1806260cca0996d756e98fb902ca",
-        "fetch_kib": 54265.8, "write_kib": 165.7,
+        "sha256": "f7100fd97014434a0fc6c54137c3199149d398793dfb48e2b479c99621e17798",
+        "fetch_kib": 54327.1, "write_kib": 168.8,
     },
 }
 
