@@ -6,6 +6,7 @@
 //
 //   schedule: M tiles of at most kBM consecutive CSR pairs of one expert, listed from the
 //             device CSR (no host read-back); also the pair -> CSR slot map for the combine.
+//   xcast:    x to f16 per token row, scaled by a power of two (exact), for the gate/up GEMM.
 //   gemm:     one 8-wave workgroup per (N tile of 512 weight rows, M tile). The A operand is the
 //             weights, staged raw in LDS one NVFP4 block per row per K step; every wave
 //             decodes its own 64 rows straight into bf16 MFMA fragments in registers -- exact,
@@ -13,13 +14,16 @@
 //             token rows (x gathered by token for gate/up, the h_hi / h_lo rows of the CSR
 //             slots for down) with an XOR swizzle of their 16-byte parts so that fragment reads
 //             are free of bank conflicts. Three LDS stages keep two K steps in flight.
-//             v_mfma_f32_16x16x32_bf16 with fp32 accumulation; a wave owns 64 rows x 128
+//             MFMA 16x16x32 with fp32 accumulation; a wave owns 64 rows x 128
 //             tokens (gate/up) or 64 rows x 64 tokens (down, whose workgroups take half an M
 //             tile so that h_hi and h_lo fit the stages) and skips the second half of its token
 //             columns when the tile does not reach them. Each weight row is decoded by one wave
 //             only, and each B fragment read from LDS feeds four MFMAs: per K step the LDS
 //             reads of a workgroup (the B tile once per wave) stay below what the matrix cores
 //             take to consume them, which at 32 rows per wave they did not.
+//             Gate/up multiplies in f16 (v_mfma_f32_16x16x32_f16: weights decoded to f16 at
+//             half the VALU of bf16, which has no packed multiply; x cast per token) and
+//             unscales its sums per token column. Down multiplies in bf16.
 //             Gate/up: rows are 256 gate rows and the matching up rows; the epilogue forms
 //             h = SiLU(g) * u and stores it as a bf16 pair h_hi + h_lo (h_hi = bf16(h),
 //             h_lo = bf16(h - h_hi)), which carries h to about 16 significant bits. Down: the
@@ -46,6 +50,8 @@ constexpr int kRowsW = 64;            // A rows per wave
 constexpr int kGemmThreads = 512;      // 8 waves, one workgroup per CU
 
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 
 // ------------------------------------------------------------------------------- schedule
 
@@ -99,6 +105,53 @@ __global__ __launch_bounds__(kThreadsSched) void schedule_kernel(
     if (threadIdx.x == 0) n_tiles[0] = min(total, max_tiles);
 }
 
+// ------------------------------------------------------------------------------ x to f16
+
+constexpr int kCastThreads = 256;
+
+// Token row t of x (bf16) -> f16 scaled by 2^-xs[t], xs[t] chosen so that the row's largest
+// magnitude lands in [2^14, 2^15): exact for every value within 2^28 of that maximum (bf16 has 8
+// significant bits, f16 11; values further down go subnormal and keep fewer), so the gate/up
+// GEMM can run on f16 MFMA and unscale its fp32 sums per token column.
+__global__ __launch_bounds__(kCastThreads) void xcast_kernel(const uint16_t *__restrict__ x,
+                                                            int32_t H, uint16_t *__restrict__ x16,
+                                                            int32_t *__restrict__ xs) {
+    __shared__ uint32_t wmax[kCastThreads / 64];
+    const int t = blockIdx.x, tid = threadIdx.x;
+    const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + (int64_t)t * H);
+    const int n8 = H / 8;   // 8 bf16 per 16-byte part
+    uint32_t amax = 0;      // |x| as bf16 bits: ordered like the magnitudes for finite values
+    for (int i = tid; i < n8; i += kCastThreads) {
+        const u32x4_t v = src[i];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            amax = max(amax, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));
+    }
+    for (int d = 32; d > 0; d >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
+    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+    __syncthreads();
+    amax = wmax[0];
+    for (int w = 1; w < kCastThreads / 64; w++) amax = max(amax, wmax[w]);
+    const float mx = __uint_as_float(amax << 16);
+    int e = 0;
+    if (mx > 0.f) (void)frexpf(mx, &e);   // mx = f * 2^e, f in [0.5, 1)
+    const int sc = mx > 0.f ? e - 15 : 0;
+    const float inv = ldexpf(1.0f, -sc);
+    u32x4_t *dst = reinterpret_cast<u32x4_t *>(x16 + (int64_t)t * H);
+    for (int i = tid; i < n8; i += kCastThreads) {
+        const u32x4_t v = src[i];
+        u32x4_t o;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const f16x2_t h2 = {(_Float16)(__uint_as_float(v[j] << 16) * inv),
+                                (_Float16)(__uint_as_float(v[j] & 0xffff0000u) * inv)};
+            o[j] = __builtin_bit_cast(uint32_t, h2);
+        }
+        dst[i] = o;
+    }
+    if (tid == 0) xs[t] = sc;
+}
+
 // ------------------------------------------------------------------------------- gemm
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -116,10 +169,31 @@ __device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t c, float S) {
                                                 pack_bf16(v3[0] * S, v3[1] * S)});
 }
 
+// 8 E2M1 codes times the group scale -> 8 f16, exact (every E2M1 x UE4M3 product is an f16
+// value). The converts scale by 2^8 (their scale operand contributes its exponent only); the
+// UE4M3 byte shifted into the f16 exponent and mantissa fields reads as 2^-8 times its value,
+// for normal and subnormal bytes alike. Half the VALU of the bf16 route, which has no packed
+// multiply.
+__device__ __forceinline__ f16x8_t dequant8_f16(uint32_t c, uint32_t scale_byte) {
+    const _Float16 s = __builtin_bit_cast(f16x2_t, scale_byte << 7)[0];
+    const f16x2_t S = {s, s};
+    const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 0) * S;
+    const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 1) * S;
+    const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 2) * S;
+    const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c, 256.0f, 3) * S;
+    return __builtin_bit_cast(f16x8_t, u32x4_t{__builtin_bit_cast(uint32_t, p0),
+                                               __builtin_bit_cast(uint32_t, p1),
+                                               __builtin_bit_cast(uint32_t, p2),
+                                               __builtin_bit_cast(uint32_t, p3)});
+}
+
 // Target builtins stay inside __device__ helpers: used directly in a kernel template they make
 // its host-side instantiation fail, and the launch stub goes missing.
 __device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ void dma4(const void *g, void *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 4, 0, 0);
@@ -158,8 +232,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const int32_t *__restrict__ pair_ids, const i32x2_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, int32_t max_tiles, int32_t n_ntiles,
     const uint8_t *__restrict__ w0, int64_t s0, const uint8_t *__restrict__ w1, int64_t s1,
-    int32_t k, int32_t K, int32_t F, int32_t H, uint16_t *__restrict__ h_hi,
-    uint16_t *__restrict__ h_lo, float *__restrict__ ypair) {
+    int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
+    uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, float *__restrict__ ypair) {
     constexpr int kThreads = kGemmThreads;
     constexpr int kWaves = kThreads / 64;
     constexpr int kRows = kRowsW * kWaves;          // A rows per workgroup
@@ -250,6 +324,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     };
     const int ops = a_loads + kNB * kBUnits;   // loads per step of this wave
 
+    // operand type: gate/up multiplies f16 (x cast per token by xcast_kernel, weights decoded to
+    // f16), down bf16 (h as bf16 hi + lo)
+    using BT = std::conditional_t<DOWN, bf16x8_t, f16x8_t>;
     constexpr int kAT0 = kRowsW / 16;
     f32x4_t acc[kAT0][kCols];
 #pragma unroll
@@ -291,23 +368,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; s2++) {
-                bf16x8_t bfr[kNB][kC];
+                BT bfr[kNB][kC];
 #pragma unroll
                 for (int o = 0; o < kNB; o++)
 #pragma unroll
                     for (int c = 0; c < kC; c++)
-                        bfr[o][c] = *reinterpret_cast<const bf16x8_t *>(
+                        bfr[o][c] = *reinterpret_cast<const BT *>(
                             st + kABytes + o * kBBytesW + 16 * b_slot(16 * c + n, 2 * q + s2));
                 // A: lane (n, q) takes scale group q of its row: sub-step s2 = weights
                 // 16q + 8 s2 .. +7
 #pragma unroll
                 for (int f = 0; f < kAT; f++) {
-                    const bf16x8_t af = dequant8_bf16(cw[f][s2], ue4m3_to_f32(sb[f]));
+                    if constexpr (DOWN) {
+                        const bf16x8_t af = dequant8_bf16(cw[f][s2], ue4m3_to_f32(sb[f]));
 #pragma unroll
-                    for (int o = 0; o < kNB; o++)
+                        for (int o = 0; o < kNB; o++)
 #pragma unroll
-                        for (int c = 0; c < kC; c++)
-                            acc[f][c] = mfma_bf16(af, bfr[o][c], acc[f][c]);
+                            for (int c = 0; c < kC; c++)
+                                acc[f][c] = mfma_bf16(af, bfr[o][c], acc[f][c]);
+                    } else {
+                        const f16x8_t af = dequant8_f16(cw[f][s2], sb[f]);
+#pragma unroll
+                        for (int c = 0; c < kC; c++) acc[f][c] = mfma_f16(af, bfr[0][c], acc[f][c]);
+                    }
                 }
             }
         };
@@ -340,14 +423,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
             for (int c = 0; c < kCols; c++) {
                 const int col = 16 * c + n;
                 if (col < mt) {
+                    const int sc = xs[rowid[col]];   // the token row's f16 scale exponent
                     uint32_t hi2[2], lo2[2];
 #pragma unroll
                     for (int v = 0; v < 4; v += 2) {
-                        const float h0 = silu(acc[t][c][v]) * acc[2 + t][c][v];
-                        const float h1 = silu(acc[t][c][v + 1]) * acc[2 + t][c][v + 1];
-                        const __bf16 g0 = (__bf16)h0, g1 = (__bf16)h1;
-                        hi2[v / 2] = pack_bf16((float)g0, (float)g1);
-                        lo2[v / 2] = pack_bf16(h0 - (float)g0, h1 - (float)g1);
+                        const float g0 = ldexpf(acc[t][c][v], sc), u0 = ldexpf(acc[2 + t][c][v], sc);
+                        const float g1 = ldexpf(acc[t][c][v + 1], sc);
+                        const float u1 = ldexpf(acc[2 + t][c][v + 1], sc);
+                        const float h0 = silu(g0) * u0, h1 = silu(g1) * u1;
+                        const __bf16 b0 = (__bf16)h0, b1 = (__bf16)h1;
+                        hi2[v / 2] = pack_bf16((float)b0, (float)b1);
+                        lo2[v / 2] = pack_bf16(h0 - (float)b0, h1 - (float)b1);
                     }
                     const int64_t off = (int64_t)(q0 + col) * F + o;
                     *reinterpret_cast<i32x2_t *>(h_hi + off) = i32x2_t{(int)hi2[0], (int)hi2[1]};
@@ -366,11 +452,13 @@ struct PrefillWs {
     int32_t *n_tiles;
     uint16_t *h_hi, *h_lo;
     float *ypair;
+    uint16_t *x16;   // [T][H] x as scaled f16 (in the ypair region: dead before down writes it)
+    int32_t *xs;     // [T] its scale exponents
 };
 
 int max_tiles(int32_t P, int32_t E) { return P / kBM + std::min(E, P) + 1; }
 
-PrefillWs carve(void *ws, int32_t P, int32_t E, int32_t F) {
+PrefillWs carve(void *ws, int32_t T, int32_t P, int32_t E, int32_t H, int32_t F) {
     uint8_t *b = static_cast<uint8_t *>(ws);
     PrefillWs w;
     w.pos = reinterpret_cast<int32_t *>(b);
@@ -384,6 +472,8 @@ PrefillWs carve(void *ws, int32_t P, int32_t E, int32_t F) {
     w.h_lo = reinterpret_cast<uint16_t *>(b);
     b += align256(2 * (size_t)P * F);
     w.ypair = reinterpret_cast<float *>(b);
+    w.x16 = reinterpret_cast<uint16_t *>(b);   // 2 T H bytes <= 4 P H: P = T k >= T
+    w.xs = reinterpret_cast<int32_t *>(b + align256(2 * (size_t)T * H));
     return w;
 }
 
@@ -408,12 +498,13 @@ int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
         hipLaunchKernelGGL((gemm_kernel<true>), dim3(grid), dim3(kGemmThreads), lds, s, nullptr,
                            w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt, n_ntiles,
                            a.down.base, a.down.expert_stride, nullptr, (int64_t)0, a.k, a.F, a.F,
-                           a.H, nullptr, nullptr, w.ypair);
+                           a.H, nullptr, nullptr, nullptr, w.ypair);
     else
-        hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kGemmThreads), lds, s, a.x,
-                           nullptr, nullptr, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt,
-                           n_ntiles, a.gate.base, a.gate.expert_stride, a.up.base,
-                           a.up.expert_stride, a.k, a.H, a.F, a.H, w.h_hi, w.h_lo, nullptr);
+        hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kGemmThreads), lds, s,
+                           (const uint16_t *)w.x16, nullptr, nullptr, a.offsets, a.pair_ids,
+                           w.tiles, w.n_tiles, mt, n_ntiles, a.gate.base, a.gate.expert_stride,
+                           a.up.base, a.up.expert_stride, a.k, a.H, a.F, a.H,
+                           (const int32_t *)w.xs, w.h_hi, w.h_lo, nullptr);
     prof_stop(id, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
@@ -428,13 +519,15 @@ size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
 
 int launch_prefill(const FfnArgs &a, hipStream_t s) {
     const int32_t P = a.T * a.k;
-    const PrefillWs w = carve(a.ws, P, a.E, a.F);
+    const PrefillWs w = carve(a.ws, a.T, P, a.E, a.H, a.F);
     const int mt = max_tiles(P, a.E);
     const int sched_blocks = std::max(1, std::min(256, (P + kThreadsSched - 1) / kThreadsSched));
     prof_start(MOE_KERNEL_SCHEDULE, s);
     hipLaunchKernelGGL(schedule_kernel, dim3(sched_blocks), dim3(kThreadsSched), 0, s, a.offsets,
                        a.pair_ids, a.active, a.counts, P, mt, w.tiles, w.n_tiles, w.pos);
     prof_stop(MOE_KERNEL_SCHEDULE, s);
+    if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
+    hipLaunchKernelGGL(xcast_kernel, dim3(a.T), dim3(kCastThreads), 0, s, a.x, a.H, w.x16, w.xs);
     if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
     int st = launch_gemm<false>(a, w, mt, s);
     if (st != MOE_OK) return st;
