@@ -294,7 +294,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp32" if decode else "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": desc, "E": E, "H": H, "F": F, "top_k": k, "T": T,
                    "path": "decode" if decode else "prefill",

@@ -1,4 +1,4 @@
-// Prefill path of the routed NVFP4 FFN: grouped GEMMs over expert-first CSR tiles on bf16 MFMA.
+// Prefill path of the routed NVFP4 FFN: grouped GEMMs over expert-first CSR tiles on f16 MFMA.
 //
 // moe_sk_repro.rs times a prefill MoE layer as three grouped GEMMs (gate, up, down) over the
 // expert buckets, in 128-row M tiles; here gate and up share one kernel so the SiLU(g) * u
@@ -9,8 +9,8 @@
 //   xcast:    x to f16 per token row, scaled by a power of two (exact), for the gate/up GEMM.
 //   gemm:     one 8-wave workgroup per (N tile of 512 weight rows, M tile). The A operand is the
 //             weights, staged raw in LDS one NVFP4 block per row per K step; every wave
-//             decodes its own 64 rows straight into bf16 MFMA fragments in registers -- exact,
-//             since every E2M1 x UE4M3 product is a bf16 value. The B operand is the M tile's
+//             decodes its own 64 rows straight into f16 MFMA fragments in registers -- exact,
+//             since every E2M1 x UE4M3 product is an f16 value. The B operand is the M tile's
 //             token rows (x gathered by token for gate/up, the h_hi / h_lo rows of the CSR
 //             slots for down) with an XOR swizzle of their 16-byte parts so that fragment reads
 //             are free of bank conflicts. Three LDS stages keep two K steps in flight.
@@ -21,13 +21,16 @@
 //             only, and each B fragment read from LDS feeds four MFMAs: per K step the LDS
 //             reads of a workgroup (the B tile once per wave) stay below what the matrix cores
 //             take to consume them, which at 32 rows per wave they did not.
-//             Gate/up multiplies in f16 (v_mfma_f32_16x16x32_f16: weights decoded to f16 at
-//             half the VALU of bf16, which has no packed multiply; x cast per token) and
-//             unscales its sums per token column. Down multiplies in bf16.
+//             Both multiply in f16 (v_mfma_f32_16x16x32_f16: weights decoded to f16 at half
+//             the VALU of bf16, which has no packed multiply). Gate/up takes x cast per token
+//             (exact, power-of-two scaled) and unscales its sums per token column.
 //             Gate/up: rows are 256 gate rows and the matching up rows; the epilogue forms
-//             h = SiLU(g) * u and stores it as a bf16 pair h_hi + h_lo (h_hi = bf16(h),
-//             h_lo = bf16(h - h_hi)), which carries h to about 16 significant bits. Down: the
-//             same tile times h_hi plus times h_lo, into the fp32 per-pair rows ypair.
+//             h = SiLU(g) * u and stores it as an f16 pair, h = 2^s (h_hi + h_lo) with one
+//             power-of-two s per (pair, the tile's 256 features) bringing their largest |h| into
+//             [2^14, 2^15) (about 22 significant bits). Down: the same tile times h_hi plus times
+//             h_lo, K segment by K segment: at each new segment the running fp32 sums are
+//             rescaled to its exponent (exact), and the epilogue applies the last one; into the
+//             fp32 per-pair rows ypair.
 //   combine:  the decode path's ordered fp32 combine.
 //
 // Workgroups are mapped XCD-aware (hardware workgroup b runs on XCD b mod 8): M tile t runs on
@@ -43,11 +46,14 @@ namespace {
 constexpr int kThreadsSched = 256;
 constexpr int kBM = 128;               // pairs per M tile
 constexpr int kCF = kBM / 16;          // token column tiles per M tile
-constexpr int kBRow = 64 * 2;          // bytes of one token row per K step (64 bf16)
+constexpr int kBRow = 64 * 2;          // bytes of one token row per K step (64 f16)
 constexpr int kBBytes = kBM * kBRow;   // 16 KB per B operand per stage (128 tokens)
 constexpr int kStages = 3;            // LDS stages: two K steps in flight
 constexpr int kRowsW = 64;            // A rows per wave
+
 constexpr int kGemmThreads = 512;      // 8 waves, one workgroup per CU
+constexpr int kSegF = kRowsW / 2 * (kGemmThreads / 64);   // h features per gate/up N tile (256)
+constexpr int kMaxSeg = 32;           // h scale segments per pair: ff <= 32 * 256
 
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
@@ -154,21 +160,6 @@ __global__ __launch_bounds__(kCastThreads) void xcast_kernel(const uint16_t *__r
 
 // ------------------------------------------------------------------------------- gemm
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    bf16x2_t v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// 8 E2M1 codes (one code dword) times the group scale S -> 8 bf16, exact.
-__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t c, float S) {
-    f32x2_t v0 = e2m1x2_to_f32<0>(c), v1 = e2m1x2_to_f32<1>(c);
-    f32x2_t v2 = e2m1x2_to_f32<2>(c), v3 = e2m1x2_to_f32<3>(c);
-    return __builtin_bit_cast(bf16x8_t, u32x4_t{pack_bf16(v0[0] * S, v0[1] * S),
-                                                pack_bf16(v1[0] * S, v1[1] * S),
-                                                pack_bf16(v2[0] * S, v2[1] * S),
-                                                pack_bf16(v3[0] * S, v3[1] * S)});
-}
-
 // 8 E2M1 codes times the group scale -> 8 f16, exact (every E2M1 x UE4M3 product is an f16
 // value). The converts scale by 2^8 (their scale operand contributes its exponent only); the
 // UE4M3 byte shifted into the f16 exponent and mantissa fields reads as 2^-8 times its value,
@@ -189,9 +180,6 @@ __device__ __forceinline__ f16x8_t dequant8_f16(uint32_t c, uint32_t scale_byte)
 
 // Target builtins stay inside __device__ helpers: used directly in a kernel template they make
 // its host-side instantiation fail, and the launch stub goes missing.
-__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -217,7 +205,8 @@ __device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ (r & 7
 // One workgroup: N tile nt (512 weight rows) of M tile ti (gate/up: all of its up to 128 pairs;
 // down: the half hf of 64 pairs). DOWN = false: gate/up (A rows are 256 gate rows then the
 // matching up rows; K = H; B = x rows by token); DOWN = true: down (A rows are 512 rows of W_d;
-// K = F; B = h_hi and h_lo rows by CSR slot). N tiles may run past the matrix: rows beyond it
+// K = F; B = h_hi and h_lo rows by CSR slot, with their scale exponents per 256-feature
+// segment). N tiles may run past the matrix: rows beyond it
 // read the last row and are not stored.
 //
 // Each K step of 64 stages one NVFP4 block of every A row (three 12-byte direct-to-LDS loads per
@@ -233,7 +222,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const int32_t *__restrict__ n_tiles, int32_t max_tiles, int32_t n_ntiles,
     const uint8_t *__restrict__ w0, int64_t s0, const uint8_t *__restrict__ w1, int64_t s1,
     int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
-    uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, float *__restrict__ ypair) {
+    uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int32_t *__restrict__ hs,
+    float *__restrict__ ypair) {
     constexpr int kThreads = kGemmThreads;
     constexpr int kWaves = kThreads / 64;
     constexpr int kRows = kRowsW * kWaves;          // A rows per workgroup
@@ -248,6 +238,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     constexpr int kALoadsMax = (kAUnits + kThreads - 1) / kThreads;   // 3
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int rowid[kBM2];               // token (gate/up) or CSR slot (down) of each column
+    __shared__ int hsc[DOWN ? kBM2 : 1][DOWN ? kMaxSeg : 1];   // down: h scale exponents
 
     // M tile ti runs on XCD ti mod 8 (hardware workgroup b runs on XCD b mod 8), its N tiles (and
     // halves) in consecutive slots there: they share its token rows in that XCD's L2, and the
@@ -276,6 +267,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         const int c = r < mt ? r : 0;
         rowid[r] = DOWN ? q0 + c : pair_ids[q0 + c] / k;
     }
+    const int nseg = (F + kSegF - 1) / kSegF;   // h scale segments of a pair's row
+    if constexpr (DOWN)
+        for (int i = tid; i < kBM2 * nseg; i += kThreads) {
+            const int r = i / nseg, g = i - r * nseg;
+            hsc[r][g] = hs[(int64_t)(q0 + (r < mt ? r : 0)) * nseg + g];
+        }
     lds_barrier();
 
     // A: load i of a wave covers units (i*kWaves + wave)*64 + lane (unit j = u % 3 of row
@@ -324,9 +321,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     };
     const int ops = a_loads + kNB * kBUnits;   // loads per step of this wave
 
-    // operand type: gate/up multiplies f16 (x cast per token by xcast_kernel, weights decoded to
-    // f16), down bf16 (h as bf16 hi + lo)
-    using BT = std::conditional_t<DOWN, bf16x8_t, f16x8_t>;
+    // operands are f16: weights decoded to f16; x cast per token by xcast_kernel (gate/up), h as
+    // f16 hi + lo scaled per (pair, 256-feature segment) by the gate/up epilogue (down)
+    using BT = f16x8_t;
     constexpr int kAT0 = kRowsW / 16;
     f32x4_t acc[kAT0][kCols];
 #pragma unroll
@@ -350,6 +347,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const int nsteps = nblk;
     for (int kb = 0; kb < min(kStages - 1, nsteps); kb++) issue(kb);
     for (int kb = 0; kb < nsteps; kb++) {
+        if constexpr (DOWN) {
+            // a new h segment (its own scale exponent per column): rescale the running sums to
+            // it, exactly (powers of two)
+            const int g = kb / (kSegF / kBlockWeights);
+            if (g > 0 && kb == g * (kSegF / kBlockWeights)) {
+#pragma unroll
+                for (int c = 0; c < kCols; c++) {
+                    const int d = hsc[16 * c + n][g - 1] - hsc[16 * c + n][g];
+#pragma unroll
+                    for (int f = 0; f < kAT0; f++)
+#pragma unroll
+                        for (int v = 0; v < 4; v++) acc[f][c][v] = ldexpf(acc[f][c][v], d);
+                }
+            }
+        }
         vm_wait_le(min(kStages - 2, nsteps - 1 - kb) * ops);   // step kb landed
         lds_barrier();   // visible to all; the stage of step kb-1 is free
         if (kb + kStages - 1 < nsteps) issue(kb + kStages - 1);
@@ -379,18 +391,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
                 // 16q + 8 s2 .. +7
 #pragma unroll
                 for (int f = 0; f < kAT; f++) {
-                    if constexpr (DOWN) {
-                        const bf16x8_t af = dequant8_bf16(cw[f][s2], ue4m3_to_f32(sb[f]));
+                    const f16x8_t af = dequant8_f16(cw[f][s2], sb[f]);
 #pragma unroll
-                        for (int o = 0; o < kNB; o++)
+                    for (int o = 0; o < kNB; o++)
 #pragma unroll
-                            for (int c = 0; c < kC; c++)
-                                acc[f][c] = mfma_bf16(af, bfr[o][c], acc[f][c]);
-                    } else {
-                        const f16x8_t af = dequant8_f16(cw[f][s2], sb[f]);
-#pragma unroll
-                        for (int c = 0; c < kC; c++) acc[f][c] = mfma_f16(af, bfr[0][c], acc[f][c]);
-                    }
+                        for (int c = 0; c < kC; c++) acc[f][c] = mfma_f16(af, bfr[o][c], acc[f][c]);
                 }
             }
         };
@@ -407,38 +412,72 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
             const int col = 16 * c + n;
             if (col < mt) {
                 const int64_t prow = (int64_t)pair_ids[q0 + col] * H;
+                const int sl = hsc[col][nseg - 1];   // the last segment's scale exponent
 #pragma unroll
                 for (int f = 0; f < kAT; f++) {
                     const int r = nt * kRows + arow[f] + 4 * q;
-                    if (r < H) *reinterpret_cast<f32x4_t *>(ypair + prow + r) = acc[f][c];
+                    const f32x4_t y4 = {ldexpf(acc[f][c][0], sl), ldexpf(acc[f][c][1], sl),
+                                        ldexpf(acc[f][c][2], sl), ldexpf(acc[f][c][3], sl)};
+                    if (r < H) *reinterpret_cast<f32x4_t *>(ypair + prow + r) = y4;
                 }
             }
         }
     } else {
+        // h = SiLU(g) * u for this lane's 2 x 4 features of each token column (features past ff
+        // count as 0), then one power-of-two scale per (pair, this tile's 256 features): the
+        // largest |h| over the tile into [2^14, 2^15), so h = 2^s (hi + lo) with hi and lo f16
+        // (about 22 significant bits)
+        // (h is formed twice, for the maxima and for the stores, rather than held in registers
+        // over the workgroup's exchange of maxima)
+        auto hval = [&](int t, int c, int v, int sc) {
+            const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q + v;
+            const float g = ldexpf(acc[t][c][v], sc), u = ldexpf(acc[2 + t][c][v], sc);
+            return o < F ? silu(g) * u : 0.f;
+        };
+        float *cmax = reinterpret_cast<float *>(smem);   // [kWaves][kBM]: stages are done
+        lds_barrier();   // every wave is past its last read of the stages
 #pragma unroll
-        for (int t = 0; t < 2; t++) {   // gate tile t and the matching up tile 2 + t
-            const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q;   // o..o+3
-            if (o >= F) continue;
+        for (int c = 0; c < kCols; c++) {
+            const int sc = xs[rowid[16 * c + n]];   // the token row's f16 scale exponent
+            float m = 0.f;
 #pragma unroll
-            for (int c = 0; c < kCols; c++) {
-                const int col = 16 * c + n;
-                if (col < mt) {
-                    const int sc = xs[rowid[col]];   // the token row's f16 scale exponent
-                    uint32_t hi2[2], lo2[2];
+            for (int t = 0; t < 2; t++)
 #pragma unroll
-                    for (int v = 0; v < 4; v += 2) {
-                        const float g0 = ldexpf(acc[t][c][v], sc), u0 = ldexpf(acc[2 + t][c][v], sc);
-                        const float g1 = ldexpf(acc[t][c][v + 1], sc);
-                        const float u1 = ldexpf(acc[2 + t][c][v + 1], sc);
-                        const float h0 = silu(g0) * u0, h1 = silu(g1) * u1;
-                        const __bf16 b0 = (__bf16)h0, b1 = (__bf16)h1;
-                        hi2[v / 2] = pack_bf16((float)b0, (float)b1);
-                        lo2[v / 2] = pack_bf16(h0 - (float)b0, h1 - (float)b1);
-                    }
-                    const int64_t off = (int64_t)(q0 + col) * F + o;
-                    *reinterpret_cast<i32x2_t *>(h_hi + off) = i32x2_t{(int)hi2[0], (int)hi2[1]};
-                    *reinterpret_cast<i32x2_t *>(h_lo + off) = i32x2_t{(int)lo2[0], (int)lo2[1]};
+                for (int v = 0; v < 4; v++) m = fmaxf(m, fabsf(hval(t, c, v, sc)));
+            m = fmaxf(m, __shfl_xor(m, 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            if (q == 0) cmax[wave * kBM + 16 * c + n] = m;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int c = 0; c < kCols; c++) {
+            const int col = 16 * c + n;
+            float m = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) m = fmaxf(m, cmax[w * kBM + col]);
+            int e = 0;
+            if (m > 0.f) (void)frexpf(m, &e);   // m = f * 2^e, f in [0.5, 1)
+            const int sh = m > 0.f ? e - 15 : 0;
+            if (col >= mt) continue;
+            if (wave == 0 && q == 0) hs[(int64_t)(q0 + col) * nseg + nt] = sh;
+            const int sc = xs[rowid[col]];
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q;
+                if (o >= F) continue;
+                uint32_t hi2[2], lo2[2];
+#pragma unroll
+                for (int v = 0; v < 4; v += 2) {
+                    const float h0 = ldexpf(hval(t, c, v, sc), -sh);
+                    const float h1 = ldexpf(hval(t, c, v + 1, sc), -sh);
+                    const _Float16 a0 = (_Float16)h0, a1 = (_Float16)h1;
+                    hi2[v / 2] = __builtin_bit_cast(uint32_t, f16x2_t{a0, a1});
+                    lo2[v / 2] = __builtin_bit_cast(
+                        uint32_t, f16x2_t{(_Float16)(h0 - (float)a0), (_Float16)(h1 - (float)a1)});
                 }
+                const int64_t off = (int64_t)(q0 + col) * F + o;
+                *reinterpret_cast<i32x2_t *>(h_hi + off) = i32x2_t{(int)hi2[0], (int)hi2[1]};
+                *reinterpret_cast<i32x2_t *>(h_lo + off) = i32x2_t{(int)lo2[0], (int)lo2[1]};
             }
         }
     }
@@ -451,12 +490,14 @@ struct PrefillWs {
     i32x2_t *tiles;
     int32_t *n_tiles;
     uint16_t *h_hi, *h_lo;
+    int32_t *hs;     // [P][segments] h scale exponents
     float *ypair;
     uint16_t *x16;   // [T][H] x as scaled f16 (in the ypair region: dead before down writes it)
     int32_t *xs;     // [T] its scale exponents
 };
 
 int max_tiles(int32_t P, int32_t E) { return P / kBM + std::min(E, P) + 1; }
+int h_segments(int32_t F) { return (F + kSegF - 1) / kSegF; }
 
 PrefillWs carve(void *ws, int32_t T, int32_t P, int32_t E, int32_t H, int32_t F) {
     uint8_t *b = static_cast<uint8_t *>(ws);
@@ -471,6 +512,8 @@ PrefillWs carve(void *ws, int32_t T, int32_t P, int32_t E, int32_t H, int32_t F)
     b += align256(2 * (size_t)P * F);
     w.h_lo = reinterpret_cast<uint16_t *>(b);
     b += align256(2 * (size_t)P * F);
+    w.hs = reinterpret_cast<int32_t *>(b);
+    b += align256(sizeof(int32_t) * (size_t)P * h_segments(F));
     w.ypair = reinterpret_cast<float *>(b);
     w.x16 = reinterpret_cast<uint16_t *>(b);   // 2 T H bytes <= 4 P H: P = T k >= T
     w.xs = reinterpret_cast<int32_t *>(b + align256(2 * (size_t)T * H));
@@ -498,13 +541,13 @@ int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
         hipLaunchKernelGGL((gemm_kernel<true>), dim3(grid), dim3(kGemmThreads), lds, s, nullptr,
                            w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt, n_ntiles,
                            a.down.base, a.down.expert_stride, nullptr, (int64_t)0, a.k, a.F, a.F,
-                           a.H, nullptr, nullptr, nullptr, w.ypair);
+                           a.H, nullptr, nullptr, nullptr, w.hs, w.ypair);
     else
         hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kGemmThreads), lds, s,
                            (const uint16_t *)w.x16, nullptr, nullptr, a.offsets, a.pair_ids,
                            w.tiles, w.n_tiles, mt, n_ntiles, a.gate.base, a.gate.expert_stride,
                            a.up.base, a.up.expert_stride, a.k, a.H, a.F, a.H,
-                           (const int32_t *)w.xs, w.h_hi, w.h_lo, nullptr);
+                           (const int32_t *)w.xs, w.h_hi, w.h_lo, w.hs, nullptr);
     prof_stop(id, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
@@ -514,11 +557,14 @@ int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
 size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
     const int32_t P = T * k;
     return align256(sizeof(int32_t) * (size_t)P) + align256(sizeof(i32x2_t) * (size_t)max_tiles(P, E)) +
-           256 + 2 * align256(2 * (size_t)P * F) + align256(sizeof(float) * (size_t)P * H);
+           256 + 2 * align256(2 * (size_t)P * F) +
+           align256(sizeof(int32_t) * (size_t)P * h_segments(F)) +
+           align256(sizeof(float) * (size_t)P * H);
 }
 
 int launch_prefill(const FfnArgs &a, hipStream_t s) {
     const int32_t P = a.T * a.k;
+    if (h_segments(a.F) > kMaxSeg) return MOE_ESHAPE;
     const PrefillWs w = carve(a.ws, a.T, P, a.E, a.H, a.F);
     const int mt = max_tiles(P, a.E);
     const int sched_blocks = std::max(1, std::min(256, (P + kThreadsSched - 1) / kThreadsSched));

@@ -80,6 +80,22 @@ def test_every_weight_value_is_exact_in_bf16(golden_dir):
     assert np.array_equal(got.reshape(-1), prod)
 
 
+def test_every_weight_value_is_exact_in_f16(golden_dir):
+    """All 16 x 127 products code * scale are float16 values too (normal ones: the smallest
+    nonzero, 2^-10, is above f16's 2^-14), so the f16-MFMA paths hold dequantized weights
+    without rounding. So is the scale alone at 2^-8 of its value (subnormal bytes included),
+    which is how the decode kernels form it from the byte's bits."""
+    tab = _e2m1_golden(golden_dir)
+    sc = _f8_e4m3fn(range(0x7F))
+    prod = np.outer(tab, sc).reshape(-1)
+    as_f16 = torch.tensor(prod).to(torch.float16).to(torch.float64).numpy()
+    assert np.array_equal(as_f16, prod)
+    assert np.abs(prod[prod != 0]).min() >= 2.0 ** -14
+    # byte << 7 read as f16 bits is 2^-8 times the UE4M3 value, for every byte 0x00..0x7E
+    bits = (np.arange(0x7F, dtype=np.uint16) << 7).astype(np.uint16)
+    assert np.array_equal(bits.view(np.float16).astype(np.float64) * 256.0, sc)
+
+
 def test_block_decode_against_independent_unpacking(golden_dir):
     """Random bytes with all 127 finite scale codes: the oracle's row decode must equal the
     numpy/torch unpacking of the same layout (scales in bytes 0..3, weight 2i in the low nibble
