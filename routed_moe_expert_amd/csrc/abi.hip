@@ -30,10 +30,8 @@ int check_common(int32_t T, int32_t k, int32_t E) {
 extern "C" {
 
 size_t moe_route_bucket_ws(int32_t T, int32_t k, int32_t E) {
-    (void)T;
-    (void)k;
-    (void)E;
-    return 0;  // the bucketing kernel works in LDS only
+    if (T < 0 || k < 1 || E < 1) return 0;
+    return bucket_ws_bytes(T, k, E);
 }
 
 int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t expert_base,
@@ -43,9 +41,9 @@ int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, i
     if (st != MOE_OK) return st;
     if (!offsets || !active || !counts) return MOE_EINVAL;
     if (T > 0 && (!topk_ids || !pair_ids)) return MOE_EINVAL;
-    if (ws_bytes < moe_route_bucket_ws(T, k, E)) return MOE_EWS;
-    (void)ws;
-    return launch_bucket(topk_ids, T, k, E, expert_base, offsets, pair_ids, active, counts,
+    const size_t need = moe_route_bucket_ws(T, k, E);
+    if (ws_bytes < need || (need && !ws)) return MOE_EWS;
+    return launch_bucket(topk_ids, T, k, E, expert_base, offsets, pair_ids, active, counts, ws,
                          reinterpret_cast<hipStream_t>(stream));
 }
 

@@ -156,9 +156,10 @@ inline void prof_stop(int id, hipStream_t s) {
 // ----------------------------------------------------------------------------- host launchers
 // Each returns a MOE_* status; arguments have been validated by the ABI layer.
 
+size_t bucket_ws_bytes(int32_t T, int32_t k, int32_t E);
 int launch_bucket(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t expert_base,
                   int32_t *offsets, int32_t *pair_ids, int32_t *active, int32_t *counts,
-                  hipStream_t s);
+                  void *ws, hipStream_t s);
 
 struct FfnArgs {
     const uint16_t *x;

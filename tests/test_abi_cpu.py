@@ -114,3 +114,17 @@ def test_one_hip_runtime_whatever_the_import_order():
                          timeout=300)
     assert out.returncode == 0, out.stderr
     assert out.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_bucket_workspace_only_past_one_workgroup():
+    """Up to 4096 pairs the bucketing runs in one workgroup's LDS; past that its chunked form
+    keeps per-chunk histograms in the workspace, and a short workspace is refused on the host."""
+    assert moe.moe_route_bucket_ws(512, 8, 288) == 0
+    big = moe.moe_route_bucket_ws(4096, 8, 288)
+    assert big > 0 and big % 256 == 0
+    assert big >= 16 * 289 * 4          # at least 16 chunks of 289 bucket counts
+    st = moe.lib.moe_route_bucket(FAKE, 4096, 8, 288, 0, FAKE, FAKE, FAKE, FAKE, FAKE, big - 256,
+                                  None)
+    assert st == moe.MOE_EWS
+    st = moe.lib.moe_route_bucket(FAKE, 4096, 8, 288, 0, FAKE, FAKE, FAKE, FAKE, None, big, None)
+    assert st == moe.MOE_EWS

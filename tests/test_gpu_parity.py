@@ -46,7 +46,9 @@ def _check_bucket(dc: DeviceCase):
 @pytest.mark.parametrize("T,k,E,base,frac", [
     (1, 10, 64, 0, 0.0), (6, 10, 512, 0, 0.0), (7, 3, 5, 0, 0.0), (50, 4, 16, 100, 0.3),
     (9, 2, 1, 0, 0.0), (200, 8, 288, 0, 0.5), (1000, 8, 2048, 0, 0.1), (3, 4, 7, 0, 1.0),
-    (0, 4, 8, 0, 0.0), (513, 2, 3, 0, 0.0)])
+    (0, 4, 8, 0, 0.0), (513, 2, 3, 0, 0.0),
+    # around and past the single-workgroup limit (4096 pairs): chunked histogram/scan/scatter
+    (512, 8, 64, 0, 0.0), (4097, 1, 7, 3, 0.2), (4096, 8, 288, 0, 0.0), (3000, 6, 2048, 0, 0.3)])
 def test_bucket_random(T, k, E, base, frac):
     _print_case("bucket_random", T=T, k=k, E=E, base=base, frac=frac)
     case = gen.make_random_case(T * 7 + k + E, T, k, E, 256, 64, nonlocal_frac=frac,
