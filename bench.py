@@ -40,8 +40,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "f7100fd97014434a0fc6c54137c3199149d398793dfb48e2b479c99621e17798",
-        "fetch_kib": 54327.1, "write_kib": 168.8,
+        "sha256": "fa96d6529b0de3e58811149867b81f84bf7e55d9a84721d2461cbdf0cadb7f84",
+        "fetch_kib": 54327.1, "write_kib": 169.1,
     },
 }
 
