@@ -305,10 +305,28 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
     int32_t *s_act = scratch, *s_off = scratch + E, *s_pair = scratch + 2 * E + 1;
     const bool pairs_in_lds = P <= kPairCap;
     if (tid == 0) meta.n_active = counts[0];
-    for (int j = tid; j < E; j += kThreads) s_act[j] = active[j];
-    for (int j = tid; j <= E; j += kThreads) s_off[j] = offsets[j];
-    if (pairs_in_lds)
-        for (int j = tid; j < P; j += kThreads) s_pair[j] = pair_ids[j];
+    // scratch[j] for j < total is entry j of active ++ offsets ++ pair_ids; each thread issues
+    // all of its loads of a batch before storing any, so the batch costs one memory round trip
+    constexpr int kBatch = 8;
+    const int total = 2 * E + 1 + (pairs_in_lds ? P : 0);
+    for (int base = 0; base < total; base += kBatch * kThreads) {
+        int32_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const int j = base + u * kThreads + tid;
+            // a pointer select and one unconditional load (past the end: counts, always valid)
+            const int32_t *src = j < E       ? active + j
+                                 : j <= 2 * E ? offsets + (j - E)
+                                 : j < total  ? pair_ids + (j - 2 * E - 1)
+                                              : counts;
+            v[u] = *src;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const int j = base + u * kThreads + tid;
+            if (j < total) scratch[j] = v[u];
+        }
+    }
     lds_barrier();
     item_range(meta.n_active, tiles, i0, i1);
     a_first = i0 / tiles;
