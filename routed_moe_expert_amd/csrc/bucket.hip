@@ -81,41 +81,47 @@ __device__ void zero_scatter_lds(ScatterLds sl, int NB) {
     for (int i = threadIdx.x; i < kWaves * NB / 4; i += kThreads) wcnt32[i] = 0;
 }
 
-// Stable scatter of pairs [p0, p1): cur[key] holds the next free CSR position of each key and is
-// advanced past the range's pairs.
-__device__ void scatter_range(const int32_t *__restrict__ ids, int p0, int p1, int E,
-                              int expert_base, int32_t *cur, ScatterLds sl,
-                              int32_t *__restrict__ pair_ids) {
+// One step of the stable scatter: the workgroup's 512 consecutive pairs, thread t holding pair
+// p = (first pair) + t with bucket key (-1: no pair). cur[key] holds the next free CSR position of
+// each key and is advanced past the step's pairs.
+__device__ void scatter_step(int key, int p, int E, int32_t *cur, ScatterLds sl,
+                             int32_t *__restrict__ pair_ids) {
     const int NB = E + 1, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     uint32_t *my_tbl = sl.tbl + 2 * wave * NB;
+    if (key >= 0) atomicOr(&my_tbl[2 * key + (lane >> 5)], 1u << (lane & 31));
+    // the wave's own LDS operations complete in order; wait for them before reading back
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    int rank = 0, gsize = 0;
+    if (key >= 0) {
+        const uint64_t m = (uint64_t)my_tbl[2 * key] | ((uint64_t)my_tbl[2 * key + 1] << 32);
+        rank = __popcll(m & lanes_below);
+        gsize = __popcll(m);
+    }
+    if (key >= 0 && rank == 0) sl.wcnt[wave * NB + key] = (uint8_t)gsize;
+    lds_barrier();
+    if (key >= 0) {
+        int pos = cur[key] + rank;
+        for (int w2 = 0; w2 < wave; w2++) pos += sl.wcnt[w2 * NB + key];
+        pair_ids[pos] = p;
+    }
+    lds_barrier();
+    if (key >= 0 && rank == 0) {
+        atomicAdd(&cur[key], gsize);
+        sl.wcnt[wave * NB + key] = 0;
+        my_tbl[2 * key] = 0;
+        my_tbl[2 * key + 1] = 0;
+    }
+    lds_barrier();
+}
+
+// Stable scatter of pairs [p0, p1) (cur[] as in scatter_step).
+__device__ void scatter_range(const int32_t *__restrict__ ids, int p0, int p1, int E,
+                              int expert_base, int32_t *cur, ScatterLds sl,
+                              int32_t *__restrict__ pair_ids) {
     for (int c0 = p0; c0 < p1; c0 += kThreads) {
-        const int p = c0 + tid;
-        const int key = p < p1 ? key_of(ids, p, E, expert_base) : -1;
-        if (key >= 0) atomicOr(&my_tbl[2 * key + (lane >> 5)], 1u << (lane & 31));
-        // the wave's own LDS operations complete in order; wait for them before reading back
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        int rank = 0, gsize = 0;
-        if (key >= 0) {
-            const uint64_t m = (uint64_t)my_tbl[2 * key] | ((uint64_t)my_tbl[2 * key + 1] << 32);
-            rank = __popcll(m & lanes_below);
-            gsize = __popcll(m);
-        }
-        if (key >= 0 && rank == 0) sl.wcnt[wave * NB + key] = (uint8_t)gsize;
-        lds_barrier();
-        if (key >= 0) {
-            int pos = cur[key] + rank;
-            for (int w2 = 0; w2 < wave; w2++) pos += sl.wcnt[w2 * NB + key];
-            pair_ids[pos] = p;
-        }
-        lds_barrier();
-        if (key >= 0 && rank == 0) {
-            atomicAdd(&cur[key], gsize);
-            sl.wcnt[wave * NB + key] = 0;
-            my_tbl[2 * key] = 0;
-            my_tbl[2 * key + 1] = 0;
-        }
-        lds_barrier();
+        const int p = c0 + threadIdx.x;
+        scatter_step(p < p1 ? key_of(ids, p, E, expert_base) : -1, p, E, cur, sl, pair_ids);
     }
 }
 
@@ -173,13 +179,31 @@ __global__ __launch_bounds__(kThreads) void bucket_kernel(
     ScatterLds sl;
     carve(E, cnt, wsum, sl);
     const int NB = E + 1;
+    // thread t holds the keys of pairs u * 512 + t, all loaded before any is used (one memory
+    // round trip; past P the load reads offsets[0], always valid, and the key is -1)
+    constexpr int kKeys = kSingleMax / kThreads;
+    int key[kKeys];
+#pragma unroll
+    for (int u = 0; u < kKeys; u++) {
+        const int p = u * kThreads + threadIdx.x;
+        key[u] = *(p < P ? ids + p : offsets);
+    }
+#pragma unroll
+    for (int u = 0; u < kKeys; u++) {
+        const int64_t e = (int64_t)key[u] - expert_base;
+        key[u] = u * kThreads + (int)threadIdx.x < P ? ((e >= 0 && e < E) ? (int)e : E) : -1;
+    }
     for (int i = threadIdx.x; i < NB; i += kThreads) cnt[i] = 0;
     zero_scatter_lds(sl, NB);
     lds_barrier();
-    for (int p = threadIdx.x; p < P; p += kThreads) atomicAdd(&cnt[key_of(ids, p, E, expert_base)], 1);
+#pragma unroll
+    for (int u = 0; u < kKeys; u++)
+        if (key[u] >= 0) atomicAdd(&cnt[key[u]], 1);
     lds_barrier();
     write_csr_head(cnt, E, wsum, offsets, active, counts);
-    scatter_range(ids, 0, P, E, expert_base, cnt, sl, pair_ids);
+#pragma unroll
+    for (int u = 0; u < kKeys; u++)
+        if (u * kThreads < P) scatter_step(key[u], u * kThreads + threadIdx.x, E, cnt, sl, pair_ids);
 }
 
 // Chunked form, step 1: the histogram of chunk blockIdx.x into hist[chunk][NB].

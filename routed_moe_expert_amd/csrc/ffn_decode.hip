@@ -603,7 +603,7 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float *__restrict__ w, const int32_t *__restrict__ pos, const int32_t *__restrict__ offsets,
     int32_t E, const float *__restrict__ ypair, int32_t k, int32_t H, float *__restrict__ y) {
-    constexpr int kJ = 8;  // slots whose loads are issued together
+    constexpr int kJ = 16;  // slots whose loads are issued together (one round trip for k <= 16)
     const int t = blockIdx.y;
     const int r = (blockIdx.x * kThreads + threadIdx.x) * 4;
     if (r >= H) return;
