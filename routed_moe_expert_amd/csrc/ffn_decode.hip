@@ -31,7 +31,7 @@
 //
 // Both FFN kernels are persistent: a grid of one or two 256-thread workgroups per CU splits the
 // (expert, tile) items into contiguous ranges, read from the device CSR (nothing is read back on
-// the host). Tiles stream through a ring of LDS buffers with direct-to-LDS loads (three per
+// the host). Tiles stream through a ring of LDS buffers with direct-to-LDS loads (two per
 // workgroup with two workgroups per CU, up to six with one). Each wave copies its share of a
 // tile into registers first thing, and the buffer is refilled as soon as every wave has done
 // so, so all buffers are in flight while a tile is computed.
@@ -696,14 +696,15 @@ int64_t max_experts(int64_t n_items, int64_t tiles, int grid) {
     return (per - 1) / tiles + 2;
 }
 
-// Two workgroups per CU with three tile buffers each when the LDS holds them, else one with as
-// many as fit (at most kMaxBuf). The ring region also holds the start-up scratch, so it is at
-// least that large. Returns the dynamic LDS bytes (0: does not fit).
+// Two workgroups per CU with two tile buffers each when the LDS holds them (both in flight while
+// a tile is computed from registers: measured as fast as three, the streaming rate being set
+// elsewhere), else one with as many as fit (at most kMaxBuf). The ring region also holds the
+// start-up scratch, so it is at least that large. Returns the dynamic LDS bytes (0: does not fit).
 size_t ring_plan(size_t tile, size_t scratch, int &nbuf, int &ring_bytes, int &wgs) {
     const size_t fixed = kRedBytes + sizeof(Meta);
     const size_t scr = (scratch + 15) & ~size_t(15);
-    if (2 * (std::max(3 * tile, scr) + fixed) <= kLds) {
-        nbuf = 3;
+    if (2 * (std::max(2 * tile, scr) + fixed) <= kLds) {
+        nbuf = 2;
         wgs = 2;
     } else {
         if (kLds < fixed + 2 * tile) return 0;
