@@ -29,9 +29,12 @@
 // lane group q the weights 16q + 8s .. 16q + 8s + 7 of the block: one scale group per lane and
 // two steps per block.
 //
-// Both FFN kernels are persistent: a grid of one or two 256-thread workgroups per CU splits the
-// (expert, tile) items into contiguous ranges, read from the device CSR (nothing is read back on
-// the host). Tiles stream through a ring of LDS buffers with direct-to-LDS loads (two per
+// Both FFN kernels are persistent: a grid of one or two 256-thread workgroups per CU, read from
+// the device CSR (nothing is read back on the host). The (expert, tile) items are dealt out in
+// contiguous ranges over per-CU slots: each expert's tiles over a group of slots of its own where
+// there are no more active experts than slots and that costs at most one item over an even cut,
+// else an even cut of the item list; the two workgroups sharing a CU split their slot's range unevenly, since the
+// first dispatched runs ahead. Tiles stream through a ring of LDS buffers with direct-to-LDS loads (two per
 // workgroup with two workgroups per CU, up to six with one). Each wave copies its share of a
 // tile into registers first thing, and the buffer is refilled as soon as every wave has done
 // so, so all buffers are in flight while a tile is computed.

@@ -8,76 +8,24 @@
 
 namespace moe {
 
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 constexpr int kBlockWeights = 64;  // NVFP4: weights per block
 constexpr int kBlockBytes = 36;    // NVFP4: 4 UE4M3 scale bytes + 32 code bytes
-constexpr int kGroup = 16;         // weights per UE4M3 scale
 
 inline int64_t row_bytes(int64_t in_f) { return in_f / kBlockWeights * kBlockBytes; }
-
-// UE4M3 scale byte -> fp32, exact for all 127 finite codes. Shifting the 7 value bits into the
-// fp32 exponent/mantissa position gives value * 2^-120 for normal codes and, as an fp32 denormal,
-// m * 2^-129 for subnormal codes; a multiply by 2^120 (denormals are preserved) restores both.
-__device__ __forceinline__ float ue4m3_to_f32(uint32_t byte) {
-    return __uint_as_float(byte << 20) * 0x1p120f;
-}
-
-// Two E2M1 codes of byte `sel` of `w` -> two bf16 (low nibble first), exact. The gfx950 scaled
-// conversion applies only the exponent of its scale operand, so the scale is 1.0 here and the
-// UE4M3 group scale is applied by the caller.
-template <int sel>
-__device__ __forceinline__ bf16x2_t e2m1x2_to_bf16(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, sel);
-}
-template <int sel>
-__device__ __forceinline__ f32x2_t e2m1x2_to_f32(uint32_t w) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, sel);
-}
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    bf16x2_t va = __builtin_bit_cast(bf16x2_t, a);
-    bf16x2_t vb = __builtin_bit_cast(bf16x2_t, b);
-    return __builtin_amdgcn_fdot2_f32_bf16(va, vb, c, false);
-}
 
 // SiLU(z) = z * sigmoid(z), with the hardware reciprocal (about 1 ulp) in place of a division.
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// DPP lane moves (VALU, no LDS round trip). CTRL is the dpp_ctrl encoding: 0xB1 / 0x4E swap
-// lanes 1-apart / 2-apart inside each quad, 0x141 mirrors each 8-lane half row, 0x140 mirrors
-// each 16-lane row, 0x142 broadcasts lane 15 of a row into the next row (rows in ROW_MASK).
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
-                                                                 CTRL, ROW_MASK, 0xf, false));
-}
-// Sum over each aligned group of 8 lanes; every lane of the group receives the sum.
-__device__ __forceinline__ float sum8_dpp(float v) {
-    v += dpp_mov<0xB1>(v);
-    v += dpp_mov<0x4E>(v);
-    v += dpp_mov<0x141>(v);
-    return v;
-}
-// Sum over each 32-lane half wave; lanes 16..31 and 48..63 receive their half's sum.
-__device__ __forceinline__ float sum32_dpp(float v) {
-    v = sum8_dpp(v);
-    v += dpp_mov<0x140>(v);          // 16-lane rows
-    v += dpp_mov<0x142, 0xA>(v);     // row 0 into row 1, row 2 into row 3
-    return v;
-}
-
 // Asynchronous copy of `bytes` (a multiple of 16) from 16-byte aligned global memory into
 // 16-byte aligned LDS with the gfx950 direct-to-LDS load (global_load_lds_dwordx4): wave w moves
 // 64 consecutive 16-byte units per instruction, lane i landing at the wave's LDS base + 16*i, so
 // no VGPRs are used and every load of the workgroup is in flight at once. Completion is awaited
-// with lds_dma_wait() followed by a workgroup barrier.
+// with vm_wait_le() followed by a workgroup barrier.
 template <int kThreads>
 __device__ __forceinline__ void stage_async(void *lds, const void *g, int bytes) {
     // the wave index is uniform: as a scalar, each instruction's LDS base is set up in SGPRs
@@ -93,14 +41,12 @@ __device__ __forceinline__ void stage_async(void *lds, const void *g, int bytes)
     }
 }
 
-__device__ __forceinline__ void lds_dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
 // Workgroup barrier that orders LDS only: it waits for this wave's LDS (and scalar) operations
 // and synchronizes the workgroup, but leaves global loads in flight. __syncthreads() carries a
 // fence over global memory, for which the compiler waits for every outstanding vector-memory
 // operation, and that would drain the prefetched tiles at each barrier. Kernels using this share
 // data between waves through LDS only; data landed by direct-to-LDS loads is awaited first with
-// vm_wait_le / lds_dma_wait by every issuing wave.
+// vm_wait_le by every issuing wave.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
