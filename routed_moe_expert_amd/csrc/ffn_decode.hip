@@ -135,17 +135,32 @@ __device__ __forceinline__ int pick_scale(float mx) {
 
 // B operands of one token column for a K slice of NB blocks starting at blk0: lane (n, q) holds
 // x[64 b + 16 q .. +15] of its token for every block b of the slice, as f16 scaled by 2^-s with
-// s chosen per (token, slice); returns s. Absent tokens (row == nullptr) and blocks past the row
-// give zeros. The raw bf16 words are converted in place (same register footprint).
+// s chosen per (token, slice); returns s. Absent token columns (row == nullptr) and blocks past
+// the row give zeros. fetch_x_operands issues the loads, all under one branch (so they issue
+// back to back), and convert_x_operands, once they have landed, zeroes the blocks past the row,
+// scales and converts in place (same register footprint).
 template <int NB>
-__device__ __forceinline__ int load_x_operands(u32x4_t (&xb)[NB][2], const uint16_t *row, int blk0,
-                                               int nblk, int q) {
+__device__ __forceinline__ void fetch_x_operands(u32x4_t (&xb)[NB][2], const uint16_t *row,
+                                                 int blk0, int nblk, int q) {
+#pragma unroll
+    for (int j = 0; j < NB; j++) xb[j][0] = xb[j][1] = u32x4_t{0, 0, 0, 0};
+    if (row != nullptr) {
+#pragma unroll
+        for (int j = 0; j < NB; j++) {   // blocks past the row re-read the row's start
+            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+                blk0 + j < nblk ? row + 64 * (blk0 + j) + 16 * q : row);
+            xb[j][0] = src[0];
+            xb[j][1] = src[1];
+        }
+    }
+}
+template <int NB>
+__device__ __forceinline__ int convert_x_operands(u32x4_t (&xb)[NB][2], int blk0, int nblk) {
 #pragma unroll
     for (int j = 0; j < NB; j++) {
-        const bool in = row != nullptr && blk0 + j < nblk;
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(row + 64 * (blk0 + j) + 16 * q);
-        xb[j][0] = in ? src[0] : u32x4_t{0, 0, 0, 0};
-        xb[j][1] = in ? src[1] : u32x4_t{0, 0, 0, 0};
+        const bool in = blk0 + j < nblk;   // wave-uniform
+        xb[j][0] = in ? xb[j][0] : u32x4_t{0, 0, 0, 0};
+        xb[j][1] = in ? xb[j][1] : u32x4_t{0, 0, 0, 0};
     }
     uint32_t amax = 0;   // |x| as bf16 bits: ordered like the magnitudes for finite values
 #pragma unroll
@@ -174,38 +189,52 @@ __device__ __forceinline__ int load_x_operands(u32x4_t (&xb)[NB][2], const uint1
 // B operands of one h column (fp32, CSR row of a pair) for a K slice of ff: hi + lo f16 pairs,
 // scaled by 2^-s per (pair, slice); returns s. The fp32 words land in the hi/lo registers
 // (hi[j] = values 0..7 of block j, lo[j] = values 8..15) and are converted one block at a time.
+// Absent columns and blocks past the row give zeros, as for the token rows of x; the loads
+// (fetch_h_operands) and the conversion (convert_h_operands) are split the same way.
 template <int NB>
-__device__ __forceinline__ int load_h_operands(u32x4_t (&hi)[NB][2], u32x4_t (&lo)[NB][2],
-                                               const float *row, int blk0, int nblk, int q) {
+__device__ __forceinline__ void fetch_h_operands(u32x4_t (&hi)[NB][2], u32x4_t (&lo)[NB][2],
+                                                 const float *row, int blk0, int nblk, int q) {
 #pragma unroll
-    for (int j = 0; j < NB; j++) {
-        const bool in = row != nullptr && blk0 + j < nblk;
-        const u32x4_t *src = reinterpret_cast<const u32x4_t *>(row + 64 * (blk0 + j) + 16 * q);
-        hi[j][0] = in ? src[0] : u32x4_t{0, 0, 0, 0};
-        hi[j][1] = in ? src[1] : u32x4_t{0, 0, 0, 0};
-        lo[j][0] = in ? src[2] : u32x4_t{0, 0, 0, 0};
-        lo[j][1] = in ? src[3] : u32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < NB; j++)
+        hi[j][0] = hi[j][1] = lo[j][0] = lo[j][1] = u32x4_t{0, 0, 0, 0};
+    if (row != nullptr) {
+#pragma unroll
+        for (int j = 0; j < NB; j++) {   // blocks past the row re-read the row's start
+            const u32x4_t *src = reinterpret_cast<const u32x4_t *>(
+                blk0 + j < nblk ? row + 64 * (blk0 + j) + 16 * q : row);
+            hi[j][0] = src[0];
+            hi[j][1] = src[1];
+            lo[j][0] = src[2];
+            lo[j][1] = src[3];
+        }
     }
+}
+template <int NB>
+__device__ __forceinline__ int convert_h_operands(u32x4_t (&hi)[NB][2], u32x4_t (&lo)[NB][2],
+                                                  int blk0, int nblk) {
     float mx = 0.f;
 #pragma unroll
     for (int j = 0; j < NB; j++)
 #pragma unroll
         for (int h = 0; h < 2; h++)
 #pragma unroll
-            for (int i = 0; i < 4; i++)
-                mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(hi[j][h][i])),
-                                     fabsf(__uint_as_float(lo[j][h][i]))));
+            for (int i = 0; i < 4; i++) {
+                const float m = fmaxf(fabsf(__uint_as_float(hi[j][h][i])),
+                                      fabsf(__uint_as_float(lo[j][h][i])));
+                mx = blk0 + j < nblk ? fmaxf(mx, m) : mx;
+            }
     const int s = pick_scale(colmax(mx));
     const float inv = ldexpf(1.0f, -s);
 #pragma unroll
     for (int j = 0; j < NB; j++) {
+        const bool in = blk0 + j < nblk;   // wave-uniform
         float v[16];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            v[i] = __uint_as_float(hi[j][0][i]) * inv;
-            v[4 + i] = __uint_as_float(hi[j][1][i]) * inv;
-            v[8 + i] = __uint_as_float(lo[j][0][i]) * inv;
-            v[12 + i] = __uint_as_float(lo[j][1][i]) * inv;
+            v[i] = in ? __uint_as_float(hi[j][0][i]) * inv : 0.f;
+            v[4 + i] = in ? __uint_as_float(hi[j][1][i]) * inv : 0.f;
+            v[8 + i] = in ? __uint_as_float(lo[j][0][i]) * inv : 0.f;
+            v[12 + i] = in ? __uint_as_float(lo[j][1][i]) * inv : 0.f;
         }
 #pragma unroll
         for (int st = 0; st < 2; st++)      // K step st: values 8 st .. 8 st + 7
@@ -340,9 +369,20 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
         meta.e[tid] = e;
         meta.q0[tid] = q0;
         meta.m[tid] = m;
+        // an active expert has m >= 1: entries past m re-read entry m - 1 and are then zeroed
+        if (pairs_in_lds) {
 #pragma unroll
-        for (int j = 0; j < kCols; j++)
-            meta.pid[tid][j] = j < m ? (pairs_in_lds ? s_pair[q0 + j] : pair_ids[q0 + j]) : 0;
+            for (int j = 0; j < kCols; j++) {
+                const int v = s_pair[q0 + min(j, m - 1)];
+                meta.pid[tid][j] = j < m ? v : 0;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kCols; j++) {
+                const int v = pair_ids[q0 + min(j, m - 1)];
+                meta.pid[tid][j] = j < m ? v : 0;
+            }
+        }
     }
     lds_barrier();
 }
@@ -354,11 +394,12 @@ __device__ __forceinline__ int chunk_pid(const Meta &meta, const int32_t *pair_i
 }
 
 // Gate/up + SiLU * up over the union of active experts; the four waves split K = hidden. A unit
-// of work is one item (or, past 16 tokens of an expert, one token chunk of it). Each unit has a
-// single barrier: it publishes the previous unit's partial tiles (double-buffered) and hands back
-// the previous tile's buffer; one wave (rotating) then sums the previous unit while the others
-// go on. Tile i is awaited with "at most the tiles behind it outstanding": loads complete in
-// issue order, so that wait covers tile i.
+// of work is one item (or, past 16 tokens of an expert, one token chunk of it). A unit's first
+// barrier publishes tile i and the previous unit's partial tiles (double-buffered); once every
+// wave holds its slice of tile i in registers, a second barrier hands the buffer back to the
+// stream. One wave (rotating) then sums the previous unit's partials while the others contract.
+// Tile i is awaited with "at most the memory operations issued after it outstanding": vector
+// memory operations complete in issue order, so that wait covers tile i and nothing newer.
 template <int NB>
 __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
@@ -409,11 +450,13 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
                 dma16((o < 0 ? ut : gt) + (o & 0x7fffffff), dst + base * 16);
             }
         }
+        asm volatile("" ::: "memory");   // later stores stay behind these loads (ring waits)
         if (++it == tiles) { it = 0; ++ia; }
         if (++is == nbuf) is = 0;
     };
 
-    // reduction of a unit by one wave: lane -> (feature f, token column nn)
+    // reduction of a unit by one wave: lane -> (feature f, token column nn). One wave (rotating)
+    // takes it while the others go on, which measured faster than a quarter per wave.
     auto reduce = [&](const float *rp, int q0, int c, int t, int mt) {
         for (int o = lane; o < kGuO * mt; o += 64) {
             const int f = o & (kGuO - 1), nn = o / kGuO;
@@ -429,19 +472,20 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
 
     u32x4_t xb[NB][2];
     int xs = 0, cur_a = -1, cur_c = -1;
-    // the token rows of the first unit are loaded right after the first tile, before the rest of
-    // the ring: waiting for them then waits for one tile, not for every buffer in flight
-    auto load_x = [&](int a_, int c_) {
+    auto fetch_x = [&](int a_, int c_) {   // token rows of chunk c_ of expert a_
         const int mt = min(kCols, meta.m[a_] - c_ * kCols);
         const uint16_t *row = nullptr;
         if (n < mt) row = x + (int64_t)(chunk_pid(meta, pair_ids, a_, c_, n) / k) * H;
-        xs = load_x_operands<NB>(xb, row, blk0, nblk, q);
+        fetch_x_operands<NB>(xb, row, blk0, nblk, q);
         cur_a = a_;
         cur_c = c_;
     };
+    // the token rows of the first unit are loaded with the first tile, before the rest of the
+    // ring: waiting for them then waits for one tile, not for every buffer in flight
     if (i0 < i1) {
+        fetch_x(0, 0);
         issue_next();
-        load_x(0, 0);
+        xs = convert_x_operands<NB>(xb, blk0, nblk);
     }
     for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
 
@@ -452,8 +496,13 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
         const uint8_t *wt = wb + slot * tile_bytes + n * pitch;   // this lane's row of the tile
         for (int c = 0; c * kCols < m; c++, unit++) {
             const int mt = min(kCols, m - c * kCols);
-            if (a != cur_a || c != cur_c) load_x(a, c);   // token rows of this chunk
-            if (c == 0) vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst);   // tile i landed
+            if (a != cur_a || c != cur_c) {   // token rows of this chunk
+                fetch_x(a, c);
+                xs = convert_x_operands<NB>(xb, blk0, nblk);
+            }
+            // tile i landed: issued after it are at least the tiles behind it (the reducing
+            // wave's h stores are not counted: they only make its wait stricter)
+            if (c == 0) vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst);
             lds_barrier();   // tile i and the previous unit's partials visible to all
             SliceA<NB> sa;
             read_slice<NB>(wt, blk0, nblk, q, sa);
@@ -463,15 +512,17 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
             }
             if (unit > 0 && wave == (unit - 1) % kWaves)
                 reduce(red + ((unit - 1) & 1) * kRedFloats, p_q0, p_c, p_t, p_mt);
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            // two independent accumulation chains (K steps 0 and 1 of each block) halve the
+            // dependent MFMA latency
+            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
             for (int j = 0; j < NB; j++) {
                 const f16x2_t S = scale_f16x2(sa.s[j]);
-                acc = mfma16(dequant8(sa.c[j][0], S), __builtin_bit_cast(f16x8_t, xb[j][0]), acc);
-                acc = mfma16(dequant8(sa.c[j][1], S), __builtin_bit_cast(f16x8_t, xb[j][1]), acc);
+                acc0 = mfma16(dequant8(sa.c[j][0], S), __builtin_bit_cast(f16x8_t, xb[j][0]), acc0);
+                acc1 = mfma16(dequant8(sa.c[j][1], S), __builtin_bit_cast(f16x8_t, xb[j][1]), acc1);
             }
             *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats + (wave * kCols + n) * 16 +
-                                         4 * q) = unscale(acc, xs);
+                                         4 * q) = unscale(acc0 + acc1, xs);
             p_q0 = q0;
             p_c = c;
             p_t = t;
@@ -493,7 +544,8 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
 // Down projection over the union of active experts, same streaming scheme; an item is 16*RT
 // down rows, wave w takes row tile w % RT and K slice w / RT of ff. With one K slice (RT = 4,
 // ff up to 640) every wave owns whole rows and stores them from registers; otherwise the slices
-// are summed through LDS like gate/up, by all waves.
+// are summed through LDS like gate/up, a quarter of the outputs per wave. Either way every wave
+// issues at least one store per unit, which the ring waits count.
 template <int NB>
 __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
@@ -507,6 +559,7 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     uint8_t *wb = smem;                                                // [nbuf][rows]
     float *red = reinterpret_cast<float *>(smem + ring_bytes);         // [2][wave][col][16 rows]
     __shared__ Meta meta;
+    __shared__ int s_pid[2][kCols];   // pair ids of the token columns of the last two units
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;
@@ -524,73 +577,87 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
         const int e = meta.e[ia];
         stage_async<kThreads>(wb + is * tile_bytes,
                               down + e * down_stride + (int64_t)it * tile_bytes, tile_bytes);
+        asm volatile("" ::: "memory");   // later stores stay behind these loads (ring waits)
         if (++it == tiles) { it = 0; ++ia; }
         if (++is == nbuf) is = 0;
     };
-    // (row r of the item, token column nn) sums the KS slices of r's row tile
-    auto reduce = [&](const float *rp, int a, int c, int t, int mt) {
-        for (int u = tid; u < rows * mt; u += kThreads) {
-            const int r = u % rows, nn = u / rows;
+    // output u = (token column u / rows, row u % rows of the item) sums the KS slices of its row
+    // tile; wave w takes the quarter u in [w Q, (w + 1) Q), Q = rows mt / 4 >= 4
+    auto reduce = [&](const float *rp, const int *pids, int t, int mt) {
+        const int Q = rows * mt / kWaves;
+        for (int l = lane; l < Q; l += 64) {
+            const int u = wave * Q + l, r = u % rows, nn = u / rows;
             float v = 0.f;
             for (int s2 = 0; s2 < KS; s2++) v += rp[((s2 * RT + r / 16) * kCols + nn) * 16 + r % 16];
-            ypair[(int64_t)chunk_pid(meta, pair_ids, a, c, nn) * H + t * rows + r] = v;
+            ypair[(int64_t)pids[nn] * H + t * rows + r] = v;
         }
     };
 
     u32x4_t hh[NB][2], hl[NB][2];
     int hs = 0, cur_a = -1, cur_c = -1;
-    auto load_h = [&](int a_, int c_) {
+    int pid_n = 0;   // pair id of token column n of the current chunk (its ypair row)
+    const float *h_row = nullptr;
+    auto locate_h = [&](int a_, int c_) {   // h row and pair id of column n of chunk c_ of a_
         const int mt = min(kCols, meta.m[a_] - c_ * kCols);
-        const float *row = n < mt ? h + (int64_t)(meta.q0[a_] + c_ * kCols + n) * F : nullptr;
-        hs = load_h_operands<NB>(hh, hl, row, blk0, nblk, q);
+        h_row = n < mt ? h + (int64_t)(meta.q0[a_] + c_ * kCols + n) * F : nullptr;
+        pid_n = n < mt ? chunk_pid(meta, pair_ids, a_, c_, n) : 0;
         cur_a = a_;
         cur_c = c_;
     };
-    // the h rows of the first unit come right after the first tile, before the rest of the ring
+    // the h rows of the first unit are loaded with the first tile, before the rest of the ring
+    locate_h(0, 0);
+    fetch_h_operands<NB>(hh, hl, h_row, blk0, nblk, q);
     issue_next();
-    load_h(0, 0);
+    hs = convert_h_operands<NB>(hh, hl, blk0, nblk);
     for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
 
-    int unit = 0, p_a = 0, p_c = 0, p_t = 0, p_mt = 0;
+    int unit = 0, p_t = 0, p_mt = 0;
     int a = 0, t = i0 - a_first * tiles, slot = 0;
     for (int i = i0; i < i1; i++) {
         const int m = meta.m[a];
         const uint8_t *wt = wb + slot * tile_bytes + (rt * 16 + n) * rb;
         for (int c = 0; c * kCols < m; c++, unit++) {
             const int mt = min(kCols, m - c * kCols);
-            if (a != cur_a || c != cur_c) load_h(a, c);
-            if (c == 0) vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst);   // tile i landed
+            if (a != cur_a || c != cur_c) {
+                locate_h(a, c);
+                fetch_h_operands<NB>(hh, hl, h_row, blk0, nblk, q);
+                hs = convert_h_operands<NB>(hh, hl, blk0, nblk);
+            }
+            // tile i landed: issued after it are the tiles behind it and one store per wave and
+            // unit (from unit 1 on with KS > 1; a lower bound past one chunk or with two stores)
+            if (c == 0)
+                vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst +
+                           (KS == 1 ? min(nbuf, i - i0) : max(0, min(nbuf, i - i0 - 1))));
             lds_barrier();
+            if (KS > 1 && wave == 0 && lane < kCols) s_pid[unit & 1][lane] = pid_n;
             SliceA<NB> sa;
             read_slice<NB>(wt, blk0, nblk, q, sa);
             if ((c + 1) * kCols >= m && i + nbuf < i1) {
                 lds_barrier();   // tile i is in every wave's registers: refill its buffer
                 issue_next();
             }
-            if (KS > 1 && unit > 0) reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            if (KS > 1 && unit > 0)
+                reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt);
+            // hi and lo parts accumulate in two independent chains (half the dependent latency)
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acl = acc;
 #pragma unroll
             for (int j = 0; j < NB; j++) {
                 const f16x2_t S = scale_f16x2(sa.s[j]);
                 const f16x8_t a0 = dequant8(sa.c[j][0], S), a1 = dequant8(sa.c[j][1], S);
                 acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hh[j][0]), acc);
-                acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hl[j][0]), acc);
+                acl = mfma16(a0, __builtin_bit_cast(f16x8_t, hl[j][0]), acl);
                 acc = mfma16(a1, __builtin_bit_cast(f16x8_t, hh[j][1]), acc);
-                acc = mfma16(a1, __builtin_bit_cast(f16x8_t, hl[j][1]), acc);
+                acl = mfma16(a1, __builtin_bit_cast(f16x8_t, hl[j][1]), acl);
             }
-            acc = unscale(acc, hs);
+            acc = unscale(acc + acl, hs);
             if (KS == 1) {   // whole rows: lane holds rows 4q..4q+3 of token column n
-                if (n < mt) {
-                    const int p = chunk_pid(meta, pair_ids, a, c, n);
-                    *reinterpret_cast<f32x4_t *>(ypair + (int64_t)p * H + t * rows + rt * 16 +
+                if (n < mt)
+                    *reinterpret_cast<f32x4_t *>(ypair + (int64_t)pid_n * H + t * rows + rt * 16 +
                                                  4 * q) = acc;
-                }
             } else {
                 *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats +
                                              (wave * kCols + n) * 16 + 4 * q) = acc;
             }
-            p_a = a;
-            p_c = c;
             p_t = t;
             p_mt = mt;
         }
@@ -599,7 +666,7 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     }
     if (KS > 1) {
         lds_barrier();
-        reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
+        reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt);
     }
 }
 
