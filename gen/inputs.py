@@ -20,6 +20,7 @@ NVFP4_SCALES_PER_BLOCK = 4
 
 # stream ids: one per buffer kind, so adding a buffer never shifts another's values
 S_GATE, S_UP, S_DOWN, S_GATEUP, S_X, S_ROUTE, S_LOGITS, S_PERM = 1, 2, 3, 4, 5, 6, 7, 8
+S_RLOGITS = 9
 
 
 def rng_for(seed: int, stream: int, sub: int = 0) -> np.random.Generator:
@@ -86,6 +87,15 @@ def router_weights(seed: int, T: int, k: int) -> np.ndarray:
     p = np.exp(z)
     p /= p.sum(axis=1, keepdims=True)
     return p.astype(np.float32)
+
+
+def router_logits(seed: int, T: int, E: int, ties: bool = False) -> np.ndarray:
+    """float32 [T, E] N(0,1) router logits. ties=True rounds them to multiples of 1/4, so that
+    equal logits (and ties at the k-th place) are common."""
+    z = rng_for(seed, S_RLOGITS).standard_normal(size=(T, E), dtype=np.float32)
+    if ties:
+        z = np.round(z * 4.0).astype(np.float32) / np.float32(4.0)
+    return np.ascontiguousarray(z, dtype=np.float32)
 
 
 def route_distinct(seed: int, T: int, k: int, E: int) -> np.ndarray:

@@ -7,6 +7,7 @@ Functions follow the definitions cited in moe_oracle.c. Every function here is p
 CPU test against something other than itself (see tests/test_oracle_pins.py):
   e2m1 / ue4m3 / nvfp4 decode  - the OCP element tables and torch's float8_e4m3fn decoding;
   route_bucket                 - a stable sort of the pair list (Python's sorted) and invariants;
+  router_topk                  - numpy's stable sort and scipy's softmax, closed forms, ties;
   ffn_per_slot / ffn_union     - numpy float64 matmuls on independently decoded weights,
                                  closed-form special cases, invariances.
 """
@@ -64,6 +65,9 @@ def _load():
             _u16p, _f32p, _i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, _u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _u8p,
             ctypes.c_int64, _i64p, ctypes.c_int64, _f64p, ctypes.c_int32]
+        lib.orc_router_topk.restype = ctypes.c_int
+        lib.orc_router_topk.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        _i32p, _f64p]
         lib.orc_ffn_union.restype = ctypes.c_int
         lib.orc_ffn_union.argtypes = [
             _u16p, _f32p, _i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -113,6 +117,19 @@ def route_bucket(ids: np.ndarray, E: int, expert_base: int = 0):
         raise ValueError("orc_route_bucket rejected its arguments")
     n_local = int(offsets[E])
     return offsets, pair_ids[:n_local].copy(), active[:counts[0]].copy(), int(counts[0]), int(counts[1])
+
+
+def router_topk(logits: np.ndarray, k: int):
+    """(ids int32 [T, k], w float64 [T, k]) from fp32 logits [T, E]: the k largest logits of each
+    row in descending order (equal logits in ascending expert id), w the softmax over them."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    ids = np.zeros((T, k), dtype=np.int32)
+    w = np.zeros((T, k), dtype=np.float64)
+    rc = _load().orc_router_topk(_p(logits, _f32p), T, E, k, _p(ids, _i32p), _p(w, _f64p))
+    if rc:
+        raise ValueError("orc_router_topk rejected its arguments")
+    return ids, w
 
 
 def bank_views(case: dict):

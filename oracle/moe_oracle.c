@@ -282,3 +282,40 @@ out:
     free(offsets); free(pair_ids); free(active); free(D); free(has); free(Wg); free(Wu); free(Wd);
     return rc;
 }
+
+/*
+ * Router: top-k selection plus softmax weights, per token (the step that produces the routed
+ * pairs the rest of this file consumes). The pages name a router without spelling it out; the
+ * reading taken here is the plainest one consistent with their workloads (k distinct experts per
+ * token, weights a softmax over the selected experts' logits):
+ *  - slot j of token t holds the j-th largest logit of row t, with equal logits taken in
+ *    ascending expert id, and no expert taken twice;
+ *  - w[t,j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the k selected logits (l_0 the largest),
+ *    in fp64 from the fp32 logits.
+ * Selection compares the fp32 logits exactly (as doubles, which order them identically).
+ * Returns 0, or -1 on bad arguments (k < 1 or k > E).
+ */
+int orc_router_topk(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *ids, double *w)
+{
+    if (T < 0 || E < 1 || k < 1 || k > E) return -1;
+    unsigned char *taken = malloc((size_t)E);
+    if (!taken) return -1;
+    for (int64_t t = 0; t < T; t++) {
+        const float *l = logits + t * E;
+        memset(taken, 0, (size_t)E);
+        for (int32_t j = 0; j < k; j++) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; e++) {
+                if (taken[e]) continue;
+                if (best < 0 || (double)l[e] > (double)l[best]) best = e;   /* first max wins */
+            }
+            taken[best] = 1;
+            ids[t * k + j] = best;
+        }
+        double top = (double)l[ids[t * k]], sum = 0.0;
+        for (int32_t j = 0; j < k; j++) sum += exp((double)l[ids[t * k + j]] - top);
+        for (int32_t j = 0; j < k; j++) w[t * k + j] = exp((double)l[ids[t * k + j]] - top) / sum;
+    }
+    free(taken);
+    return 0;
+}

@@ -341,3 +341,58 @@ def test_h_is_silu_gate_times_up(golden_dir):
         g = _decode_independent(case["gate"][e], 128, tab) @ x[p // 2]
         u = _decode_independent(case["up"][e], 128, tab) @ x[p // 2]
         assert _rel(h[p], g * expit(g) * u) < 1e-12
+
+
+# ----------------------------------------------------------------------------- router top-k
+# The router reading (largest logits first, equal logits in ascending expert id, softmax over the
+# selected logits) is pinned to numpy's stable sort, scipy's softmax and closed forms.
+
+def _stable_topk(l, k):
+    """numpy: order by descending logit, ties by ascending index (lexsort keys: last is primary)."""
+    order = np.lexsort((np.arange(l.shape[-1]), -l.astype(np.float64)))
+    return order[:k]
+
+
+@pytest.mark.parametrize("T,E,k,ties", [(7, 64, 8, False), (5, 288, 8, True), (3, 512, 10, True),
+                                        (4, 70, 70, True), (6, 33, 1, True)])
+def test_router_topk_matches_stable_sort_and_softmax(T, E, k, ties):
+    from scipy.special import softmax
+    logits = gen.router_logits(40 + E, T, E, ties=ties)
+    ids, w = oracle.router_topk(logits, k)
+    for t in range(T):
+        ref = _stable_topk(logits[t], k)
+        assert np.array_equal(ids[t], ref)
+        assert np.allclose(w[t], softmax(logits[t, ref].astype(np.float64)), rtol=1e-14, atol=0)
+
+
+def test_router_topk_closed_forms():
+    # all logits equal: the first k experts, equal weights
+    ids, w = oracle.router_topk(np.zeros((2, 16), np.float32), 5)
+    assert np.array_equal(ids, np.tile(np.arange(5), (2, 1)))
+    assert np.all(w == 0.2)
+    # k = 1: weight exactly 1
+    ids, w = oracle.router_topk(np.array([[0.5, -1.0, 3.0, 3.0]], np.float32), 1)
+    assert ids[0, 0] == 2 and w[0, 0] == 1.0
+    # two selected: the weights are the logistic function of the logit gap
+    a, b = 1.25, -0.5
+    ids, w = oracle.router_topk(np.array([[b, -3.0, a, -2.0]], np.float32), 2)
+    assert list(ids[0]) == [2, 0]
+    assert abs(w[0, 0] - 1.0 / (1.0 + np.exp(b - a))) < 1e-15
+    assert abs(w[0, 1] - 1.0 / (1.0 + np.exp(a - b))) < 1e-15
+    # ties at the k-th place go to the lower expert id
+    ids, _ = oracle.router_topk(np.array([[1.0, 3.0, 3.0, 2.0, 2.0]], np.float32), 4)
+    assert list(ids[0]) == [1, 2, 3, 4]
+
+
+def test_router_topk_invariances():
+    logits = gen.router_logits(41, 6, 96, ties=True)   # multiples of 1/4: the shift is exact
+    ids, w = oracle.router_topk(logits, 8)
+    # a common shift of a row changes neither the selection nor the weights
+    ids2, w2 = oracle.router_topk(logits + np.float32(64.0), 8)
+    assert np.array_equal(ids, ids2) and np.allclose(w, w2, rtol=1e-12, atol=0)
+    # weights are positive, sum to one and do not increase along the slots
+    assert np.all(w > 0) and np.allclose(w.sum(axis=1), 1.0, rtol=1e-15, atol=1e-15)
+    assert np.all(np.diff(w, axis=1) <= 0)
+    # k = E lists every expert once
+    ids3, _ = oracle.router_topk(logits, 96)
+    assert np.array_equal(np.sort(ids3, axis=1), np.tile(np.arange(96), (6, 1)))
