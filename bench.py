@@ -79,7 +79,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="verify_chunk",
                     choices=["verify_chunk", "tiny_decode", "e256_plateau", "skewed_prefill",
-                             "full_prefill"])
+                             "full_prefill", "router"])
+    ap.add_argument("--E", type=int, default=288, help="experts (router workload)")
+    ap.add_argument("--k", type=int, default=8, help="top-k (router workload)")
     ap.add_argument("--T", type=int, default=None, help="tokens (workload default if unset)")
     ap.add_argument("--U", type=int, default=60, help="union size for verify_chunk")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
@@ -175,6 +177,9 @@ def main():
     import routed_moe_expert_amd as moe
 
     torch.cuda.set_device(0)
+    if args.workload == "router":
+        bench_router(args, torch, gen, moe)
+        return
     D = build_inputs(args, torch, gen, moe)
     E, H, F, k, T = D["E"], D["H"], D["F"], D["k"], D["T"]
     P = T * k
@@ -305,6 +310,108 @@ def main():
         "unique_expert_bytes": unique_bytes,
         "hbm_frac_unique": (unique_bytes / s / 1e9) / HBM_PEAK_GBS,
         "useful_tflops": useful_flops / s / 1e12,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def kernel_times_ms(moe, kid, K, step):
+    """Average of the library's HIP-event times of kernel `kid` over K more calls of step(i)."""
+    import torch
+    hip = _hip()
+    starts, stops = [], []
+    for _ in range(K):
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        hip.hipEventCreate(ctypes.byref(a))
+        hip.hipEventCreate(ctypes.byref(b))
+        starts.append(a.value)
+        stops.append(b.value)
+    torch.cuda.synchronize()
+    moe.moe_profile_kernel(kid, starts, stops)
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    n_rec = moe.moe_profile_count()
+    moe.moe_profile_kernel(moe.MOE_KERNEL_NONE, [], [])
+    kms = []
+    for i in range(n_rec):
+        f = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(starts[i]), ctypes.c_void_p(stops[i]))
+        kms.append(f.value)
+    for a, b in zip(starts, stops):
+        hip.hipEventDestroy(ctypes.c_void_p(a))
+        hip.hipEventDestroy(ctypes.c_void_p(b))
+    return (sum(kms) / len(kms) if kms else float("nan")), len(kms)
+
+
+def bench_router(args, torch, gen, moe):
+    """The router step alone (moe_router_topk): fp32 logits [T, E] -> top-k ids and softmax
+    weights. One step = one call over one logits batch; consecutive steps read different copies
+    so that more than 2 x 256 MB cycle through (the logits come from HBM, not the Infinity Cache,
+    where a batch is large enough for that to matter)."""
+    import numpy as np
+    import oracle
+
+    T, E, k = args.T or 4096, args.E, args.k
+    logits = gen.router_logits(11, T, E)
+    lb = T * E * 4
+    copies = max(1, min(128, math.ceil(512e6 / lb)))
+    dev = torch.device("cuda")
+    base = torch.from_numpy(logits).to(dev)
+    lg = [base.clone() for _ in range(copies)]
+    ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+    w = torch.empty(T, k, dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def step(i):
+        moe.moe_router_topk(lg[i % copies], T, E, k, ids, w, stream=sh)
+
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(K):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / K
+    k_ms, n_k = kernel_times_ms(moe, moe.MOE_KERNEL_ROUTER, K, step)
+    nbytes = lb + T * k * 8
+    s = ms_per_step * 1e-3
+    roof = {"bound": "hbm", "kernel": "router_topk_kernel", "achieved": nbytes / (k_ms * 1e-3) / 1e9,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "bytes_per_launch": nbytes,
+            "avg_launch_us": k_ms * 1e3, "launches": n_k, "traffic": None}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    cpu = None
+    if not args.no_cpu_baseline:
+        n = min(T, 4096)
+        t1 = time.perf_counter()
+        reps = 0
+        while True:
+            oracle.router_topk(logits[:n], k)
+            reps += 1
+            el = time.perf_counter() - t1
+            if el >= min(args.cpu_seconds, 10.0):
+                break
+        sec = el / reps * T / n
+        cpu = {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} of the {T} tokens per repetition, scaled to the batch",
+               "seconds_per_batch": sec, "reps": reps}
+    out = {
+        "metric": "router step µs + GB/s of logits read and ids/weights written",
+        "value": nbytes / s / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"router top-{k}: E={E} T={T}, N(0,1) fp32 logits", "E": E,
+                   "top_k": k, "T": T, "hbm": f"{copies} logits copies in rotation"},
+        "step_us": ms_per_step * 1e3,
         "roofline": roof,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,

@@ -10,7 +10,8 @@
  *   y_t = sum over local slots j, in ascending j, of topk_w[t*k+j] * d     (fp32, no atomics)
  *
  * Two calls make one layer: moe_route_bucket (expert-first CSR of the routed pairs) and then
- * moe_ffn_nvfp4 (the FFN over that CSR).
+ * moe_ffn_nvfp4 (the FFN over that CSR). moe_router_topk can produce the routed pairs and their
+ * weights from router logits first.
  *
  * Conventions for every entry point:
  *  - Pointers marked (device) are GPU device addresses; the library never allocates, frees,
@@ -65,6 +66,7 @@ enum {
 #define MOE_MAX_PAIRS (1 << 24)    /* T*k limit */
 #define MOE_MAX_HIDDEN 16384       /* H limit */
 #define MOE_MAX_FF 8192            /* F limit */
+#define MOE_MAX_ROUTER_K 64        /* k limit of moe_router_topk (one slot per wavefront lane) */
 
 /* One weight bank: expert e's rows start at base + e*expert_stride (bytes, device). */
 typedef struct {
@@ -139,6 +141,23 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
                   moe_stream_t stream);
 
 /*
+ * Router step (the step before moe_route_bucket; the pages route each token to k distinct experts
+ * with softmax router weights -- the Rocket post's E512 top-10, the moe_sk_repro.rs top-8 -- but
+ * leave the router itself unspecified; the reading implemented here is the plain one):
+ *   for each token t, slot j < k holds the expert with the j-th largest logit of row t, equal
+ *   logits taken in ascending expert id, no expert twice (a total order: the result is unique);
+ *   topk_w[t*k+j] = exp(l_j - l_0) / sum over the k selected of exp(l_i - l_0), in fp32.
+ * The outputs are the topk_ids / topk_w arrays moe_route_bucket and moe_ffn_nvfp4 take.
+ *   logits    (device) fp32 [T, E], row-major.
+ *   topk_ids  (device) int32 [T, k]; topk_w (device) fp32 [T, k].
+ * No workspace. T = 0 is a valid no-op. Logits must be finite (NaN or Inf: undefined outputs).
+ * Errors: MOE_EINVAL (null pointer with T > 0, T<0, E<1, k<1, k>E), MOE_ESHAPE (E >
+ * MOE_MAX_EXPERTS, k > MOE_MAX_ROUTER_K or T*k > MOE_MAX_PAIRS), MOE_ELAUNCH.
+ */
+int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
+                    float *topk_w, moe_stream_t stream);
+
+/*
  * Diagnostics: timing of one kernel of the layer with caller-created HIP events.
  * After this call, the next n_events launches of kernel `kernel_id` (a MOE_KERNEL_* value) are
  * bracketed by hipEventRecord(start_events[i]) / hipEventRecord(stop_events[i]) on the launch
@@ -154,7 +173,8 @@ enum {
     MOE_KERNEL_COMBINE = 4,      /* ordered router-weighted combine */
     MOE_KERNEL_SCHEDULE = 5,     /* prefill tile schedule */
     MOE_KERNEL_GU_PREFILL = 6,   /* prefill gate/up grouped GEMM */
-    MOE_KERNEL_DN_PREFILL = 7    /* prefill down grouped GEMM */
+    MOE_KERNEL_DN_PREFILL = 7,   /* prefill down grouped GEMM */
+    MOE_KERNEL_ROUTER = 8        /* moe_router_topk's kernel */
 };
 int moe_profile_kernel(int32_t kernel_id, void *const *start_events, void *const *stop_events,
                        int32_t n_events);

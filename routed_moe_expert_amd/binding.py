@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 MOE_OK, MOE_EINVAL, MOE_EWS, MOE_ESHAPE, MOE_ELAUNCH = 0, 1, 2, 3, 4
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 (MOE_KERNEL_NONE, MOE_KERNEL_BUCKET, MOE_KERNEL_GU_DECODE, MOE_KERNEL_DN_DECODE, MOE_KERNEL_COMBINE,
- MOE_KERNEL_SCHEDULE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_DN_PREFILL) = range(8)
+ MOE_KERNEL_SCHEDULE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_DN_PREFILL, MOE_KERNEL_ROUTER) = range(9)
 
 
 class MoeError(RuntimeError):
@@ -49,6 +49,8 @@ def _load():
     l.moe_ffn_nvfp4.restype = ctypes.c_int
     l.moe_ffn_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
                                 i32, i32, i32, i32, i32, vp, i32, vp, sz, vp]
+    l.moe_router_topk.restype = ctypes.c_int
+    l.moe_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     l.moe_profile_kernel.restype = ctypes.c_int
     l.moe_profile_kernel.argtypes = [i32, ctypes.POINTER(vp), ctypes.POINTER(vp), i32]
     l.moe_profile_count.restype = i32
@@ -117,6 +119,12 @@ def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, 
                            _ptr(counts), gate, up, down, T, k, E, H, F, _ptr(y), path, _ptr(ws),
                            ws_bytes, _stream(stream))
     return _check("moe_ffn_nvfp4", st, raise_on_error)
+
+
+def moe_router_topk(logits, T: int, E: int, k: int, topk_ids, topk_w, stream=None,
+                    raise_on_error: bool = True) -> int:
+    st = lib.moe_router_topk(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _stream(stream))
+    return _check("moe_router_topk", st, raise_on_error)
 
 
 def moe_profile_kernel(kernel_id: int, start_events, stop_events) -> int:

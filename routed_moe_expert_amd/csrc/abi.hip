@@ -77,9 +77,20 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
     return path == MOE_PATH_DECODE ? launch_decode(a, s) : launch_prefill(a, s);
 }
 
+int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
+                    float *topk_w, moe_stream_t stream) {
+    if (T < 0 || E < 1 || k < 1 || k > E) return MOE_EINVAL;
+    if (E > MOE_MAX_EXPERTS || k > MOE_MAX_ROUTER_K || (int64_t)T * k > MOE_MAX_PAIRS)
+        return MOE_ESHAPE;
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_w) return MOE_EINVAL;
+    return launch_router_topk(logits, T, E, k, topk_ids, topk_w,
+                              reinterpret_cast<hipStream_t>(stream));
+}
+
 int moe_profile_kernel(int32_t kernel_id, void *const *start_events, void *const *stop_events,
                        int32_t n_events) {
-    if (kernel_id < MOE_KERNEL_NONE || kernel_id > MOE_KERNEL_DN_PREFILL || n_events < 0)
+    if (kernel_id < MOE_KERNEL_NONE || kernel_id > MOE_KERNEL_ROUTER || n_events < 0)
         return MOE_EINVAL;
     if (kernel_id != MOE_KERNEL_NONE && n_events > 0 && (!start_events || !stop_events))
         return MOE_EINVAL;

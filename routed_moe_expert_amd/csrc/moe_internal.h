@@ -124,6 +124,9 @@ bool decode_supported(const FfnArgs &a);   // shape within the decode kernels' l
 int launch_decode(const FfnArgs &a, hipStream_t s);
 int launch_prefill(const FfnArgs &a, hipStream_t s);
 
+int launch_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids,
+                       float *w, hipStream_t s);
+
 // y[t] = sum_j w[t,j] * ypair[pos[t*k+j]] over local slots; pos[p] >= n_local means non-local.
 int launch_combine(const float *w, const int32_t *pos, const int32_t *offsets, int32_t E,
                    const float *ypair, int32_t T, int32_t k, int32_t H, float *y, hipStream_t s);

@@ -25,7 +25,7 @@ def _declared():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert {"moe_route_bucket", "moe_ffn_nvfp4", "moe_route_bucket_ws", "moe_ffn_nvfp4_ws",
-            "moe_status_str"} <= names
+            "moe_router_topk", "moe_status_str"} <= names
     for n in names:
         assert hasattr(moe.lib, n), n
 
@@ -128,3 +128,21 @@ def test_bucket_workspace_only_past_one_workgroup():
     assert st == moe.MOE_EWS
     st = moe.lib.moe_route_bucket(FAKE, 4096, 8, 288, 0, FAKE, FAKE, FAKE, FAKE, None, big, None)
     assert st == moe.MOE_EWS
+
+
+def _router(**over):
+    a = dict(logits=FAKE, T=4, E=64, k=8, ids=FAKE, w=FAKE)
+    a.update(over)
+    return moe.moe_router_topk(a["logits"], a["T"], a["E"], a["k"], a["ids"], a["w"], stream=0,
+                               raise_on_error=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(logits=0), moe.MOE_EINVAL), (dict(ids=0), moe.MOE_EINVAL), (dict(w=0), moe.MOE_EINVAL),
+    (dict(T=-1), moe.MOE_EINVAL), (dict(E=0), moe.MOE_EINVAL), (dict(k=0), moe.MOE_EINVAL),
+    (dict(k=65, E=64), moe.MOE_EINVAL), (dict(k=65, E=128), moe.MOE_ESHAPE),
+    (dict(E=4096), moe.MOE_ESHAPE), (dict(T=1 << 22, k=8), moe.MOE_ESHAPE),
+    (dict(T=0), moe.MOE_OK), (dict(T=0, logits=0, ids=0, w=0), moe.MOE_OK),
+])
+def test_router_host_checks(over, status):
+    assert _router(**over) == status
