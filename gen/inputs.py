@@ -167,6 +167,8 @@ WORKLOADS = {
     "e256_plateau": dict(E=256, H=2560, F=640, k=10, fused=True, seed=3),
     "skewed_prefill": dict(E=288, H=4096, F=640, k=8, fused=False, seed=4),
     "full_prefill": dict(E=288, H=4096, F=1280, k=8, fused=False, seed=5),
+    # the shared expert (Rocket post: N320 beside the routed experts) as a one-expert layer
+    "shared_expert": dict(E=1, H=2560, F=320, k=1, fused=False, seed=6),
 }
 
 
@@ -193,6 +195,8 @@ def make_routing(name: str, T: int, U: int | None = None, seed: int | None = Non
         ids = route_union(s, T, k, E, U if U is not None else T * k)
     elif name == "e256_plateau":
         ids = route_cyclic(s, T, k, E)
+    elif name == "shared_expert":   # every token, one slot, weight 1
+        return np.zeros((T, 1), dtype=np.int32), np.ones((T, 1), dtype=np.float32)
     else:
         ids = route_skewed(T, k, E)
     return ids, router_weights(s, T, k)
@@ -228,3 +232,32 @@ def make_random_case(seed: int, T: int, k: int, E: int, H: int, F: int,
                x=bf16_normal(seed, (T, H)))
     out.update(make_banks(E, H, F, fused, seed, scales))
     return out
+
+
+def make_shared_case(seed: int, T: int, H: int, F: int, scales: str = "pow2"):
+    """The shared expert as a case of the routed layer: one expert (E = 1) that every token
+    takes in its only slot (k = 1) with router weight 1, so the layer is the dense SwiGLU FFN
+    y_t = Wd (silu(Wg x_t) * Wu x_t) over all T rows. Separate gate, up and down banks."""
+    out = dict(E=1, H=H, F=F, k=1, T=T, fused=False, expert_base=0,
+               ids=np.zeros((T, 1), dtype=np.int32), w=np.ones((T, 1), dtype=np.float32),
+               x=bf16_normal(seed, (T, H)))
+    out.update(make_banks(1, H, F, False, seed, scales))
+    return out
+
+
+def split_ff(case: dict, F1: int):
+    """Split a separate-bank case along ff at F1 (a multiple of 64), as a tensor-parallel shard
+    of the FFN would hold it: rows [0, F1) and [F1, F) of gate and up, and of each down row the
+    NVFP4 blocks of input features [0, F1) and [F1, F). Pure byte slicing: two cases whose
+    outputs add up to the original's (the down projection is linear in h)."""
+    F = case["F"]
+    if F1 % NVFP4_BLOCK_WEIGHTS or not 0 < F1 < F:
+        raise ValueError("F1 must be a multiple of 64 strictly inside (0, F)")
+    b1 = row_bytes(F1)
+    a = dict(case, F=F1, gate=np.ascontiguousarray(case["gate"][:, :F1]),
+             up=np.ascontiguousarray(case["up"][:, :F1]),
+             down=np.ascontiguousarray(case["down"][:, :, :b1]))
+    b = dict(case, F=F - F1, gate=np.ascontiguousarray(case["gate"][:, F1:]),
+             up=np.ascontiguousarray(case["up"][:, F1:]),
+             down=np.ascontiguousarray(case["down"][:, :, b1:]))
+    return a, b

@@ -396,3 +396,30 @@ def test_router_topk_invariances():
     # k = E lists every expert once
     ids3, _ = oracle.router_topk(logits, 96)
     assert np.array_equal(np.sort(ids3, axis=1), np.tile(np.arange(96), (6, 1)))
+
+
+# ------------------------------------------------------------------------------ shared expert
+# The shared expert is the routed layer with one expert taken by every token at weight 1; the
+# pins are a dense SwiGLU on independently decoded weights and the linearity of the down
+# projection over an ff split (the pages' split-versus-full check).
+
+def test_shared_expert_is_dense_swiglu(golden_dir):
+    tab = _e2m1_golden(golden_dir)
+    case = gen.make_shared_case(91, T=5, H=128, F=192)
+    y = oracle.ffn_union(case)
+    x = torch.tensor(case["x"].astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    Wg = _decode_independent(case["gate"][0], 128, tab)
+    Wu = _decode_independent(case["up"][0], 128, tab)
+    Wd = _decode_independent(case["down"][0], 192, tab)
+    g, u = x @ Wg.T, x @ Wu.T
+    ref = (g * expit(g) * u) @ Wd.T
+    assert _rel(y, ref) < 1e-12
+
+
+@pytest.mark.parametrize("F,F1", [(320, 192), (384, 192), (320, 64)])
+def test_shared_expert_split_adds_up(F, F1):
+    case = gen.make_shared_case(92 + F1, T=4, H=256, F=F)
+    a, b = gen.split_ff(case, F1)
+    y = oracle.ffn_union(case)
+    ya, yb = oracle.ffn_union(a), oracle.ffn_union(b)
+    assert _rel(ya + yb, y) < 1e-12
