@@ -21,6 +21,7 @@ NVFP4_SCALES_PER_BLOCK = 4
 # stream ids: one per buffer kind, so adding a buffer never shifts another's values
 S_GATE, S_UP, S_DOWN, S_GATEUP, S_X, S_ROUTE, S_LOGITS, S_PERM = 1, 2, 3, 4, 5, 6, 7, 8
 S_RLOGITS = 9
+S_S2 = 10
 
 
 def rng_for(seed: int, stream: int, sub: int = 0) -> np.random.Generator:
@@ -261,3 +262,10 @@ def split_ff(case: dict, F1: int):
              up=np.ascontiguousarray(case["up"][:, F1:]),
              down=np.ascontiguousarray(case["down"][:, :, b1:]))
     return a, b
+
+
+def second_level_scales(seed: int, E: int, banks=("gate_s2", "up_s2", "down_s2")):
+    """Per-expert fp32 second-level scales for each bank (ModelOpt's two-level NVFP4 keeps one
+    such factor per weight tensor): log-uniform in [2^-4, 2^4], so none is a power of two."""
+    rng = rng_for(seed, S_S2)
+    return {b: np.exp2(rng.uniform(-4.0, 4.0, size=E)).astype(np.float32) for b in banks}

@@ -8,8 +8,9 @@ CPU test against something other than itself (see tests/test_oracle_pins.py):
   e2m1 / ue4m3 / nvfp4 decode  - the OCP element tables and torch's float8_e4m3fn decoding;
   route_bucket                 - a stable sort of the pair list (Python's sorted) and invariants;
   router_topk                  - numpy's stable sort and scipy's softmax, closed forms, ties;
-  ffn_per_slot / ffn_union     - numpy float64 matmuls on independently decoded weights,
-                                 closed-form special cases, invariances.
+  ffn_per_slot / ffn_union     - numpy float64 matmuls on independently decoded weights (with
+                                 and without second-level scales), closed-form special cases,
+                                 invariances.
 """
 from __future__ import annotations
 
@@ -60,19 +61,19 @@ def _load():
         lib.orc_route_bucket.restype = ctypes.c_int
         lib.orc_route_bucket.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                          ctypes.c_int32, _i32p, _i32p, _i32p, _i32p]
-        lib.orc_ffn_per_slot.restype = ctypes.c_int
-        lib.orc_ffn_per_slot.argtypes = [
+        lib.orc_ffn_per_slot_s2.restype = ctypes.c_int
+        lib.orc_ffn_per_slot_s2.argtypes = [
             _u16p, _f32p, _i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, _u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _u8p,
-            ctypes.c_int64, _i64p, ctypes.c_int64, _f64p, ctypes.c_int32]
+            ctypes.c_int64, _f32p, _f32p, _f32p, _i64p, ctypes.c_int64, _f64p, ctypes.c_int32]
         lib.orc_router_topk.restype = ctypes.c_int
         lib.orc_router_topk.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         _i32p, _f64p]
-        lib.orc_ffn_union.restype = ctypes.c_int
-        lib.orc_ffn_union.argtypes = [
+        lib.orc_ffn_union_s2.restype = ctypes.c_int
+        lib.orc_ffn_union_s2.argtypes = [
             _u16p, _f32p, _i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, _u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _u8p,
-            ctypes.c_int64, _f64p, _f64p, ctypes.c_int32]
+            ctypes.c_int64, _f32p, _f32p, _f32p, _f64p, _f64p, ctypes.c_int32]
         _lib = lib
     return _lib
 
@@ -149,6 +150,23 @@ def bank_views(case: dict):
     return gate, F * rbh, up, F * rbh, np.ascontiguousarray(case["down"]).reshape(-1), H * (F // 64 * 36)
 
 
+def _s2(case: dict):
+    """The case's second-level scales (float32 [E] per bank under gate_s2 / up_s2 / down_s2),
+    each as a ctypes pointer or None, plus the arrays to keep alive."""
+    keep, ptrs = [], []
+    for key in ("gate_s2", "up_s2", "down_s2"):
+        a = case.get(key)
+        if a is None:
+            ptrs.append(None)
+        else:
+            a = np.ascontiguousarray(a, dtype=np.float32)
+            if a.size != case["E"]:
+                raise ValueError(f"{key} needs one scale per expert")
+            keep.append(a)
+            ptrs.append(_p(a, _f32p))
+    return ptrs, keep
+
+
 def ffn_per_slot(case: dict, tokens=None, threads: int = 0, expert_base: int | None = None):
     """fp64 y[len(tokens), H] (all tokens when tokens is None), per-slot form."""
     lib = _load()
@@ -165,9 +183,10 @@ def ffn_per_slot(case: dict, tokens=None, threads: int = 0, expert_base: int | N
         tok = np.ascontiguousarray(tokens, dtype=np.int64)
         tok_p, n = _p(tok, _i64p), tok.size
     y = np.zeros((n, H), dtype=np.float64)
-    rc = lib.orc_ffn_per_slot(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
-                              _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds,
-                              tok_p, n, _p(y, _f64p), threads)
+    s2, _keep = _s2(case)
+    rc = lib.orc_ffn_per_slot_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
+                                 _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds, *s2,
+                                 tok_p, n, _p(y, _f64p), threads)
     if rc:
         raise ValueError("orc_ffn_per_slot rejected its arguments")
     return y
@@ -185,9 +204,10 @@ def ffn_union(case: dict, threads: int = 0, expert_base: int | None = None, want
     gate, gs, up, us, down, ds = bank_views(case)
     y = np.zeros((T, H), dtype=np.float64)
     h = np.full((T * k, F), np.nan) if want_h else None
-    rc = lib.orc_ffn_union(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
-                           _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds,
-                           _p(y, _f64p), _p(h, _f64p) if want_h else None, threads)
+    s2, _keep = _s2(case)
+    rc = lib.orc_ffn_union_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
+                              _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds, *s2,
+                              _p(y, _f64p), _p(h, _f64p) if want_h else None, threads)
     if rc:
         raise ValueError("orc_ffn_union rejected its arguments")
     return (y, h) if want_h else y

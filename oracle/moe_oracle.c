@@ -24,6 +24,10 @@
  *    sel_gu_silu and sel_v3 kernels it names; moe_sk_repro.rs: gate, up and down grouped
  *    calls). Everything is fp64; the intermediate h is not rounded.
  *
+ *  - Second-level scales (the ModelOpt NVFP4 form the Rocket post's banks use): optionally one
+ *    fp32 factor per expert and bank multiplies every weight of that expert's bank, so a weight
+ *    is code value * UE4M3 scale * s2[e]. Absent (NULL), the factor is 1.
+ *
  * Two forms of the FFN are provided. The per-slot form walks the pairs of each token and decodes
  * each needed weight row as it goes. The union form decodes every distinct active expert once
  * and then walks that expert's bucket (moe_union_probe.rs: the union-of-experts gather). Both
@@ -150,23 +154,37 @@ static void pair_ffn_dense(const double *x, const double *Wg, const double *Wu, 
     }
 }
 
-/* The same arithmetic, decoding each weight row just before it is used. */
+/* Multiply n decoded weights by a bank's second-level scale (s = 1: unchanged). */
+static void scale_weights(double *w, int64_t n, double s)
+{
+    if (s != 1.0)
+        for (int64_t i = 0; i < n; i++) w[i] *= s;
+}
+
+/* The second-level scale of expert e in a bank (1 when the bank has none). */
+static double s2_of(const float *s2, int64_t e) { return s2 ? (double)s2[e] : 1.0; }
+
+/* The same arithmetic, decoding each weight row just before it is used; sg, su, sd are the
+ * expert's second-level scales of the three banks. */
 static void pair_ffn_rowwise(const double *x, const uint8_t *gate, const uint8_t *up,
-                             const uint8_t *down, int32_t H, int32_t F, double *row, double *h,
-                             double *d)
+                             const uint8_t *down, int32_t H, int32_t F, double sg, double su,
+                             double sd, double *row, double *h, double *d)
 {
     int64_t rbh = orc_row_bytes(H), rbf = orc_row_bytes(F);
     for (int32_t o = 0; o < F; o++) {
         double g = 0.0, u = 0.0;
         orc_dequant_rows(gate + o * rbh, 1, H, row);
+        scale_weights(row, H, sg);
         for (int32_t i = 0; i < H; i++) g += row[i] * x[i];
         orc_dequant_rows(up + o * rbh, 1, H, row);
+        scale_weights(row, H, su);
         for (int32_t i = 0; i < H; i++) u += row[i] * x[i];
         h[o] = orc_silu(g) * u;
     }
     for (int32_t r = 0; r < H; r++) {
         double s = 0.0;
         orc_dequant_rows(down + r * rbf, 1, F, row);
+        scale_weights(row, F, sd);
         for (int32_t o = 0; o < F; o++) s += row[o] * h[o];
         d[r] = s;
     }
@@ -187,11 +205,12 @@ static void set_threads(int32_t n)
  * Banks: expert e's gate rows start at gate + e*gate_stride (bytes), likewise up and down;
  * gate/up rows have H inputs, down rows F inputs.
  */
-int orc_ffn_per_slot(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
-                     int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
-                     const uint8_t *gate, int64_t gate_stride, const uint8_t *up,
-                     int64_t up_stride, const uint8_t *down, int64_t down_stride,
-                     const int64_t *tokens, int64_t n_tokens, double *y, int32_t n_threads)
+int orc_ffn_per_slot_s2(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids,
+                        int64_t T, int32_t k, int32_t E, int32_t expert_base, int32_t H,
+                        int32_t F, const uint8_t *gate, int64_t gate_stride, const uint8_t *up,
+                        int64_t up_stride, const uint8_t *down, int64_t down_stride,
+                        const float *gate_s2, const float *up_s2, const float *down_s2,
+                        const int64_t *tokens, int64_t n_tokens, double *y, int32_t n_threads)
 {
     if (T < 0 || k < 1 || E < 1 || H % 64 || F % 64 || H < 64 || F < 64) return -1;
     if (!tokens && n_tokens != T) return -1;
@@ -212,7 +231,8 @@ int orc_ffn_per_slot(const uint16_t *x_bf16, const float *topk_w, const int32_t 
             int64_t e = (int64_t)ids[t * k + j] - expert_base;
             if (e < 0 || e >= E) continue;
             pair_ffn_rowwise(xr, gate + e * gate_stride, up + e * up_stride,
-                             down + e * down_stride, H, F, row, h, d);
+                             down + e * down_stride, H, F, s2_of(gate_s2, e), s2_of(up_s2, e),
+                             s2_of(down_s2, e), row, h, d);
             double wt = (double)topk_w[t * k + j];
             for (int32_t r = 0; r < H; r++) yr[r] += wt * d[r];
         }
@@ -221,17 +241,30 @@ int orc_ffn_per_slot(const uint16_t *x_bf16, const float *topk_w, const int32_t 
     return bad ? -1 : 0;
 }
 
+/* Without second-level scales. */
+int orc_ffn_per_slot(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
+                     int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
+                     const uint8_t *gate, int64_t gate_stride, const uint8_t *up,
+                     int64_t up_stride, const uint8_t *down, int64_t down_stride,
+                     const int64_t *tokens, int64_t n_tokens, double *y, int32_t n_threads)
+{
+    return orc_ffn_per_slot_s2(x_bf16, topk_w, ids, T, k, E, expert_base, H, F, gate,
+                               gate_stride, up, up_stride, down, down_stride, NULL, NULL, NULL,
+                               tokens, n_tokens, y, n_threads);
+}
+
 /*
  * Union form over all T tokens: bucket the pairs, decode each active expert once, run every
  * pair of its bucket, then combine each token's slots in ascending slot order. y[T][H] fp64.
  * If h_out is not NULL it receives h[p][F] for every local pair p (rows of non-local pairs are
  * left untouched).
  */
-int orc_ffn_union(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
-                  int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
-                  const uint8_t *gate, int64_t gate_stride, const uint8_t *up, int64_t up_stride,
-                  const uint8_t *down, int64_t down_stride, double *y, double *h_out,
-                  int32_t n_threads)
+int orc_ffn_union_s2(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
+                     int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
+                     const uint8_t *gate, int64_t gate_stride, const uint8_t *up,
+                     int64_t up_stride, const uint8_t *down, int64_t down_stride,
+                     const float *gate_s2, const float *up_s2, const float *down_s2, double *y,
+                     double *h_out, int32_t n_threads)
 {
     if (T < 0 || k < 1 || E < 1 || H % 64 || F % 64 || H < 64 || F < 64) return -1;
     set_threads(n_threads);
@@ -253,6 +286,9 @@ int orc_ffn_union(const uint16_t *x_bf16, const float *topk_w, const int32_t *id
         orc_dequant_rows(gate + e * gate_stride, F, H, Wg);
         orc_dequant_rows(up + e * up_stride, F, H, Wu);
         orc_dequant_rows(down + e * down_stride, H, F, Wd);
+        scale_weights(Wg, (int64_t)F * H, s2_of(gate_s2, e));
+        scale_weights(Wu, (int64_t)F * H, s2_of(up_s2, e));
+        scale_weights(Wd, (int64_t)H * F, s2_of(down_s2, e));
         int32_t b0 = offsets[e], b1 = offsets[e + 1];
 #pragma omp parallel for schedule(dynamic, 1)
         for (int32_t q = b0; q < b1; q++) {
@@ -281,6 +317,18 @@ int orc_ffn_union(const uint16_t *x_bf16, const float *topk_w, const int32_t *id
 out:
     free(offsets); free(pair_ids); free(active); free(D); free(has); free(Wg); free(Wu); free(Wd);
     return rc;
+}
+
+/* Without second-level scales. */
+int orc_ffn_union(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
+                  int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
+                  const uint8_t *gate, int64_t gate_stride, const uint8_t *up, int64_t up_stride,
+                  const uint8_t *down, int64_t down_stride, double *y, double *h_out,
+                  int32_t n_threads)
+{
+    return orc_ffn_union_s2(x_bf16, topk_w, ids, T, k, E, expert_base, H, F, gate, gate_stride,
+                            up, up_stride, down, down_stride, NULL, NULL, NULL, y, h_out,
+                            n_threads);
 }
 
 /*

@@ -225,6 +225,11 @@ def _dense_reference(case, e2m1_tab):
         Wg = [_decode_independent(case["gate"][e], H, e2m1_tab) for e in range(E)]
         Wu = [_decode_independent(case["up"][e], H, e2m1_tab) for e in range(E)]
     Wd = [_decode_independent(case["down"][e], F, e2m1_tab) for e in range(E)]
+    # second-level scales, when the case has them: every weight of expert e's bank times s2[e]
+    for key, W in (("gate_s2", Wg), ("up_s2", Wu), ("down_s2", Wd)):
+        if case.get(key) is not None:
+            for e in range(E):
+                W[e] = W[e] * float(case[key][e])
     x = torch.tensor(case["x"].astype(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     T = x.shape[0]
     y = np.zeros((T, H))
@@ -423,3 +428,40 @@ def test_shared_expert_split_adds_up(F, F1):
     y = oracle.ffn_union(case)
     ya, yb = oracle.ffn_union(a), oracle.ffn_union(b)
     assert _rel(ya + yb, y) < 1e-12
+
+
+
+# --------------------------------------------------------------------- second-level scales
+# ModelOpt's two-level NVFP4: one fp32 factor per expert and bank on top of the UE4M3 group
+# scales. Pinned to the dense numpy reference with the factors applied to the decoded weights,
+# and to exact scaling laws (powers of two in the up and down banks scale y exactly).
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_ffn_second_level_scales_match_numpy_dense(golden_dir, fused):
+    tab = _e2m1_golden(golden_dir)
+    case = gen.make_random_case(51, T=6, k=3, E=4, H=128, F=64, scales="all", fused=fused,
+                                nonlocal_frac=0.2)
+    case.update(gen.second_level_scales(52, 4))
+    ref = _dense_reference(case, tab)
+    assert _rel(oracle.ffn_per_slot(case), ref) < 1e-12
+    assert _rel(oracle.ffn_union(case), ref) < 1e-12
+    assert _rel(ref, _dense_reference(dict(case, gate_s2=None, up_s2=None, down_s2=None), tab)) > 1e-3
+
+
+def test_second_level_scale_laws():
+    case = gen.make_random_case(53, T=5, k=2, E=3, H=64, F=64)
+    y = oracle.ffn_union(case)
+    ones = np.ones(3, np.float32)
+    assert np.array_equal(oracle.ffn_union(dict(case, gate_s2=ones, up_s2=ones, down_s2=ones)), y)
+    pw = np.array([0.25, 2.0, 8.0], np.float32)
+    # y is a sum over slots; a power-of-two factor on expert e's up or down bank scales exactly
+    # the slots routed to e: y2 = s * y(slots of e) + y(other slots)
+    for e in range(3):
+        only = np.ones(3, np.float32)
+        only[e] = pw[e]
+        for key in ("down_s2", "up_s2"):
+            y2 = oracle.ffn_union(dict(case, **{key: only}))
+            c_e = dict(case, w=np.where(case["ids"] == e, case["w"], 0).astype(np.float32))
+            c_r = dict(case, w=np.where(case["ids"] != e, case["w"], 0).astype(np.float32))
+            y_e, y_r = oracle.ffn_union(c_e), oracle.ffn_union(c_r)
+            assert _rel(y2, pw[e] * y_e + y_r) < 1e-12
