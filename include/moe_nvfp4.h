@@ -68,10 +68,18 @@ enum {
 #define MOE_MAX_FF 8192            /* F limit */
 #define MOE_MAX_ROUTER_K 64        /* k limit of moe_router_topk (one slot per wavefront lane) */
 
-/* One weight bank: expert e's rows start at base + e*expert_stride (bytes, device). */
+/*
+ * One weight bank: expert e's rows start at base + e*expert_stride (bytes, device).
+ * scale2 (device, fp32 [E], or NULL): the optional second level of two-level NVFP4 (the
+ * ModelOpt form of the Rocket post's banks; moe_union_probe.rs names its "modelopt" kernels):
+ * every weight of expert e in this bank is code value * UE4M3 group scale * scale2[e]. The
+ * factor multiplies the bank's fp32 sums once, before SiLU for gate and up, at the output for
+ * down. NULL means 1 for every expert. Must be 4-byte aligned.
+ */
 typedef struct {
     const uint8_t *base;
     int64_t expert_stride;
+    const float *scale2;
 } moe_bank;
 
 /*

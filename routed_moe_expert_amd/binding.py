@@ -26,7 +26,8 @@ class MoeError(RuntimeError):
 
 
 class moe_bank(ctypes.Structure):
-    _fields_ = [("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64)]
+    _fields_ = [("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64),
+                ("scale2", ctypes.c_void_p)]
 
 
 def _load():
@@ -107,9 +108,11 @@ def moe_route_bucket(topk_ids, T: int, k: int, E: int, expert_base: int, offsets
     return _check("moe_route_bucket", st, raise_on_error)
 
 
-def bank(base, expert_stride: int, byte_offset: int = 0) -> moe_bank:
-    """A moe_bank for a device tensor (or address) plus an optional byte offset."""
-    return moe_bank(_ptr(base) + byte_offset if base is not None else None, int(expert_stride))
+def bank(base, expert_stride: int, byte_offset: int = 0, scale2=None) -> moe_bank:
+    """A moe_bank for a device tensor (or address) plus an optional byte offset, and optionally
+    the bank's per-expert fp32 second-level scales (a device tensor of E floats)."""
+    return moe_bank(_ptr(base) + byte_offset if base is not None else None, int(expert_stride),
+                    _ptr(scale2) or None)
 
 
 def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, up: moe_bank,

@@ -16,7 +16,7 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 bool bank_ok(const moe_bank &b) {
     return b.base != nullptr && aligned(b.base, 16) && b.expert_stride >= 0 &&
-           b.expert_stride % 16 == 0;
+           b.expert_stride % 16 == 0 && aligned(b.scale2, 4);
 }
 
 int check_common(int32_t T, int32_t k, int32_t E) {

@@ -312,11 +312,13 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
 }
 
 // The CSR entries a workgroup needs: its experts, their first CSR slot, pair count and first 16
-// pair ids.
+// pair ids, and the experts' second-level weight scales of up to two banks (1 when a bank has
+// none).
 constexpr int kMaxMeta = 32;   // experts per workgroup range; grids are sized so this holds
 struct Meta {
     int n_active;
     int e[kMaxMeta], q0[kMaxMeta], m[kMaxMeta], pid[kMaxMeta][kCols];
+    float s2a[kMaxMeta], s2b[kMaxMeta];
 };
 
 constexpr int kPairCap = 4096;   // pair ids read whole at start up to this many
@@ -331,7 +333,8 @@ inline size_t plan_scratch_bytes(int E, int P) {
 // costs one round trip to memory instead of the chain counts -> active -> offsets -> pair ids.
 __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restrict__ counts,
                           const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
-                          const int32_t *__restrict__ pair_ids, int E, int P, int tiles, int &i0,
+                          const int32_t *__restrict__ pair_ids, const float *__restrict__ s2a,
+                          const float *__restrict__ s2b, int E, int P, int tiles, int &i0,
                           int &i1, int &a_first) {
     const int tid = threadIdx.x;
     int32_t *s_act = scratch, *s_off = scratch + E, *s_pair = scratch + 2 * E + 1;
@@ -369,6 +372,8 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
         meta.e[tid] = e;
         meta.q0[tid] = q0;
         meta.m[tid] = m;
+        meta.s2a[tid] = s2a ? s2a[e] : 1.f;
+        meta.s2b[tid] = s2b ? s2b[e] : 1.f;
         // an active expert has m >= 1: entries past m re-read entry m - 1 and are then zeroed
         if (pairs_in_lds) {
 #pragma unroll
@@ -405,8 +410,9 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const int32_t *__restrict__ active,
     const int32_t *__restrict__ counts, const uint8_t *__restrict__ gate, int64_t gate_stride,
-    const uint8_t *__restrict__ up, int64_t up_stride, int32_t k, int32_t P, int32_t E, int32_t H,
-    int32_t F, int32_t nbuf, int32_t ring_bytes, float *__restrict__ h, int32_t *__restrict__ pos) {
+    const uint8_t *__restrict__ up, int64_t up_stride, const float *__restrict__ gate_s2,
+    const float *__restrict__ up_s2, int32_t k, int32_t P, int32_t E, int32_t H, int32_t F,
+    int32_t nbuf, int32_t ring_bytes, float *__restrict__ h, int32_t *__restrict__ pos) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = H / kBlockWeights * kBlockBytes;
     const int side = kGuO * rb;
@@ -421,8 +427,8 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const int tiles = F / kGuO;
 
     int i0, i1, a_first;
-    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, E, P,
-              tiles, i0, i1, a_first);
+    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, gate_s2,
+              up_s2, E, P, tiles, i0, i1, a_first);
     // load k of this wave moves LDS chunk p = 64 wave + 256 k + lane of the tile,
     // row p / cpr, chunk p % cpr of it (the last one a copy of chunk 0); its source offset within
     // the gate or up rows of the tile (sign bit: up) is the same for every tile
@@ -457,7 +463,10 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
 
     // reduction of a unit by one wave: lane -> (feature f, token column nn). One wave (rotating)
     // takes it while the others go on, which measured faster than a quarter per wave.
-    auto reduce = [&](const float *rp, int q0, int c, int t, int mt) {
+    // (a_: the unit's expert index, for its first CSR slot and second-level gate and up scales)
+    auto reduce = [&](const float *rp, int a_, int c, int t, int mt) {
+        const int q0 = meta.q0[a_];
+        const float sg = meta.s2a[a_], su = meta.s2b[a_];
         for (int o = lane; o < kGuO * mt; o += 64) {
             const int f = o & (kGuO - 1), nn = o / kGuO;
             float g = 0.f, u = 0.f;
@@ -466,6 +475,8 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
                 g += rp[(w * kCols + nn) * 16 + f];
                 u += rp[(w * kCols + nn) * 16 + f + kGuO];
             }
+            g *= sg;
+            u *= su;
             h[(int64_t)(q0 + c * kCols + nn) * F + t * kGuO + f] = silu(g) * u;
         }
     };
@@ -489,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     }
     for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
 
-    int unit = 0, p_q0 = 0, p_c = 0, p_t = 0, p_mt = 0;
+    int unit = 0, p_a = 0, p_c = 0, p_t = 0, p_mt = 0;
     int a = 0, t = i0 - a_first * tiles, slot = 0;   // item i: expert index, row tile, ring slot
     for (int i = i0; i < i1; i++) {
         const int q0 = meta.q0[a], m = meta.m[a];
@@ -511,7 +522,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
                 issue_next();
             }
             if (unit > 0 && wave == (unit - 1) % kWaves)
-                reduce(red + ((unit - 1) & 1) * kRedFloats, p_q0, p_c, p_t, p_mt);
+                reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
             // two independent accumulation chains (K steps 0 and 1 of each block) halve the
             // dependent MFMA latency
             f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
@@ -523,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
             }
             *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats + (wave * kCols + n) * 16 +
                                          4 * q) = unscale(acc0 + acc1, xs);
-            p_q0 = q0;
+            p_a = a;
             p_c = c;
             p_t = t;
             p_mt = mt;
@@ -534,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     if (unit > 0) {
         lds_barrier();
         if (wave == (unit - 1) % kWaves)
-            reduce(red + ((unit - 1) & 1) * kRedFloats, p_q0, p_c, p_t, p_mt);
+            reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
     }
     // pair -> CSR slot map for the combine (not needed before it)
     for (int q2 = blockIdx.x * kThreads + tid; q2 < P; q2 += gridDim.x * kThreads)
@@ -550,9 +561,9 @@ template <int NB>
 __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
     const int32_t *__restrict__ active, const int32_t *__restrict__ counts,
-    const uint8_t *__restrict__ down, int64_t down_stride, int32_t P, int32_t E, int32_t H,
-    int32_t F, int32_t RT, int32_t nbuf, int32_t ring_bytes, const float *__restrict__ h,
-    float *__restrict__ ypair) {
+    const uint8_t *__restrict__ down, int64_t down_stride, const float *__restrict__ down_s2,
+    int32_t P, int32_t E, int32_t H, int32_t F, int32_t RT, int32_t nbuf, int32_t ring_bytes,
+    const float *__restrict__ h, float *__restrict__ ypair) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = F / kBlockWeights * kBlockBytes;
     const int rows = 16 * RT, tile_bytes = rows * rb;
@@ -568,8 +579,8 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int tiles = H / rows;
 
     int i0, i1, a_first;
-    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, E, P,
-              tiles, i0, i1, a_first);
+    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, down_s2,
+              nullptr, E, P, tiles, i0, i1, a_first);
     if (i0 >= i1) return;
     const int n_inst = stage_async_count<kThreads>(tile_bytes);
     int ia = 0, it = i0 - a_first * tiles, is = 0;   // stream cursor
@@ -583,13 +594,14 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     };
     // output u = (token column u / rows, row u % rows of the item) sums the KS slices of its row
     // tile; wave w takes the quarter u in [w Q, (w + 1) Q), Q = rows mt / 4 >= 4
-    auto reduce = [&](const float *rp, const int *pids, int t, int mt) {
+    // (sd: the expert's second-level down scale)
+    auto reduce = [&](const float *rp, const int *pids, int t, int mt, float sd) {
         const int Q = rows * mt / kWaves;
         for (int l = lane; l < Q; l += 64) {
             const int u = wave * Q + l, r = u % rows, nn = u / rows;
             float v = 0.f;
             for (int s2 = 0; s2 < KS; s2++) v += rp[((s2 * RT + r / 16) * kCols + nn) * 16 + r % 16];
-            ypair[(int64_t)pids[nn] * H + t * rows + r] = v;
+            ypair[(int64_t)pids[nn] * H + t * rows + r] = v * sd;
         }
     };
 
@@ -612,9 +624,11 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
 
     int unit = 0, p_t = 0, p_mt = 0;
+    float p_sd = 1.f;
     int a = 0, t = i0 - a_first * tiles, slot = 0;
     for (int i = i0; i < i1; i++) {
         const int m = meta.m[a];
+        const float sd = meta.s2a[a];
         const uint8_t *wt = wb + slot * tile_bytes + (rt * 16 + n) * rb;
         for (int c = 0; c * kCols < m; c++, unit++) {
             const int mt = min(kCols, m - c * kCols);
@@ -637,7 +651,7 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
                 issue_next();
             }
             if (KS > 1 && unit > 0)
-                reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt);
+                reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt, p_sd);
             // hi and lo parts accumulate in two independent chains (half the dependent latency)
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acl = acc;
 #pragma unroll
@@ -653,20 +667,21 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
             if (KS == 1) {   // whole rows: lane holds rows 4q..4q+3 of token column n
                 if (n < mt)
                     *reinterpret_cast<f32x4_t *>(ypair + (int64_t)pid_n * H + t * rows + rt * 16 +
-                                                 4 * q) = acc;
+                                                 4 * q) = acc * sd;
             } else {
                 *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats +
                                              (wave * kCols + n) * 16 + 4 * q) = acc;
             }
             p_t = t;
             p_mt = mt;
+            p_sd = sd;
         }
         if (++t == tiles) { t = 0; ++a; }
         if (++slot == nbuf) slot = 0;
     }
     if (KS > 1) {
         lds_barrier();
-        reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt);
+        reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt, p_sd);
     }
 }
 
@@ -806,7 +821,8 @@ int launch_gu(const FfnArgs &a, const DecodeWs &d, int max_active, hipStream_t s
     prof_start(MOE_KERNEL_GU_DECODE, s);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.x, a.offsets, a.pair_ids,
                        a.active, a.counts, a.gate.base, a.gate.expert_stride, a.up.base,
-                       a.up.expert_stride, a.k, P, a.E, a.H, a.F, nbuf, ring_bytes, d.h, d.pos);
+                       a.up.expert_stride, a.gate.scale2, a.up.scale2, a.k, P, a.E, a.H, a.F, nbuf,
+                       ring_bytes, d.h, d.pos);
     prof_stop(MOE_KERNEL_GU_DECODE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
@@ -830,8 +846,8 @@ int launch_dn(const FfnArgs &a, const DecodeWs &d, int max_active, int RT, hipSt
     if (max_experts((int64_t)max_active * tiles, tiles, grid) > kMaxMeta) return MOE_ESHAPE;
     prof_start(MOE_KERNEL_DN_DECODE, s);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.offsets, a.pair_ids, a.active,
-                       a.counts, a.down.base, a.down.expert_stride, P, a.E, a.H, a.F, RT, nbuf,
-                       ring_bytes, d.h, d.ypair);
+                       a.counts, a.down.base, a.down.expert_stride, a.down.scale2, P, a.E, a.H,
+                       a.F, RT, nbuf, ring_bytes, d.h, d.ypair);
     prof_stop(MOE_KERNEL_DN_DECODE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

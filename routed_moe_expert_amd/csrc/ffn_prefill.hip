@@ -221,6 +221,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const int32_t *__restrict__ pair_ids, const i32x2_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, int32_t max_tiles, int32_t n_ntiles,
     const uint8_t *__restrict__ w0, int64_t s0, const uint8_t *__restrict__ w1, int64_t s1,
+    const float *__restrict__ w0_s2, const float *__restrict__ w1_s2,
     int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
     uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int32_t *__restrict__ hs,
     float *__restrict__ ypair) {
@@ -254,6 +255,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const int q0 = offsets[e] + m0;
     const int mt = min(kBM2, offsets[e + 1] - q0);
     if (mt <= 0) return;
+    // the expert's second-level scales of bank 0 (gate or down) and bank 1 (up): 1 if none
+    const float sc0 = w0_s2 ? w0_s2[e] : 1.f, sc1 = w1_s2 ? w1_s2[e] : 1.f;
     const int ncol = (mt + 15) >> 4;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -416,8 +419,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
 #pragma unroll
                 for (int f = 0; f < kAT; f++) {
                     const int r = nt * kRows + arow[f] + 4 * q;
-                    const f32x4_t y4 = {ldexpf(acc[f][c][0], sl), ldexpf(acc[f][c][1], sl),
-                                        ldexpf(acc[f][c][2], sl), ldexpf(acc[f][c][3], sl)};
+                    const f32x4_t y4 = {ldexpf(acc[f][c][0], sl) * sc0, ldexpf(acc[f][c][1], sl) * sc0,
+                                        ldexpf(acc[f][c][2], sl) * sc0, ldexpf(acc[f][c][3], sl) * sc0};
                     if (r < H) *reinterpret_cast<f32x4_t *>(ypair + prow + r) = y4;
                 }
             }
@@ -431,7 +434,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         // over the workgroup's exchange of maxima)
         auto hval = [&](int t, int c, int v, int sc) {
             const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q + v;
-            const float g = ldexpf(acc[t][c][v], sc), u = ldexpf(acc[2 + t][c][v], sc);
+            const float g = ldexpf(acc[t][c][v], sc) * sc0, u = ldexpf(acc[2 + t][c][v], sc) * sc1;
             return o < F ? silu(g) * u : 0.f;
         };
         float *cmax = reinterpret_cast<float *>(smem);   // [kWaves][kBM]: stages are done
@@ -540,13 +543,14 @@ int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
     if constexpr (DOWN)
         hipLaunchKernelGGL((gemm_kernel<true>), dim3(grid), dim3(kGemmThreads), lds, s, nullptr,
                            w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt, n_ntiles,
-                           a.down.base, a.down.expert_stride, nullptr, (int64_t)0, a.k, a.F, a.F,
-                           a.H, nullptr, nullptr, nullptr, w.hs, w.ypair);
+                           a.down.base, a.down.expert_stride, nullptr, (int64_t)0, a.down.scale2,
+                           nullptr, a.k, a.F, a.F, a.H, nullptr, nullptr, nullptr, w.hs, w.ypair);
     else
         hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kGemmThreads), lds, s,
                            (const uint16_t *)w.x16, nullptr, nullptr, a.offsets, a.pair_ids,
                            w.tiles, w.n_tiles, mt, n_ntiles, a.gate.base, a.gate.expert_stride,
-                           a.up.base, a.up.expert_stride, a.k, a.H, a.F, a.H,
+                           a.up.base, a.up.expert_stride, a.gate.scale2, a.up.scale2, a.k, a.H,
+                           a.F, a.H,
                            (const int32_t *)w.xs, w.h_hi, w.h_lo, w.hs, nullptr);
     prof_stop(id, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;

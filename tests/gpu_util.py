@@ -32,17 +32,20 @@ class DeviceCase:
         self.x = to_dev(case["x"])
         H, F = self.H, self.F
         rbh, rbf = H // 64 * 36, F // 64 * 36
+        # optional per-expert second-level scales of each bank
+        self.s2 = {key: to_dev(case[key].astype(np.float32)) if case.get(key) is not None else None
+                   for key in ("gate_s2", "up_s2", "down_s2")}
         if "gate_up" in case:
             self.gu = to_dev(case["gate_up"])
-            self.gate = moe.bank(self.gu, 2 * F * rbh)
-            self.up = moe.bank(self.gu, 2 * F * rbh, F * rbh)
+            self.gate = moe.bank(self.gu, 2 * F * rbh, scale2=self.s2["gate_s2"])
+            self.up = moe.bank(self.gu, 2 * F * rbh, F * rbh, scale2=self.s2["up_s2"])
         else:
             self.g = to_dev(case["gate"])
             self.u = to_dev(case["up"])
-            self.gate = moe.bank(self.g, F * rbh)
-            self.up = moe.bank(self.u, F * rbh)
+            self.gate = moe.bank(self.g, F * rbh, scale2=self.s2["gate_s2"])
+            self.up = moe.bank(self.u, F * rbh, scale2=self.s2["up_s2"])
         self.d = to_dev(case["down"])
-        self.down = moe.bank(self.d, H * rbf)
+        self.down = moe.bank(self.d, H * rbf, scale2=self.s2["down_s2"])
         dev = self.ids.device
         self.offsets = torch.empty(self.E + 1, dtype=torch.int32, device=dev)
         self.pair_ids = torch.empty(max(P, 1), dtype=torch.int32, device=dev)
