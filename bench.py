@@ -40,8 +40,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "fa96d6529b0de3e58811149867b81f84bf7e55d9a84721d2461cbdf0cadb7f84",
-        "fetch_kib": 54327.1, "write_kib": 169.1,
+        "sha256": "3398d323e473ca3053507694251d5eba84ecb6e1d37a7c5b40f5839188d1cb70",
+        "fetch_kib": 54336.9, "write_kib": 171.6,
     },
 }
 
