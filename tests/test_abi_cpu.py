@@ -64,7 +64,7 @@ def _ffn(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(x=0), moe.MOE_EINVAL), (dict(y=0), moe.MOE_EINVAL), (dict(ws=0), moe.MOE_EINVAL),
     (dict(T=-1), moe.MOE_EINVAL), (dict(k=0), moe.MOE_EINVAL), (dict(E=0), moe.MOE_EINVAL),
-    (dict(H=320), moe.MOE_EINVAL), (dict(F=96), moe.MOE_EINVAL), (dict(path=7), moe.MOE_EINVAL),
+    (dict(H=320), moe.MOE_EINVAL), (dict(F=96), moe.MOE_EINVAL), (dict(path=7), moe.MOE_EINVAL), (dict(path=4), moe.MOE_EINVAL),
     (dict(gate=_bank(FAKE + 4)), moe.MOE_EINVAL), (dict(down=_bank(stride=100)), moe.MOE_EINVAL),
     (dict(up=_bank(0)), moe.MOE_EINVAL), (dict(x=FAKE + 2), moe.MOE_EINVAL),
     (dict(ws=FAKE + 16), moe.MOE_EINVAL),
