@@ -75,11 +75,17 @@ enum {
  * every weight of expert e in this bank is code value * UE4M3 group scale * scale2[e]. The
  * factor multiplies the bank's fp32 sums once, before SiLU for gate and up, at the output for
  * down. NULL means 1 for every expert. Must be 4-byte aligned.
+ * experts (device, [E] device pointers, or NULL): the per-expert table form (moe_sk_repro.rs
+ * builds a table of per-expert weight pointers for its grouped calls): when not NULL, expert e's
+ * rows start at experts[e] and base / expert_stride are not used (base may be NULL). Every
+ * experts[e] of an expert that is routed to must be 16-byte aligned (not checkable on the host:
+ * a misaligned entry gives undefined results); the table itself must be 8-byte aligned.
  */
 typedef struct {
     const uint8_t *base;
     int64_t expert_stride;
     const float *scale2;
+    const uint8_t *const *experts;
 } moe_bank;
 
 /*

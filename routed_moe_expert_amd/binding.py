@@ -27,7 +27,7 @@ class MoeError(RuntimeError):
 
 class moe_bank(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64),
-                ("scale2", ctypes.c_void_p)]
+                ("scale2", ctypes.c_void_p), ("experts", ctypes.c_void_p)]
 
 
 def _load():
@@ -108,11 +108,12 @@ def moe_route_bucket(topk_ids, T: int, k: int, E: int, expert_base: int, offsets
     return _check("moe_route_bucket", st, raise_on_error)
 
 
-def bank(base, expert_stride: int, byte_offset: int = 0, scale2=None) -> moe_bank:
+def bank(base, expert_stride: int, byte_offset: int = 0, scale2=None, experts=None) -> moe_bank:
     """A moe_bank for a device tensor (or address) plus an optional byte offset, and optionally
-    the bank's per-expert fp32 second-level scales (a device tensor of E floats)."""
+    the bank's per-expert fp32 second-level scales (a device tensor of E floats) and a per-expert
+    pointer table (a device int64 tensor of E addresses; base and expert_stride are then unused)."""
     return moe_bank(_ptr(base) + byte_offset if base is not None else None, int(expert_stride),
-                    _ptr(scale2) or None)
+                    _ptr(scale2) or None, _ptr(experts) or None)
 
 
 def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, up: moe_bank,

@@ -15,8 +15,10 @@ namespace {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool bank_ok(const moe_bank &b) {
+    if (!aligned(b.scale2, 4)) return false;
+    if (b.experts != nullptr) return aligned(b.experts, 8);   // base and stride unused
     return b.base != nullptr && aligned(b.base, 16) && b.expert_stride >= 0 &&
-           b.expert_stride % 16 == 0 && aligned(b.scale2, 4);
+           b.expert_stride % 16 == 0;
 }
 
 int check_common(int32_t T, int32_t k, int32_t E) {

@@ -312,14 +312,22 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
 }
 
 // The CSR entries a workgroup needs: its experts, their first CSR slot, pair count and first 16
-// pair ids, and the experts' second-level weight scales of up to two banks (1 when a bank has
-// none).
+// pair ids, and for up to two banks the experts' first weight rows and second-level weight scales
+// (1 when a bank has none).
 constexpr int kMaxMeta = 32;   // experts per workgroup range; grids are sized so this holds
 struct Meta {
     int n_active;
     int e[kMaxMeta], q0[kMaxMeta], m[kMaxMeta], pid[kMaxMeta][kCols];
     float s2a[kMaxMeta], s2b[kMaxMeta];
+    const uint8_t *pa[kMaxMeta], *pb[kMaxMeta];
 };
+
+// Expert e's first weight row in a bank: from the bank's per-expert pointer table when it has one,
+// else at base + e * stride.
+__device__ __forceinline__ const uint8_t *expert_rows(const uint8_t *base, int64_t stride,
+                                                      const uint8_t *const *tab, int e) {
+    return tab ? tab[e] : base + e * stride;
+}
 
 constexpr int kPairCap = 4096;   // pair ids read whole at start up to this many
 
@@ -333,7 +341,9 @@ inline size_t plan_scratch_bytes(int E, int P) {
 // costs one round trip to memory instead of the chain counts -> active -> offsets -> pair ids.
 __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restrict__ counts,
                           const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
-                          const int32_t *__restrict__ pair_ids, const float *__restrict__ s2a,
+                          const int32_t *__restrict__ pair_ids, const uint8_t *wa, int64_t sa,
+                          const uint8_t *const *ta, const float *__restrict__ s2a,
+                          const uint8_t *wb, int64_t sb, const uint8_t *const *tb,
                           const float *__restrict__ s2b, int E, int P, int tiles, int &i0,
                           int &i1, int &a_first) {
     const int tid = threadIdx.x;
@@ -374,6 +384,8 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
         meta.m[tid] = m;
         meta.s2a[tid] = s2a ? s2a[e] : 1.f;
         meta.s2b[tid] = s2b ? s2b[e] : 1.f;
+        meta.pa[tid] = expert_rows(wa, sa, ta, e);
+        meta.pb[tid] = (wb || tb) ? expert_rows(wb, sb, tb, e) : nullptr;
         // an active expert has m >= 1: entries past m re-read entry m - 1 and are then zeroed
         if (pairs_in_lds) {
 #pragma unroll
@@ -410,7 +422,8 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const uint16_t *__restrict__ x, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const int32_t *__restrict__ active,
     const int32_t *__restrict__ counts, const uint8_t *__restrict__ gate, int64_t gate_stride,
-    const uint8_t *__restrict__ up, int64_t up_stride, const float *__restrict__ gate_s2,
+    const uint8_t *const *__restrict__ gate_tab, const uint8_t *__restrict__ up, int64_t up_stride,
+    const uint8_t *const *__restrict__ up_tab, const float *__restrict__ gate_s2,
     const float *__restrict__ up_s2, int32_t k, int32_t P, int32_t E, int32_t H, int32_t F,
     int32_t nbuf, int32_t ring_bytes, float *__restrict__ h, int32_t *__restrict__ pos) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -427,8 +440,9 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const int tiles = F / kGuO;
 
     int i0, i1, a_first;
-    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, gate_s2,
-              up_s2, E, P, tiles, i0, i1, a_first);
+    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, gate,
+              gate_stride, gate_tab, gate_s2, up, up_stride, up_tab, up_s2, E, P, tiles, i0, i1,
+              a_first);
     // load k of this wave moves LDS chunk p = 64 wave + 256 k + lane of the tile,
     // row p / cpr, chunk p % cpr of it (the last one a copy of chunk 0); its source offset within
     // the gate or up rows of the tile (sign bit: up) is the same for every tile
@@ -444,10 +458,9 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     // stream cursor: the next item to load (expert index, row tile, ring slot)
     int ia = 0, it = i0 - a_first * tiles, is = 0;
     auto issue_next = [&]() {
-        const int e = meta.e[ia];
         uint8_t *dst = wb + is * tile_bytes;
-        const uint8_t *gt = gate + e * gate_stride + (int64_t)it * side;
-        const uint8_t *ut = up + e * up_stride + (int64_t)it * side;
+        const uint8_t *gt = meta.pa[ia] + (int64_t)it * side;
+        const uint8_t *ut = meta.pb[ia] + (int64_t)it * side;
 #pragma unroll
         for (int kk = 0; kk < kMaxTileInst; kk++) {
             const int base = wave * 64 + kk * kThreads;
@@ -561,7 +574,8 @@ template <int NB>
 __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
     const int32_t *__restrict__ active, const int32_t *__restrict__ counts,
-    const uint8_t *__restrict__ down, int64_t down_stride, const float *__restrict__ down_s2,
+    const uint8_t *__restrict__ down, int64_t down_stride,
+    const uint8_t *const *__restrict__ down_tab, const float *__restrict__ down_s2,
     int32_t P, int32_t E, int32_t H, int32_t F, int32_t RT, int32_t nbuf, int32_t ring_bytes,
     const float *__restrict__ h, float *__restrict__ ypair) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -579,15 +593,15 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int tiles = H / rows;
 
     int i0, i1, a_first;
-    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, down_s2,
-              nullptr, E, P, tiles, i0, i1, a_first);
+    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, down,
+              down_stride, down_tab, down_s2, nullptr, 0, nullptr, nullptr, E, P, tiles, i0, i1,
+              a_first);
     if (i0 >= i1) return;
     const int n_inst = stage_async_count<kThreads>(tile_bytes);
     int ia = 0, it = i0 - a_first * tiles, is = 0;   // stream cursor
     auto issue_next = [&]() {
-        const int e = meta.e[ia];
-        stage_async<kThreads>(wb + is * tile_bytes,
-                              down + e * down_stride + (int64_t)it * tile_bytes, tile_bytes);
+        stage_async<kThreads>(wb + is * tile_bytes, meta.pa[ia] + (int64_t)it * tile_bytes,
+                              tile_bytes);
         asm volatile("" ::: "memory");   // later stores stay behind these loads (ring waits)
         if (++it == tiles) { it = 0; ++ia; }
         if (++is == nbuf) is = 0;
@@ -820,8 +834,9 @@ int launch_gu(const FfnArgs &a, const DecodeWs &d, int max_active, hipStream_t s
     if (max_experts((int64_t)max_active * tiles, tiles, grid) > kMaxMeta) return MOE_ESHAPE;
     prof_start(MOE_KERNEL_GU_DECODE, s);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.x, a.offsets, a.pair_ids,
-                       a.active, a.counts, a.gate.base, a.gate.expert_stride, a.up.base,
-                       a.up.expert_stride, a.gate.scale2, a.up.scale2, a.k, P, a.E, a.H, a.F, nbuf,
+                       a.active, a.counts, a.gate.base, a.gate.expert_stride, a.gate.experts,
+                       a.up.base, a.up.expert_stride, a.up.experts, a.gate.scale2, a.up.scale2, a.k,
+                       P, a.E, a.H, a.F, nbuf,
                        ring_bytes, d.h, d.pos);
     prof_stop(MOE_KERNEL_GU_DECODE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
@@ -846,7 +861,8 @@ int launch_dn(const FfnArgs &a, const DecodeWs &d, int max_active, int RT, hipSt
     if (max_experts((int64_t)max_active * tiles, tiles, grid) > kMaxMeta) return MOE_ESHAPE;
     prof_start(MOE_KERNEL_DN_DECODE, s);
     hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.offsets, a.pair_ids, a.active,
-                       a.counts, a.down.base, a.down.expert_stride, a.down.scale2, P, a.E, a.H,
+                       a.counts, a.down.base, a.down.expert_stride, a.down.experts, a.down.scale2,
+                       P, a.E, a.H,
                        a.F, RT, nbuf, ring_bytes, d.h, d.ypair);
     prof_stop(MOE_KERNEL_DN_DECODE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;

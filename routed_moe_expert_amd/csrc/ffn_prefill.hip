@@ -220,7 +220,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const uint16_t *__restrict__ hin_lo, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const i32x2_t *__restrict__ tiles,
     const int32_t *__restrict__ n_tiles, int32_t max_tiles, int32_t n_ntiles,
-    const uint8_t *__restrict__ w0, int64_t s0, const uint8_t *__restrict__ w1, int64_t s1,
+    const uint8_t *__restrict__ w0, int64_t s0, const uint8_t *const *__restrict__ t0,
+    const uint8_t *__restrict__ w1, int64_t s1, const uint8_t *const *__restrict__ t1,
     const float *__restrict__ w0_s2, const float *__restrict__ w1_s2,
     int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
     uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int32_t *__restrict__ hs,
@@ -257,6 +258,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     if (mt <= 0) return;
     // the expert's second-level scales of bank 0 (gate or down) and bank 1 (up): 1 if none
     const float sc0 = w0_s2 ? w0_s2[e] : 1.f, sc1 = w1_s2 ? w1_s2[e] : 1.f;
+    // the expert's first row in bank 0 and bank 1: from a per-expert pointer table, else strided
+    const uint8_t *e0 = t0 ? t0[e] : w0 + e * s0;
+    const uint8_t *e1 = DOWN ? nullptr : t1 ? t1[e] : w1 + e * s1;
     const int ncol = (mt + 15) >> 4;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -287,11 +291,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         const int row = u / 3;
         const uint8_t *base;
         if (DOWN) {
-            base = w0 + e * s0 + (int64_t)min(nt * kRows + row, n_out - 1) * rb;
+            base = e0 + (int64_t)min(nt * kRows + row, n_out - 1) * rb;
         } else {
             const int half = kRows / 2;   // gate rows, then the matching up rows
             const int f = min(nt * half + (row < half ? row : row - half), n_out - 1);
-            base = (row < half ? w0 + e * s0 : w1 + e * s1) + (int64_t)f * rb;
+            base = (row < half ? e0 : e1) + (int64_t)f * rb;
         }
         asrc[i] = base + 12 * (u % 3);
     }
@@ -543,13 +547,15 @@ int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
     if constexpr (DOWN)
         hipLaunchKernelGGL((gemm_kernel<true>), dim3(grid), dim3(kGemmThreads), lds, s, nullptr,
                            w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt, n_ntiles,
-                           a.down.base, a.down.expert_stride, nullptr, (int64_t)0, a.down.scale2,
-                           nullptr, a.k, a.F, a.F, a.H, nullptr, nullptr, nullptr, w.hs, w.ypair);
+                           a.down.base, a.down.expert_stride, a.down.experts, nullptr, (int64_t)0,
+                           nullptr, a.down.scale2, nullptr, a.k, a.F, a.F, a.H, nullptr, nullptr,
+                           nullptr, w.hs, w.ypair);
     else
         hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kGemmThreads), lds, s,
                            (const uint16_t *)w.x16, nullptr, nullptr, a.offsets, a.pair_ids,
                            w.tiles, w.n_tiles, mt, n_ntiles, a.gate.base, a.gate.expert_stride,
-                           a.up.base, a.up.expert_stride, a.gate.scale2, a.up.scale2, a.k, a.H,
+                           a.gate.experts, a.up.base, a.up.expert_stride, a.up.experts,
+                           a.gate.scale2, a.up.scale2, a.k, a.H,
                            a.F, a.H,
                            (const int32_t *)w.xs, w.h_hi, w.h_lo, w.hs, nullptr);
     prof_stop(id, s);

@@ -67,6 +67,8 @@ def _ffn(**over):
     (dict(H=320), moe.MOE_EINVAL), (dict(F=96), moe.MOE_EINVAL), (dict(path=7), moe.MOE_EINVAL), (dict(path=4), moe.MOE_EINVAL),
     (dict(gate=_bank(FAKE + 4)), moe.MOE_EINVAL), (dict(down=_bank(stride=100)), moe.MOE_EINVAL),
     (dict(up=_bank(0)), moe.MOE_EINVAL), (dict(x=FAKE + 2), moe.MOE_EINVAL),
+    (dict(gate=moe_bank(0, 0, None, FAKE + 4)), moe.MOE_EINVAL),      # pointer table misaligned
+    (dict(down=moe_bank(FAKE, 4096, FAKE + 2)), moe.MOE_EINVAL),      # scale2 misaligned
     (dict(ws=FAKE + 16), moe.MOE_EINVAL),
     (dict(E=4096), moe.MOE_ESHAPE), (dict(H=1 << 15), moe.MOE_ESHAPE),
     (dict(ws_bytes=16), moe.MOE_EWS),
