@@ -40,8 +40,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "3398d323e473ca3053507694251d5eba84ecb6e1d37a7c5b40f5839188d1cb70",
-        "fetch_kib": 54336.9, "write_kib": 171.6,
+        "sha256": "7d25a06425f08585f3a9cceb854efa8f898c2d20925880848a54d2d93c461e37",
+        "fetch_kib": 54326.5, "write_kib": 171.6,
     },
 }
 
