@@ -84,6 +84,8 @@ def parse():
     ap.add_argument("--k", type=int, default=8, help="top-k (router workload)")
     ap.add_argument("--T", type=int, default=None, help="tokens (workload default if unset)")
     ap.add_argument("--U", type=int, default=60, help="union size for verify_chunk")
+    ap.add_argument("--virtual", type=int, default=0,
+                    help="shared_expert: virtual experts over its one weight copy (0: T/16)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--warm", action="store_true", help="reuse one routing (cache-warm numbers)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,6 +120,7 @@ def build_inputs(args, torch, gen, moe):
     T = args.T or DEFAULT_T[name]
     U = None
     copies = 1
+    virtual = 0
     if name == "verify_chunk":
         U = args.U
         variants = [gen.route_union_rotated(seed, T, k, E, U, v)
@@ -127,6 +130,11 @@ def build_inputs(args, torch, gen, moe):
         copies = 1 if args.warm else 3          # 3 bank copies x disjoint windows > 2 x 256 MB
         variants = [gen.route_union_rotated(seed, T, k, E, k, v)
                     for v in range(1 if args.warm else E // k)]
+    elif name == "shared_expert":
+        # the one expert as G virtual experts (pointer tables onto its one copy), tokens dealt
+        # round-robin: the same dense SwiGLU with G times the work items
+        virtual = args.virtual or max(1, math.ceil(T / 16))
+        variants = [gen.shared_virtual_routing(T, virtual)[0]]
     else:
         variants = [gen.make_routing(name, T)[0]]
     banks = gen.make_banks(E, H, F, w["fused"], seed)
@@ -148,13 +156,23 @@ def build_inputs(args, torch, gen, moe):
             gate, up = moe.bank(g_, F * rbh), moe.bank(u_, F * rbh)
             keep = [g_, u_]
         d_ = t(banks["down"])
-        bank_sets.append((gate, up, moe.bank(d_, H * rbf), keep + [d_]))
+        down = moe.bank(d_, H * rbf)
+        keep.append(d_)
+        if virtual:
+            tabs = [torch.full((virtual,), b.base, dtype=torch.int64, device=dev)
+                    for b in (gate, up, down)]
+            gate, up, down = (moe.bank(None, 0, experts=tb) for tb in tabs)
+            keep += tabs
+        bank_sets.append((gate, up, down, keep))
     del banks
     ids_dev = [t(v.reshape(-1).astype(np.int32)) for v in variants]
-    uniq = [int(np.unique(v).size) for v in variants]
-    return dict(name=name, E=E, H=H, F=F, k=k, T=T, U=U, copies=copies, variants=variants,
-                ids=ids_dev, uniq=uniq, x=t(x), w=t(wts.reshape(-1)), bank_sets=bank_sets,
-                host=dict(x=x, w=wts))
+    uniq = [1] if virtual else [int(np.unique(v).size) for v in variants]
+    out = dict(name=name, E=virtual or E, H=H, F=F, k=k, T=T, U=U, copies=copies,
+               variants=variants, ids=ids_dev, uniq=uniq, x=t(x), w=t(wts.reshape(-1)),
+               bank_sets=bank_sets, host=dict(x=x, w=wts), virtual=virtual)
+    if virtual:   # the oracle takes the plain one-expert form
+        out.update(oracle_E=E, oracle_ids=np.zeros((T, 1), dtype=np.int32))
+    return out
 
 
 def main():
@@ -307,7 +325,8 @@ def main():
             "e256_plateau": f"rank-local E256 plateau: E={E} H={H} F={F} top-{k} T={T}",
             "skewed_prefill": f"skewed prefill: E={E} H={H} F={F} top-{k} T={T}",
             "full_prefill": f"full-width prefill: E={E} H={H} F={F} top-{k} T={T}",
-            "shared_expert": f"shared expert (dense SwiGLU, every token): H={H} F={F} T={T}"}[wl]
+            "shared_expert": f"shared expert (dense SwiGLU, every token): H={H} F={F} T={T}, "
+                             f"as {D['virtual']} virtual experts over its one weight copy"}[wl]
     out = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -438,9 +457,9 @@ def cpu_baseline(args, D, gen, unit, per_expert):
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(os.cpu_count() or 1, 16)
     name = D["name"]
     w = gen.WORKLOADS[name]
-    E, H, F, k, T = D["E"], D["H"], D["F"], D["k"], D["T"]
+    E, H, F, k, T = D.get("oracle_E", D["E"]), D["H"], D["F"], D["k"], D["T"]
     banks = gen.make_banks(E, H, F, w["fused"], w["seed"])
-    ids = D["variants"][0]
+    ids = D.get("oracle_ids", D["variants"][0])
     if T * k <= 160 or name != "skewed_prefill" and name != "full_prefill":
         tok = None
         sample = f"whole layer (all {T} tokens, {T * k} routed slots), union form"

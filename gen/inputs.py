@@ -246,6 +246,15 @@ def make_shared_case(seed: int, T: int, H: int, F: int, scales: str = "pow2"):
     return out
 
 
+def shared_virtual_routing(T: int, G: int):
+    """The shared expert's tokens dealt round-robin to G virtual experts (token t -> t mod G), one
+    slot each with router weight 1. With every virtual expert's bank rows pointing at the one
+    expert's copy (a per-expert pointer table), the routed layer computes the same dense SwiGLU,
+    with G times as many independent work items."""
+    ids = (np.arange(T, dtype=np.int32) % G).reshape(T, 1)
+    return ids, np.ones((T, 1), dtype=np.float32)
+
+
 def split_ff(case: dict, F1: int):
     """Split a separate-bank case along ff at F1 (a multiple of 64), as a tensor-parallel shard
     of the FFN would hold it: rows [0, F1) and [F1, F) of gate and up, and of each down row the

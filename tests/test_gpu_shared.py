@@ -45,3 +45,26 @@ def test_shared_expert_split_vs_full(T, F, F1):
     assert_parity(ya + yb, y, "shards summed vs full")
     rel, mx = parity(ya + yb, y)
     print(f"[split] relRMS {rel:.2e} max abs/RMS {mx:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("T,G", [(128, 8), (100, 7), (16, 16)])
+def test_shared_expert_virtual_experts(T, G):
+    """The shared expert as G virtual experts (tokens dealt round-robin, every virtual expert's
+    rows at the one weight copy through pointer tables) computes the one-expert layer bit for bit
+    on both paths: a token column's sums do not depend on which tokens share its tile."""
+    print(f"[case] shared virtual T={T} G={G}", flush=True)
+    case = gen.make_shared_case(500 + T, T, 2560, 320)
+    dc = DeviceCase(case)
+    ids, w = gen.shared_virtual_routing(T, G)
+    dv = DeviceCase(dict(case, E=G, ids=ids, w=w))
+    # dv's strided banks would address G experts in a one-expert allocation: replace them before
+    # any call with tables whose G entries all point at the one expert's rows
+    tabs = [torch.full((G,), b.base, dtype=torch.int64, device="cuda")
+            for b in (dv.gate, dv.up, dv.down)]
+    dv.gate, dv.up, dv.down = (moe.bank(None, 0, experts=tb) for tb in tabs)
+    ref = oracle.ffn_union(case)
+    for path in (moe.MOE_PATH_DECODE, moe.MOE_PATH_PREFILL):
+        y1 = dc.run(path)
+        yv = dv.run(path)
+        assert np.array_equal(yv, y1), f"virtual experts differ on path {path}"
+        assert_parity(yv, ref, f"shared virtual path {path}")
