@@ -43,6 +43,13 @@ TRAFFIC = {
         "sha256": "7d25a06425f08585f3a9cceb854efa8f898c2d20925880848a54d2d93c461e37",
         "fetch_kib": 54326.5, "write_kib": 171.6,
     },
+    # (`bench.py --workload full_prefill --steps 4 --warmup 1 --no-cpu-baseline`)
+    ("gemm_kernel<false>", "full_prefill", 4096, None): {
+        "sources": ["routed_moe_expert_amd/csrc/ffn_prefill.hip",
+                    "routed_moe_expert_amd/csrc/moe_internal.h"],
+        "sha256": "6a28cce44ef8130f6b5ba06796dd38f417e493b5b85c7ef7558393b468e073c9",
+        "fetch_kib": 1335311.0, "write_kib": 171952.8,
+    },
 }
 
 
@@ -301,8 +308,10 @@ def main():
     tr = measured_traffic(kname, D["name"], T, D["U"] if D["name"] == "verify_chunk" else None)
     roof["traffic"] = tr["bytes"] if tr else None
     if tr:
+        # prefill gate/up: the unique experts' gate and up weights, x (f16) once, h hi + lo
+        alg = gu_bytes if decode else uniq * 2 * F * rbh + T * H * 2 + P * F * 4
         roof["traffic_detail"] = tr
-        roof["traffic_over_algorithmic"] = tr["bytes"] / (gu_bytes if decode else float("nan"))
+        roof["traffic_over_algorithmic"] = tr["bytes"] / alg
 
     cpu = None
     if not args.no_cpu_baseline:
