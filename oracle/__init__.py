@@ -69,6 +69,8 @@ def _load():
         lib.orc_router_topk.restype = ctypes.c_int
         lib.orc_router_topk.argtypes = [_f32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                         _i32p, _f64p]
+        lib.orc_set_h_round.restype = None
+        lib.orc_set_h_round.argtypes = [ctypes.c_int32]
         lib.orc_ffn_union_s2.restype = ctypes.c_int
         lib.orc_ffn_union_s2.argtypes = [
             _u16p, _f32p, _i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -167,8 +169,27 @@ def _s2(case: dict):
     return ptrs, keep
 
 
-def ffn_per_slot(case: dict, tokens=None, threads: int = 0, expert_base: int | None = None):
-    """fp64 y[len(tokens), H] (all tokens when tokens is None), per-slot form."""
+H_ROUND = {"none": 0, "bf16": 1, "hi_lo": 2}
+
+
+class _HRound:
+    """Sets the oracle's diagnostic rounding of h for one call and restores the canonical mode
+    (h unrounded) afterwards, whatever happens."""
+
+    def __init__(self, lib, mode: str):
+        self.lib, self.mode = lib, H_ROUND[mode]
+
+    def __enter__(self):
+        self.lib.orc_set_h_round(self.mode)
+
+    def __exit__(self, *exc):
+        self.lib.orc_set_h_round(0)
+
+
+def ffn_per_slot(case: dict, tokens=None, threads: int = 0, expert_base: int | None = None,
+                 h_round: str = "none"):
+    """fp64 y[len(tokens), H] (all tokens when tokens is None), per-slot form. h_round is the
+    diagnostic rounding of the intermediate h: "none" (canonical), "bf16" or "hi_lo"."""
     lib = _load()
     x = np.ascontiguousarray(case["x"], dtype=np.uint16)
     w = np.ascontiguousarray(case["w"], dtype=np.float32)
@@ -184,16 +205,19 @@ def ffn_per_slot(case: dict, tokens=None, threads: int = 0, expert_base: int | N
         tok_p, n = _p(tok, _i64p), tok.size
     y = np.zeros((n, H), dtype=np.float64)
     s2, _keep = _s2(case)
-    rc = lib.orc_ffn_per_slot_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
-                                 _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds, *s2,
-                                 tok_p, n, _p(y, _f64p), threads)
+    with _HRound(lib, h_round):
+        rc = lib.orc_ffn_per_slot_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H,
+                                     F, _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds,
+                                     *s2, tok_p, n, _p(y, _f64p), threads)
     if rc:
         raise ValueError("orc_ffn_per_slot rejected its arguments")
     return y
 
 
-def ffn_union(case: dict, threads: int = 0, expert_base: int | None = None, want_h: bool = False):
-    """fp64 y[T, H], union form (optionally also h[T*k, F] for local pairs, NaN elsewhere)."""
+def ffn_union(case: dict, threads: int = 0, expert_base: int | None = None, want_h: bool = False,
+              h_round: str = "none"):
+    """fp64 y[T, H], union form (optionally also h[T*k, F] for local pairs, NaN elsewhere).
+    h_round as for ffn_per_slot."""
     lib = _load()
     x = np.ascontiguousarray(case["x"], dtype=np.uint16)
     w = np.ascontiguousarray(case["w"], dtype=np.float32)
@@ -205,9 +229,10 @@ def ffn_union(case: dict, threads: int = 0, expert_base: int | None = None, want
     y = np.zeros((T, H), dtype=np.float64)
     h = np.full((T * k, F), np.nan) if want_h else None
     s2, _keep = _s2(case)
-    rc = lib.orc_ffn_union_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
-                              _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds, *s2,
-                              _p(y, _f64p), _p(h, _f64p) if want_h else None, threads)
+    with _HRound(lib, h_round):
+        rc = lib.orc_ffn_union_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
+                                  _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds, *s2,
+                                  _p(y, _f64p), _p(h, _f64p) if want_h else None, threads)
     if rc:
         raise ValueError("orc_ffn_union rejected its arguments")
     return (y, h) if want_h else y

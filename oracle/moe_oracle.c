@@ -22,7 +22,8 @@
  *    the gate times the up value, the down projection, and the router-weighted sum over the
  *    token's k slots taken in ascending slot order (moe_union_probe.rs: the fused
  *    sel_gu_silu and sel_v3 kernels it names; moe_sk_repro.rs: gate, up and down grouped
- *    calls). Everything is fp64; the intermediate h is not rounded.
+ *    calls). Everything is fp64; the intermediate h is not rounded (a diagnostic switch,
+ *    orc_set_h_round, rounds it to bf16 or to a bf16 hi + lo pair instead).
  *
  *  - Second-level scales (the ModelOpt NVFP4 form the Rocket post's banks use): optionally one
  *    fp32 factor per expert and bank multiplies every weight of that expert's bank, so a weight
@@ -136,6 +137,33 @@ int orc_route_bucket(const int32_t *ids, int64_t T, int32_t k, int32_t E, int32_
 
 static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
+/* Diagnostic rounding of the intermediate h (a reading the pages leave open: how precisely the
+ * gate/up result is carried into the down projection). The canonical oracle keeps h unrounded
+ * (mode 0). Mode 1 rounds h to fp32 and then to bf16 (nearest, ties to even), as a pipeline
+ * storing h as one bf16 value would; mode 2 keeps the fp32 value as hi + lo, hi its bf16
+ * rounding and lo the bf16 rounding of the remainder. Process-wide; tests set and reset it. */
+static int g_h_round = 0;
+void orc_set_h_round(int32_t mode) { g_h_round = mode; }
+
+static double bf16_round(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static double round_h(double h)
+{
+    if (g_h_round == 0) return h;
+    const float f = (float)h;
+    const double hi = bf16_round(f);
+    if (g_h_round == 1) return hi;
+    /* f - hi is exact in fp32: both are fp32 values and hi agrees with f in its top 8 bits */
+    return hi + bf16_round((float)((double)f - hi));
+}
+
 /* One pair through one expert, from dense decoded matrices:
  * g = Wg x, u = Wu x, h = silu(g) * u, d = Wd h. Sums run in ascending index. */
 static void pair_ffn_dense(const double *x, const double *Wg, const double *Wu, const double *Wd,
@@ -145,7 +173,7 @@ static void pair_ffn_dense(const double *x, const double *Wg, const double *Wu, 
         double g = 0.0, u = 0.0;
         for (int32_t i = 0; i < H; i++) g += Wg[(int64_t)o * H + i] * x[i];
         for (int32_t i = 0; i < H; i++) u += Wu[(int64_t)o * H + i] * x[i];
-        h[o] = orc_silu(g) * u;
+        h[o] = round_h(orc_silu(g) * u);
     }
     for (int32_t r = 0; r < H; r++) {
         double s = 0.0;
@@ -179,7 +207,7 @@ static void pair_ffn_rowwise(const double *x, const uint8_t *gate, const uint8_t
         orc_dequant_rows(up + o * rbh, 1, H, row);
         scale_weights(row, H, su);
         for (int32_t i = 0; i < H; i++) u += row[i] * x[i];
-        h[o] = orc_silu(g) * u;
+        h[o] = round_h(orc_silu(g) * u);
     }
     for (int32_t r = 0; r < H; r++) {
         double s = 0.0;

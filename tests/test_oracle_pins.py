@@ -465,3 +465,51 @@ def test_second_level_scale_laws():
             c_r = dict(case, w=np.where(case["ids"] != e, case["w"], 0).astype(np.float32))
             y_e, y_r = oracle.ffn_union(c_e), oracle.ffn_union(c_r)
             assert _rel(y2, pw[e] * y_e + y_r) < 1e-12
+
+
+# ------------------------------------------------------------------ rounding of h (diagnostic)
+# The pages leave open how precisely h reaches the down projection. The canonical oracle keeps it
+# unrounded; its diagnostic modes round it to bf16 or to a bf16 hi + lo pair. Pinned to torch's
+# float32 -> bfloat16 casts applied to the oracle's own unrounded h, and to an independently
+# decoded down projection.
+
+@pytest.mark.parametrize("mode", ["bf16", "hi_lo"])
+def test_h_round_modes_match_torch_rounding(golden_dir, mode):
+    tab = _e2m1_golden(golden_dir)
+    E, H, F, k = 3, 128, 64, 2
+    case = gen.make_random_case(12, T=5, k=k, E=E, H=H, F=F, scales="all")
+    y0, h = oracle.ffn_union(case, want_h=True)
+    y = oracle.ffn_union(case, h_round=mode)
+    f32 = torch.tensor(h).to(torch.float32)
+    hi = f32.to(torch.bfloat16).to(torch.float32)
+    hr = hi.to(torch.float64)
+    if mode == "hi_lo":
+        hr = hr + (f32 - hi).to(torch.bfloat16).to(torch.float64)
+    hr = hr.numpy()
+    Wd = [_decode_independent(case["down"][e], F, tab) for e in range(E)]
+    ref = np.zeros((5, H))
+    for t in range(5):
+        for j in range(k):
+            ref[t] += float(case["w"][t, j]) * (Wd[int(case["ids"][t, j])] @ hr[t * k + j])
+    assert _rel(y, ref) < 1e-12
+    assert not np.array_equal(y, y0)
+    assert np.array_equal(oracle.ffn_union(case), y0)          # canonical mode restored
+    assert np.array_equal(oracle.ffn_per_slot(case, h_round=mode), y)
+
+
+def test_single_bf16_h_fails_the_parity_bound():
+    """Why h stays wider than one bf16 value: rounding it to bf16 moves y by relRMS ~1.7e-3 and
+    max ~1.5e-2 * RMS(y), beyond the bound (relRMS 1e-3, max 2e-3 * RMS); a bf16 hi + lo pair
+    moves it by ~2.4e-6 and ~2.5e-5, far inside."""
+    case = gen.make_random_case(7, T=32, k=4, E=8, H=1024, F=512, scales="all")
+    y0 = oracle.ffn_union(case)
+    rms = np.sqrt(np.mean(y0 ** 2))
+
+    def err(y):
+        e = y - y0
+        return np.sqrt(np.mean(e ** 2)) / rms, np.abs(e).max() / rms
+
+    rel, mx = err(oracle.ffn_union(case, h_round="bf16"))
+    assert rel > 1e-3 and mx > 2e-3
+    rel, mx = err(oracle.ffn_union(case, h_round="hi_lo"))
+    assert rel < 1e-4 and mx < 2e-4
