@@ -346,6 +346,7 @@ def main():
                    "hbm": hbm_note},
         "layer": layer,
         "unique_expert_bytes": unique_bytes,
+        "per_slot_bytes": P * per_expert,   # what a per-slot path would stream
         "hbm_frac_unique": (unique_bytes / s / 1e9) / HBM_PEAK_GBS,
         "useful_tflops": useful_flops / s / 1e12,
         "roofline": roof,
@@ -488,13 +489,27 @@ def cpu_baseline(args, D, gen, unit, per_expert):
         if el >= args.cpu_seconds or el * (reps + 1) / reps > 30.0:
             break
     sec = el / reps
-    if unit == "GB/s":
-        v = len(np.unique(ids)) * per_expert / sec / 1e9
+
+    def rate(sec_, ids_, n_pairs):
+        if unit == "GB/s":
+            return len(np.unique(ids_)) * per_expert / sec_ / 1e9
+        return 6.0 * n_pairs * H * F / sec_ / 1e12
+
+    v = rate(sec, ids, T * k if tok is None else len(tok) * k)
+    # one thread, on the first token's slots (same form as above), once
+    t1 = time.perf_counter()
+    if tok is None:
+        one = dict(case, T=1, ids=ids[:1], w=D["host"]["w"][:1], x=D["host"]["x"][:1])
+        oracle.ffn_union(one, threads=1)
     else:
-        n_pairs = T * k if tok is None else len(tok) * k
-        v = 6.0 * n_pairs * H * F / sec / 1e12
+        oracle.ffn_per_slot(case, tokens=np.arange(1), threads=1)
+    sec1 = time.perf_counter() - t1
+    single = {"value": rate(sec1, ids[:1], k), "cores": 1,
+              "sample": f"the first token ({k} routed slots), "
+                        f"{'union' if tok is None else 'per-slot'} form, once",
+              "seconds_per_sample": sec1}
     return {"value": v, "unit": unit, "cores": threads, "kind": "oracle", "sample": sample,
-            "seconds_per_sample": sec, "reps": reps}
+            "seconds_per_sample": sec, "reps": reps, "single_thread": single}
 
 
 if __name__ == "__main__":
