@@ -40,8 +40,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "7d25a06425f08585f3a9cceb854efa8f898c2d20925880848a54d2d93c461e37",
-        "fetch_kib": 54326.5, "write_kib": 171.6,
+        "sha256": "e7a723f1467c7a4b04c79c0b729cb65f901f1608de4f57ce3edf8f7762b65dda",
+        "fetch_kib": 54326.5, "write_kib": 169.0,
     },
     # (`bench.py --workload full_prefill --steps 4 --warmup 1 --no-cpu-baseline`)
     ("gemm_kernel<false>", "full_prefill", 4096, None): {
