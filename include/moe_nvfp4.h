@@ -134,11 +134,12 @@ size_t moe_ffn_nvfp4_ws(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
  *   offsets, pair_ids, active, counts  (device) exactly as moe_route_bucket wrote them for the
  *                      same topk_ids, T, k, E.
  *   gate, up  rows of H weights: expert e's gate row o (o < F) starts at
- *                      gate.base + e*gate.expert_stride + o*(H/64*36); likewise up. A fused
+ *                      gate.base + e*gate.expert_stride + o*(H/64*36) (gate.experts[e] +
+ *                      o*(H/64*36) for a bank given as a pointer table); likewise up. A fused
  *                      gate_up bank [E, 2F, H] with gate rows first is gate = {B, 2F*rb},
  *                      up = {B + F*rb, 2F*rb}, rb = H/64*36.
  *   down      rows of F weights: expert e's down row r (r < H) starts at
- *                      down.base + e*down.expert_stride + r*(F/64*36).
+ *                      down.base + e*down.expert_stride + r*(F/64*36) (or down.experts[e] + ...).
  *   y         (device, out) fp32 [T, H], fully overwritten; a token with no local slot gets 0.
  *   path      MOE_PATH_AUTO / MOE_PATH_DECODE / MOE_PATH_PREFILL.
  *   ws, ws_bytes (device) scratch of at least moe_ffn_nvfp4_ws(T, k, E, H, F) bytes.
