@@ -47,8 +47,8 @@ TRAFFIC = {
     ("gemm_kernel<false>", "full_prefill", 4096, None): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_prefill.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "6a28cce44ef8130f6b5ba06796dd38f417e493b5b85c7ef7558393b468e073c9",
-        "fetch_kib": 1335311.0, "write_kib": 171952.8,
+        "sha256": "faa674bc3b45a1d3ac93801fa75855425e55c45c2b9b495e671e2cc1fbfec7a8",
+        "fetch_kib": 1339114.5, "write_kib": 175615.4,
     },
 }
 

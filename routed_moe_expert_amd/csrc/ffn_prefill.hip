@@ -300,11 +300,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         asrc[i] = base + 12 * (u % 3);
     }
     const int a_loads = ((kALoadsMax - 1) * kWaves + wave) * 64 < kAUnits ? kALoadsMax : kALoadsMax - 1;
-    // B: lane loads 16-byte units u = (i*kWaves + wave)*64 + lane of each operand
+    // B: lane loads 16-byte units u = (i*kWaves + wave)*64 + lane of each operand, i.e. rows
+    // 8 (i*kWaves + wave) .. +7 of the tile. Rows past the tile (r >= mt) are not loaded: their
+    // columns are never stored. A load whose 8 rows all lie past the tile is not issued at all,
+    // so a wave's loads per step (ops below) are the same at every step.
     const uint16_t *bsrc[kNB][kBUnits];
+    bool b_on[kBUnits], b_lane[kBUnits];
+    int b_loads = 0;
 #pragma unroll
     for (int i = 0; i < kBUnits; i++) {
         const int u = (i * kWaves + wave) * 64 + lane;
+        b_on[i] = (i * kWaves + wave) * 8 < mt;   // wave-uniform
+        b_lane[i] = (u >> 3) < mt;
+        b_loads += b_on[i] ? 1 : 0;
         const int r = u >> 3, p = (u & 7) ^ (r & 7);
         const int64_t off = (int64_t)rowid[r] * (DOWN ? F : H) + 8 * p;
         if (DOWN) {
@@ -324,9 +332,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         for (int o = 0; o < kNB; o++)
 #pragma unroll
             for (int i = 0; i < kBUnits; i++)
-                dma16(bsrc[o][i] + kb * 64, st + kABytes + o * kBBytesW + (i * kWaves + wave) * 1024);
+                if (b_on[i] && b_lane[i])
+                    dma16(bsrc[o][i] + kb * 64, st + kABytes + o * kBBytesW + (i * kWaves + wave) * 1024);
     };
-    const int ops = a_loads + kNB * kBUnits;   // loads per step of this wave
+    const int ops = a_loads + kNB * b_loads;   // loads per step of this wave
 
     // operands are f16: weights decoded to f16; x cast per token by xcast_kernel (gate/up), h as
     // f16 hi + lo scaled per (pair, 256-feature segment) by the gate/up epilogue (down)
