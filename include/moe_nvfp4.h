@@ -59,7 +59,7 @@ enum {
 enum {
     MOE_PATH_AUTO = 0,          /* decode path for T <= 128, grouped-GEMM prefill path above */
     MOE_PATH_DECODE = 1,        /* force the bandwidth-bound decode path */
-    MOE_PATH_PREFILL = 2        /* force the bf16-MFMA grouped-GEMM path */
+    MOE_PATH_PREFILL = 2        /* force the grouped-GEMM path (f16 MFMA) */
 };
 
 #define MOE_MAX_EXPERTS 2048       /* E limit of the bucketing kernel */
