@@ -25,7 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed-MoE layer µs + HBM GB/s (% of 8 TB/s) at T=1..128; TFLOP/s at T=4096"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense MFMA, f16 and bf16 alike (the GEMMs run f16)
 COPY_BYTES = 1 << 30
 
 # HBM traffic of the dominant kernel, per launch, from two rocprofv3 --pmc passes over
