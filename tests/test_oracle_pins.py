@@ -267,6 +267,57 @@ def test_ffn_single_expert_is_dense_swiglu(golden_dir):
     assert _rel(y, ref) < 1e-12
 
 
+def _brute_force_layer(case, e2m1_tab):
+    """The layer with plain Python scalars, one weight at a time: weight i of a row is the E2M1
+    nibble (low nibble for even i) of byte 4 + (i % 64) / 2 of its 36-byte block, times the
+    UE4M3 scale byte (i % 64) / 16 of that block (2^(e-7) (1 + m/8), or m 2^-9 for e = 0)."""
+    import math
+    import struct
+
+    E, H, F, k, T = case["E"], case["H"], case["F"], case["k"], case["T"]
+
+    def weight(row, i):
+        blk = (i // 64) * 36
+        s = int(row[blk + (i % 64) // 16])
+        e, m = s >> 3, s & 7
+        scale = m * 2.0 ** -9 if e == 0 else 2.0 ** (e - 7) * (1 + m / 8)
+        byte = int(row[blk + 4 + (i % 64) // 2])
+        code = byte & 15 if i % 2 == 0 else byte >> 4
+        return float(e2m1_tab[code]) * scale
+
+    def bf16(bits):
+        return struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0]
+
+    y = [[0.0] * H for _ in range(T)]
+    for t in range(T):
+        x = [bf16(b) for b in case["x"][t]]
+        for j in range(k):
+            e = int(case["ids"][t, j])
+            if not 0 <= e < E:
+                continue
+            h = []
+            for o in range(F):
+                g = sum(weight(case["gate"][e, o], i) * x[i] for i in range(H))
+                u = sum(weight(case["up"][e, o], i) * x[i] for i in range(H))
+                # SiLU without overflow: z / (1 + e^-z) for z >= 0, z e^z / (1 + e^z) below
+                sg = g / (1.0 + math.exp(-g)) if g >= 0 else g * math.exp(g) / (1.0 + math.exp(g))
+                h.append(sg * u)
+            for r in range(H):
+                d = sum(weight(case["down"][e, r], o) * h[o] for o in range(F))
+                y[t][r] += float(case["w"][t, j]) * d
+    return np.array(y)
+
+
+def test_ffn_matches_scalar_brute_force(golden_dir):
+    """T <= 4, E <= 4, H = F = 64, with duplicates and scales over every finite UE4M3 code."""
+    tab = _e2m1_golden(golden_dir)
+    case = gen.make_random_case(17, T=3, k=3, E=3, H=64, F=64, scales="all")
+    ref = _brute_force_layer(case, tab)
+    assert np.abs(ref).max() > 0
+    assert _rel(oracle.ffn_union(case), ref) < 1e-12
+    assert _rel(oracle.ffn_per_slot(case), ref) < 1e-12
+
+
 def test_union_equals_per_slot_bitwise():
     case = gen.make_random_case(21, T=9, k=4, E=6, H=128, F=128, scales="all", nonlocal_frac=0.1)
     assert np.array_equal(oracle.ffn_per_slot(case), oracle.ffn_union(case))
