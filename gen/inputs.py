@@ -22,6 +22,7 @@ NVFP4_SCALES_PER_BLOCK = 4
 S_GATE, S_UP, S_DOWN, S_GATEUP, S_X, S_ROUTE, S_LOGITS, S_PERM = 1, 2, 3, 4, 5, 6, 7, 8
 S_RLOGITS = 9
 S_S2 = 10
+S_SKEW = 11
 
 
 def rng_for(seed: int, stream: int, sub: int = 0) -> np.random.Generator:
@@ -138,22 +139,13 @@ def route_cyclic(seed: int, T: int, k: int, E: int) -> np.ndarray:
     return pi[p % E].astype(np.int32).reshape(T, k)
 
 
-_M64 = np.uint64(0xFFFFFFFFFFFFFFFF)
-
-
-def route_skewed(T: int, k: int, E: int) -> np.ndarray:
-    """The moe_sk_repro probe's deterministic skewed router, pair p = t*k + j:
-    a 64-bit multiply/xor-shift mix of p gives u in [0,1) from its top 53 bits, and the
-    expert is min(floor(u^1.35 * E), E-1). Pure function of p; no seed."""
-    p = np.arange(T * k, dtype=np.uint64)
-    with np.errstate(over="ignore"):
-        h = p * np.uint64(0x9E3779B97F4A7C15)
-        h ^= h >> np.uint64(29)
-        h = h * np.uint64(0xBF58476D1CE4E5B9)
-        h ^= h >> np.uint64(32)
-    u = (h >> np.uint64(11)).astype(np.float64) / float(1 << 53)
-    x = np.power(u, 1.35)
-    e = np.minimum((x * E).astype(np.int64), E - 1)
+def route_skewed(T: int, k: int, E: int, seed: int = 0) -> np.ndarray:
+    """Skewed routing of the moe_sk_repro probe's prefill workload: pair p = t*k + j goes to
+    expert min(floor(u_p^1.35 * E), E - 1), u_p uniform in [0, 1). u_p is the p-th double of a
+    Philox stream (53 bits of its p-th 64-bit output), i.e. a counter-based 64-bit hash of p:
+    a pure function of (seed, p), so a longer batch extends a shorter one."""
+    u = rng_for(seed, S_SKEW).random(T * k)
+    e = np.minimum(np.floor(np.power(u, 1.35) * E).astype(np.int64), E - 1)
     return e.astype(np.int32).reshape(T, k)
 
 

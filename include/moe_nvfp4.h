@@ -48,8 +48,8 @@ typedef struct ihipStream_t *moe_stream_t; /* a hipStream_t; NULL is the default
 /* Status codes. */
 enum {
     MOE_OK = 0,
-    MOE_EINVAL = 1,  /* null pointer, negative T, k<1, E<1, k>4096, H or F not a multiple of 64,
-                        H not a multiple of 256, bank base or stride not a multiple of 16 bytes */
+    MOE_EINVAL = 1,  /* null pointer, negative T, k<1, E<1, k>4096, H or F not a positive
+                        multiple of 64, bank base or stride not a multiple of 16 bytes */
     MOE_EWS = 2,     /* workspace smaller than the matching *_ws() size */
     MOE_ESHAPE = 3,  /* a size beyond what this build can launch (see MOE_MAX_*) */
     MOE_ELAUNCH = 4  /* the HIP runtime reported an error when the work was enqueued */

@@ -71,11 +71,12 @@ def _load():
                                         _i32p, _f64p]
         lib.orc_set_h_round.restype = None
         lib.orc_set_h_round.argtypes = [ctypes.c_int32]
-        lib.orc_ffn_union_s2.restype = ctypes.c_int
-        lib.orc_ffn_union_s2.argtypes = [
+        lib.orc_ffn_union_sel_s2.restype = ctypes.c_int
+        lib.orc_ffn_union_sel_s2.argtypes = [
             _u16p, _f32p, _i32p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
             ctypes.c_int32, ctypes.c_int32, _u8p, ctypes.c_int64, _u8p, ctypes.c_int64, _u8p,
-            ctypes.c_int64, _f32p, _f32p, _f32p, _f64p, _f64p, ctypes.c_int32]
+            ctypes.c_int64, _f32p, _f32p, _f32p, _i64p, ctypes.c_int64, _f64p, _f64p,
+            ctypes.c_int32]
         _lib = lib
     return _lib
 
@@ -215,9 +216,10 @@ def ffn_per_slot(case: dict, tokens=None, threads: int = 0, expert_base: int | N
 
 
 def ffn_union(case: dict, threads: int = 0, expert_base: int | None = None, want_h: bool = False,
-              h_round: str = "none"):
-    """fp64 y[T, H], union form (optionally also h[T*k, F] for local pairs, NaN elsewhere).
-    h_round as for ffn_per_slot."""
+              h_round: str = "none", tokens=None):
+    """fp64 y[T, H], union form (optionally also h[T*k, F] for computed local pairs, NaN
+    elsewhere). tokens: compute only these tokens' pairs and return their rows y[len(tokens), H]
+    (each bit for bit as in the full layer). h_round as for ffn_per_slot."""
     lib = _load()
     x = np.ascontiguousarray(case["x"], dtype=np.uint16)
     w = np.ascontiguousarray(case["w"], dtype=np.float32)
@@ -226,13 +228,19 @@ def ffn_union(case: dict, threads: int = 0, expert_base: int | None = None, want
     E, H, F = case["E"], case["H"], case["F"]
     eb = case.get("expert_base", 0) if expert_base is None else expert_base
     gate, gs, up, us, down, ds = bank_views(case)
-    y = np.zeros((T, H), dtype=np.float64)
+    if tokens is None:
+        tok_p, n = None, T
+    else:
+        tok = np.ascontiguousarray(tokens, dtype=np.int64)
+        tok_p, n = _p(tok, _i64p), tok.size
+    y = np.zeros((n, H), dtype=np.float64)
     h = np.full((T * k, F), np.nan) if want_h else None
     s2, _keep = _s2(case)
     with _HRound(lib, h_round):
-        rc = lib.orc_ffn_union_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H, F,
-                                  _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p), ds, *s2,
-                                  _p(y, _f64p), _p(h, _f64p) if want_h else None, threads)
+        rc = lib.orc_ffn_union_sel_s2(_p(x, _u16p), _p(w, _f32p), _p(ids, _i32p), T, k, E, eb, H,
+                                      F, _p(gate, _u8p), gs, _p(up, _u8p), us, _p(down, _u8p),
+                                      ds, *s2, tok_p, n, _p(y, _f64p),
+                                      _p(h, _f64p) if want_h else None, threads)
     if rc:
         raise ValueError("orc_ffn_union rejected its arguments")
     return (y, h) if want_h else y

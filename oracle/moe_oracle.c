@@ -282,11 +282,100 @@ int orc_ffn_per_slot(const uint16_t *x_bf16, const float *topk_w, const int32_t 
 }
 
 /*
- * Union form over all T tokens: bucket the pairs, decode each active expert once, run every
- * pair of its bucket, then combine each token's slots in ascending slot order. y[T][H] fp64.
- * If h_out is not NULL it receives h[p][F] for every local pair p (rows of non-local pairs are
- * left untouched).
+ * Union form: bucket the pairs, decode each active expert once, run every pair of its bucket,
+ * then combine each token's slots in ascending slot order.
+ * tokens (NULL: all T tokens, n_tokens must equal T) selects the tokens whose y rows are wanted;
+ * only the pairs of those tokens are computed, each exactly as in the full layer, and
+ * y[n][H] (fp64) receives token tokens[n]. If h_out is not NULL it receives h[p][F] for every
+ * computed local pair p (other rows are left untouched).
+ * The active experts are shared out over the threads, each decoding its experts into buffers of
+ * its own; a pair's arithmetic (and so every bit of y) does not depend on the thread count.
  */
+int orc_ffn_union_sel_s2(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids,
+                         int64_t T, int32_t k, int32_t E, int32_t expert_base, int32_t H,
+                         int32_t F, const uint8_t *gate, int64_t gate_stride, const uint8_t *up,
+                         int64_t up_stride, const uint8_t *down, int64_t down_stride,
+                         const float *gate_s2, const float *up_s2, const float *down_s2,
+                         const int64_t *tokens, int64_t n_tokens, double *y, double *h_out,
+                         int32_t n_threads)
+{
+    if (T < 0 || k < 1 || E < 1 || H % 64 || F % 64 || H < 64 || F < 64) return -1;
+    if (!tokens && n_tokens != T) return -1;
+    set_threads(n_threads);
+    int64_t P = T * k;
+    int32_t *offsets = malloc(sizeof(int32_t) * (size_t)(E + 1));
+    int32_t *pair_ids = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+    int32_t *active = malloc(sizeof(int32_t) * (size_t)E);
+    int32_t counts[2];
+    char *want = calloc((size_t)(T > 0 ? T : 1), 1);        /* token t's y row is wanted */
+    int64_t *row_of = malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));  /* its D row block */
+    double *D = NULL;
+    char *has = calloc((size_t)(P > 0 ? P : 1), 1);
+    int rc = -1, bad = 0;
+    if (!offsets || !pair_ids || !active || !want || !row_of || !has) goto out;
+    for (int64_t n = 0; n < n_tokens; n++) {
+        int64_t t = tokens ? tokens[n] : n;
+        if (t < 0 || t >= T) goto out;
+        if (!want[t]) row_of[t] = n;   /* a token listed twice takes its first row */
+        want[t] = 1;
+    }
+    /* D[(row_of[t]) * k + j][H]: the down output of slot j of a wanted token */
+    D = calloc((size_t)(n_tokens > 0 ? n_tokens : 1) * (size_t)k * (size_t)H, sizeof(double));
+    if (!D) goto out;
+    if (orc_route_bucket(ids, T, k, E, expert_base, offsets, pair_ids, active, counts)) goto out;
+#pragma omp parallel reduction(| : bad)
+    {
+        double *Wg = malloc(sizeof(double) * (size_t)F * H);
+        double *Wu = malloc(sizeof(double) * (size_t)F * H);
+        double *Wd = malloc(sizeof(double) * (size_t)H * F);
+        double *xr = malloc(sizeof(double) * (size_t)H);
+        double *h = malloc(sizeof(double) * (size_t)F);
+        if (!Wg || !Wu || !Wd || !xr || !h) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t a = 0; a < counts[0]; a++) {
+            if (!Wg || !Wu || !Wd || !xr || !h) continue;
+            int32_t e = active[a];
+            int32_t b0 = offsets[e], b1 = offsets[e + 1], needed = 0;
+            for (int32_t q = b0; q < b1; q++) needed |= want[pair_ids[q] / k];
+            if (!needed) continue;
+            orc_dequant_rows(gate + e * gate_stride, F, H, Wg);
+            orc_dequant_rows(up + e * up_stride, F, H, Wu);
+            orc_dequant_rows(down + e * down_stride, H, F, Wd);
+            scale_weights(Wg, (int64_t)F * H, s2_of(gate_s2, e));
+            scale_weights(Wu, (int64_t)F * H, s2_of(up_s2, e));
+            scale_weights(Wd, (int64_t)H * F, s2_of(down_s2, e));
+            for (int32_t q = b0; q < b1; q++) {
+                int64_t p = pair_ids[q], t = p / k;
+                if (!want[t]) continue;
+                for (int32_t i = 0; i < H; i++) xr[i] = orc_bf16(x_bf16[t * H + i]);
+                pair_ffn_dense(xr, Wg, Wu, Wd, H, F, h, D + (row_of[t] * k + p % k) * H);
+                if (h_out) memcpy(h_out + p * F, h, sizeof(double) * (size_t)F);
+                has[p] = 1;
+            }
+        }
+        free(Wg); free(Wu); free(Wd); free(xr); free(h);
+    }
+    if (bad) goto out;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_tokens; n++) {
+        int64_t t = tokens ? tokens[n] : n;
+        double *yr = y + n * H;
+        for (int32_t r = 0; r < H; r++) yr[r] = 0.0;
+        for (int32_t j = 0; j < k; j++) {
+            int64_t p = t * k + j;
+            if (!has[p]) continue;
+            double wt = (double)topk_w[p];
+            const double *d = D + (row_of[t] * k + j) * H;
+            for (int32_t r = 0; r < H; r++) yr[r] += wt * d[r];
+        }
+    }
+    rc = 0;
+out:
+    free(offsets); free(pair_ids); free(active); free(want); free(row_of); free(D); free(has);
+    return rc;
+}
+
+/* All T tokens. */
 int orc_ffn_union_s2(const uint16_t *x_bf16, const float *topk_w, const int32_t *ids, int64_t T,
                      int32_t k, int32_t E, int32_t expert_base, int32_t H, int32_t F,
                      const uint8_t *gate, int64_t gate_stride, const uint8_t *up,
@@ -294,57 +383,9 @@ int orc_ffn_union_s2(const uint16_t *x_bf16, const float *topk_w, const int32_t 
                      const float *gate_s2, const float *up_s2, const float *down_s2, double *y,
                      double *h_out, int32_t n_threads)
 {
-    if (T < 0 || k < 1 || E < 1 || H % 64 || F % 64 || H < 64 || F < 64) return -1;
-    set_threads(n_threads);
-    int64_t P = T * k;
-    int32_t *offsets = malloc(sizeof(int32_t) * (size_t)(E + 1));
-    int32_t *pair_ids = malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
-    int32_t *active = malloc(sizeof(int32_t) * (size_t)E);
-    int32_t counts[2];
-    double *D = calloc((size_t)(P > 0 ? P : 1) * (size_t)H, sizeof(double));
-    char *has = calloc((size_t)(P > 0 ? P : 1), 1);
-    double *Wg = malloc(sizeof(double) * (size_t)F * H);
-    double *Wu = malloc(sizeof(double) * (size_t)F * H);
-    double *Wd = malloc(sizeof(double) * (size_t)H * F);
-    int rc = -1;
-    if (!offsets || !pair_ids || !active || !D || !has || !Wg || !Wu || !Wd) goto out;
-    if (orc_route_bucket(ids, T, k, E, expert_base, offsets, pair_ids, active, counts)) goto out;
-    for (int32_t a = 0; a < counts[0]; a++) {
-        int32_t e = active[a];
-        orc_dequant_rows(gate + e * gate_stride, F, H, Wg);
-        orc_dequant_rows(up + e * up_stride, F, H, Wu);
-        orc_dequant_rows(down + e * down_stride, H, F, Wd);
-        scale_weights(Wg, (int64_t)F * H, s2_of(gate_s2, e));
-        scale_weights(Wu, (int64_t)F * H, s2_of(up_s2, e));
-        scale_weights(Wd, (int64_t)H * F, s2_of(down_s2, e));
-        int32_t b0 = offsets[e], b1 = offsets[e + 1];
-#pragma omp parallel for schedule(dynamic, 1)
-        for (int32_t q = b0; q < b1; q++) {
-            int64_t p = pair_ids[q], t = p / k;
-            double *xr = malloc(sizeof(double) * (size_t)H);
-            double *h = malloc(sizeof(double) * (size_t)F);
-            for (int32_t i = 0; i < H; i++) xr[i] = orc_bf16(x_bf16[t * H + i]);
-            pair_ffn_dense(xr, Wg, Wu, Wd, H, F, h, D + p * H);
-            if (h_out) memcpy(h_out + p * F, h, sizeof(double) * (size_t)F);
-            has[p] = 1;
-            free(xr); free(h);
-        }
-    }
-#pragma omp parallel for schedule(static)
-    for (int64_t t = 0; t < T; t++) {
-        double *yr = y + t * H;
-        for (int32_t r = 0; r < H; r++) yr[r] = 0.0;
-        for (int32_t j = 0; j < k; j++) {
-            int64_t p = t * k + j;
-            if (!has[p]) continue;
-            double wt = (double)topk_w[p];
-            for (int32_t r = 0; r < H; r++) yr[r] += wt * D[p * H + r];
-        }
-    }
-    rc = 0;
-out:
-    free(offsets); free(pair_ids); free(active); free(D); free(has); free(Wg); free(Wu); free(Wd);
-    return rc;
+    return orc_ffn_union_sel_s2(x_bf16, topk_w, ids, T, k, E, expert_base, H, F, gate,
+                                gate_stride, up, up_stride, down, down_stride, gate_s2, up_s2,
+                                down_s2, NULL, T, y, h_out, n_threads);
 }
 
 /* Without second-level scales. */

@@ -111,9 +111,15 @@ def moe_route_bucket(topk_ids, T: int, k: int, E: int, expert_base: int, offsets
 def bank(base, expert_stride: int, byte_offset: int = 0, scale2=None, experts=None) -> moe_bank:
     """A moe_bank for a device tensor (or address) plus an optional byte offset, and optionally
     the bank's per-expert fp32 second-level scales (a device tensor of E floats) and a per-expert
-    pointer table (a device int64 tensor of E addresses; base and expert_stride are then unused)."""
-    return moe_bank(_ptr(base) + byte_offset if base is not None else None, int(expert_stride),
-                    _ptr(scale2) or None, _ptr(experts) or None)
+    pointer table (a device int64 tensor of E addresses; base and expert_stride are then unused).
+
+    The bank holds raw addresses, so it also keeps a reference to every tensor it was given
+    (`_keep`): their memory cannot be freed and reused while the bank object is alive. Addresses
+    passed as ints are the caller's to keep valid."""
+    b = moe_bank(_ptr(base) + byte_offset if base is not None else None, int(expert_stride),
+                 _ptr(scale2) or None, _ptr(experts) or None)
+    b._keep = tuple(t for t in (base, scale2, experts) if t is not None and not isinstance(t, int))
+    return b
 
 
 def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, up: moe_bank,

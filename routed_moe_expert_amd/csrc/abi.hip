@@ -61,7 +61,7 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
                   moe_stream_t stream) {
     int st = check_common(T, k, E);
     if (st != MOE_OK) return st;
-    if (H < 256 || F < 64 || H % 256 || F % 64) return MOE_EINVAL;
+    if (H < 64 || F < 64 || H % 64 || F % 64) return MOE_EINVAL;
     if (H > MOE_MAX_HIDDEN || F > MOE_MAX_FF) return MOE_ESHAPE;
     if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_EINVAL;
     if (T == 0) return MOE_OK;

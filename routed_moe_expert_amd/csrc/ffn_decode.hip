@@ -298,13 +298,15 @@ __device__ __forceinline__ void item_range(int n_active, int tiles, int &i0, int
 }
 
 // Gate/up tile layout in LDS: 16 rows (8 gate, then the 8 matching up rows), one per lane row of
-// the MFMA tile, each lane reading its own row. Rows are whole 16-byte chunks (hidden is a
-// multiple of 256) and sit one chunk further apart than their length. For hidden 2560 (1440-byte
-// rows, 360 dwords: 8 past a multiple of the 32 LDS banks) the same byte of rows n and n + 4
-// would fall in one bank; at a 1456-byte pitch only rows n and n + 8 share one, which halves the
-// bank conflicts of the reads. The pad chunk is filled with a copy of the row's first chunk, so
-// each direct-to-LDS load still moves 64 whole chunks.
-__host__ __device__ inline int gu_pitch(int rb) { return rb + 16; }
+// the MFMA tile, each lane reading its own row. When a row is whole 16-byte chunks (hidden a
+// multiple of 256) the rows sit one chunk further apart than their length: for hidden 2560
+// (1440-byte rows, 360 dwords: 8 past a multiple of the 32 LDS banks) the same byte of rows n and
+// n + 4 would fall in one bank; at a 1456-byte pitch only rows n and n + 8 share one, which halves
+// the bank conflicts of the reads. The pad chunk is filled with a copy of the row's first chunk,
+// so each direct-to-LDS load still moves 64 whole chunks. Otherwise (hidden a multiple of 64
+// only) the 8 gate rows and the 8 up rows are each one contiguous 16-byte aligned run
+// (8 rows = 4.5 hidden bytes) and land unpadded, pitch = row length.
+__host__ __device__ inline int gu_pitch(int rb) { return rb % 16 == 0 ? rb + 16 : rb; }
 constexpr int kMaxTileInst = 10;   // loads per wave for one padded tile (hidden <= 4096)
 
 __device__ __forceinline__ void dma16(const void *g, void *lds) {
@@ -436,23 +438,32 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;   // A row / B column, and K group
-    const int nblk = H / kBlockWeights, blk0 = wave * NB;   // slices are whole: nblk = 4 NB
+    // K slices of NB blocks; a last slice may run past the row (reads clamp, operands zero)
+    const int nblk = H / kBlockWeights, blk0 = wave * NB;
     const int tiles = F / kGuO;
 
     int i0, i1, a_first;
     load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, gate,
               gate_stride, gate_tab, gate_s2, up, up_stride, up_tab, up_s2, E, P, tiles, i0, i1,
               a_first);
-    // load k of this wave moves LDS chunk p = 64 wave + 256 k + lane of the tile,
-    // row p / cpr, chunk p % cpr of it (the last one a copy of chunk 0); its source offset within
-    // the gate or up rows of the tile (sign bit: up) is the same for every tile
-    const int cpr = rb / 16 + 1, units = 2 * kGuO * cpr;
+    // load k of this wave moves LDS chunk p = 64 wave + 256 k + lane of the tile; its source
+    // offset within the gate or up rows of the tile (sign bit: up) is the same for every tile.
+    // Padded pitch: chunk p is chunk p % cpr of row p / cpr (the last one a copy of chunk 0).
+    // Unpadded: chunk p is chunk p of the 8 gate rows' run, then of the 8 up rows' run.
+    const bool padded = pitch != rb;
+    const int cpr = rb / 16 + 1, half = kGuO * rb / 16;
+    const int units = padded ? 2 * kGuO * cpr : 2 * half;
     int32_t src_off[kMaxTileInst];
 #pragma unroll
     for (int kk = 0; kk < kMaxTileInst; kk++) {
-        const int p = wave * 64 + kk * kThreads + lane, r = p / cpr, c = p - r * cpr;
-        src_off[kk] = ((r & (kGuO - 1)) * rb + (c == cpr - 1 ? 0 : c) * 16) |
-                      (r >= kGuO ? (int32_t)0x80000000 : 0);
+        const int p = wave * 64 + kk * kThreads + lane;
+        if (padded) {
+            const int r = p / cpr, c = p - r * cpr;
+            src_off[kk] = ((r & (kGuO - 1)) * rb + (c == cpr - 1 ? 0 : c) * 16) |
+                          (r >= kGuO ? (int32_t)0x80000000 : 0);
+        } else {
+            src_off[kk] = p < half ? p * 16 : ((p - half) * 16) | (int32_t)0x80000000;
+        }
     }
     const int n_inst = stage_async_count<kThreads>(units * 16);
     // stream cursor: the next item to load (expert index, row tile, ring slot)
@@ -699,40 +710,44 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     }
 }
 
+// One thread per 4 consecutive outputs of a token row; the grid's y dimension steps over the
+// tokens (it is capped on the host, so any T launches).
 __global__ __launch_bounds__(kThreads) void combine_kernel(
     const float *__restrict__ w, const int32_t *__restrict__ pos, const int32_t *__restrict__ offsets,
-    int32_t E, const float *__restrict__ ypair, int32_t k, int32_t H, float *__restrict__ y) {
+    int32_t E, const float *__restrict__ ypair, int32_t T, int32_t k, int32_t H,
+    float *__restrict__ y) {
     constexpr int kJ = 16;  // slots whose loads are issued together (one round trip for k <= 16)
-    const int t = blockIdx.y;
     const int r = (blockIdx.x * kThreads + threadIdx.x) * 4;
     if (r >= H) return;
     const int n_local = offsets[E];
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < k; j0 += kJ) {
-        int q[kJ];
-        float wt[kJ];
-        f32x4_t v[kJ];
+    for (int t = blockIdx.y; t < T; t += gridDim.y) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j0 = 0; j0 < k; j0 += kJ) {
+            int q[kJ];
+            float wt[kJ];
+            f32x4_t v[kJ];
 #pragma unroll
-        for (int u = 0; u < kJ; u++) {
-            const int p = t * k + j0 + u;
-            const bool in = j0 + u < k;
-            q[u] = in ? pos[p] : n_local;
-            wt[u] = in ? w[p] : 0.f;
-            // rows of non-local slots hold stale data; they are loaded and then skipped
-            v[u] = in ? *reinterpret_cast<const f32x4_t *>(ypair + (int64_t)p * H + r)
-                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
+            for (int u = 0; u < kJ; u++) {
+                const int64_t p = (int64_t)t * k + j0 + u;
+                const bool in = j0 + u < k;
+                q[u] = in ? pos[p] : n_local;
+                wt[u] = in ? w[p] : 0.f;
+                // rows of non-local slots hold stale data; they are loaded and then skipped
+                v[u] = in ? *reinterpret_cast<const f32x4_t *>(ypair + p * H + r)
+                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-        for (int u = 0; u < kJ; u++) {   // ascending slot order
-            if (q[u] < n_local) {
-                acc[0] = fmaf(wt[u], v[u][0], acc[0]);
-                acc[1] = fmaf(wt[u], v[u][1], acc[1]);
-                acc[2] = fmaf(wt[u], v[u][2], acc[2]);
-                acc[3] = fmaf(wt[u], v[u][3], acc[3]);
+            for (int u = 0; u < kJ; u++) {   // ascending slot order
+                if (q[u] < n_local) {
+                    acc[0] = fmaf(wt[u], v[u][0], acc[0]);
+                    acc[1] = fmaf(wt[u], v[u][1], acc[1]);
+                    acc[2] = fmaf(wt[u], v[u][2], acc[2]);
+                    acc[3] = fmaf(wt[u], v[u][3], acc[3]);
+                }
             }
         }
+        *reinterpret_cast<f32x4_t *>(y + (int64_t)t * H + r) = acc;
     }
-    *reinterpret_cast<f32x4_t *>(y + (int64_t)t * H + r) = acc;
 }
 
 struct DecodeWs {
@@ -774,10 +789,11 @@ size_t decode_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
 
 int launch_combine(const float *w, const int32_t *pos, const int32_t *offsets, int32_t E,
                    const float *ypair, int32_t T, int32_t k, int32_t H, float *y, hipStream_t s) {
-    dim3 grid((H / 4 + kThreads - 1) / kThreads, T);
+    // grid.y is limited to 65535: tokens beyond it are looped over inside the kernel
+    dim3 grid((H / 4 + kThreads - 1) / kThreads, std::min<int32_t>(T, 32768));
     prof_start(MOE_KERNEL_COMBINE, s);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, w, pos, offsets, E, ypair, k,
-                       H, y);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, w, pos, offsets, E, ypair, T,
+                       k, H, y);
     prof_stop(MOE_KERNEL_COMBINE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }

@@ -64,7 +64,7 @@ def _ffn(**over):
 @pytest.mark.parametrize("over,status", [
     (dict(x=0), moe.MOE_EINVAL), (dict(y=0), moe.MOE_EINVAL), (dict(ws=0), moe.MOE_EINVAL),
     (dict(T=-1), moe.MOE_EINVAL), (dict(k=0), moe.MOE_EINVAL), (dict(E=0), moe.MOE_EINVAL),
-    (dict(H=320), moe.MOE_EINVAL), (dict(F=96), moe.MOE_EINVAL), (dict(path=7), moe.MOE_EINVAL), (dict(path=4), moe.MOE_EINVAL),
+    (dict(H=96), moe.MOE_EINVAL), (dict(H=0), moe.MOE_EINVAL), (dict(F=96), moe.MOE_EINVAL), (dict(path=7), moe.MOE_EINVAL), (dict(path=4), moe.MOE_EINVAL),
     (dict(gate=_bank(FAKE + 4)), moe.MOE_EINVAL), (dict(down=_bank(stride=100)), moe.MOE_EINVAL),
     (dict(up=_bank(0)), moe.MOE_EINVAL), (dict(x=FAKE + 2), moe.MOE_EINVAL),
     (dict(gate=moe_bank(0, 0, None, FAKE + 4)), moe.MOE_EINVAL),      # pointer table misaligned
@@ -148,3 +148,24 @@ def _router(**over):
 ])
 def test_router_host_checks(over, status):
     assert _router(**over) == status
+
+
+def test_bank_keeps_its_tensors_alive():
+    """A moe_bank stores raw addresses; bank() must hold the tensors behind them, so that a
+    table or weight tensor cannot be freed (and its memory reused) while the bank is in use."""
+    import gc
+    import weakref
+
+    import torch
+    base = torch.zeros(4096, dtype=torch.uint8)
+    s2 = torch.ones(4, dtype=torch.float32)
+    tab = torch.tensor([base.data_ptr()] * 4, dtype=torch.int64)
+    refs = [weakref.ref(t) for t in (base, s2, tab)]
+    b = moe.bank(base, 1024, 16, scale2=s2, experts=tab)
+    assert b.base == base.data_ptr() + 16 and b.experts == tab.data_ptr()
+    del base, s2, tab
+    gc.collect()
+    assert all(r() is not None for r in refs)
+    del b
+    gc.collect()
+    assert all(r() is None for r in refs)

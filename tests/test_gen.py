@@ -6,30 +6,45 @@ import torch
 import gen
 
 
-def _route_bigint(p, E):
-    """The moe_sk_repro probe's router in Python integers (wrapping 64-bit arithmetic spelled
-    out with masks), independent of the vectorised numpy version."""
-    M = (1 << 64) - 1
-    h = (p * 0x9E3779B97F4A7C15) & M
-    h ^= h >> 29
-    h = (h * 0xBF58476D1CE4E5B9) & M
-    h ^= h >> 32
-    u = (h >> 11) / float(1 << 53)
-    return min(int(u ** 1.35 * E), E - 1)
+def _skew_cdf(e, E, a=1.35):
+    """P(expert <= e) under expert = min(floor(u^a * E), E - 1), u uniform: u^a < (e+1)/E."""
+    return np.minimum(((np.asarray(e, dtype=np.float64) + 1) / E) ** (1 / a), 1.0)
 
 
-def test_route_skewed_bit_exact():
-    ids = gen.route_skewed(4096, 8, 288).reshape(-1)
-    ref = np.array([_route_bigint(p, 288) for p in range(ids.size)])
-    assert np.array_equal(ids, ref)
+def test_route_skewed_is_a_function_of_the_pair():
+    """Each pair's expert depends on its index only: a shorter batch is a prefix of a longer one,
+    and other seeds give other routings."""
+    a = gen.route_skewed(512, 8, 288).reshape(-1)
+    b = gen.route_skewed(4096, 8, 288).reshape(-1)
+    assert np.array_equal(a, b[: a.size])
+    assert not np.array_equal(a, gen.route_skewed(512, 8, 288, seed=1).reshape(-1))
+    assert a.min() >= 0 and b.max() <= 287
 
 
 def test_route_skewed_closed_form_hot_expert():
-    """P(expert 0) = P(u^1.35 < 1/E) = (1/E)^(1/1.35)."""
+    """P(expert 0) = P(u^1.35 < 1/E) = (1/E)^(1/1.35), about 4.34 times the mean load at E=288."""
     ids = gen.route_skewed(4096, 8, 288).reshape(-1)
     p0 = (1 / 288) ** (1 / 1.35)
     n = ids.size
     assert abs((ids == 0).sum() - n * p0) < 4 * np.sqrt(n * p0)
+    assert abs(288 * p0 - 4.34) < 0.01
+
+
+def test_route_skewed_follows_the_power_law():
+    """Chi-square of the per-expert counts against the closed-form bin probabilities
+    P(e) = ((e+1)/E)^(1/1.35) - (e/E)^(1/1.35) (the last bin takes the rest): far inside the
+    tail at 287 degrees of freedom (mean 287, sd 24)."""
+    E, n = 288, 4096 * 8
+    ids = gen.route_skewed(4096, 8, E).reshape(-1)
+    cdf = _skew_cdf(np.arange(E), E)
+    p = np.diff(np.concatenate([[0.0], cdf]))
+    p[-1] = 1.0 - cdf[-2]
+    obs = np.bincount(ids, minlength=E)
+    chi2 = ((obs - n * p) ** 2 / (n * p)).sum()
+    assert chi2 < 287 + 6 * 24
+    # a wrong exponent is caught: the same counts against a = 1.58 (an 8x hot expert)
+    p8 = np.diff(np.concatenate([[0.0], _skew_cdf(np.arange(E), E, 1.58)]))
+    assert ((obs - n * p8) ** 2 / (n * p8)).sum() > 287 + 20 * 24
 
 
 @pytest.mark.parametrize("U", [10, 30, 60])
