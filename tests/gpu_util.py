@@ -94,3 +94,23 @@ def assert_parity(y, ref, what=""):
     assert rel <= REL_RMS_BOUND and mx <= MAX_ABS_BOUND, \
         f"{what}: relRMS {rel:.3e} (bound {REL_RMS_BOUND}), max abs/RMS {mx:.3e} (bound {MAX_ABS_BOUND})"
     return rel, mx
+
+
+def tile_tokens(ids: np.ndarray, E: int, expert_base: int = 0, bm: int = 128) -> np.ndarray:
+    """Tokens that put every M tile of the prefill path under test: for each active expert's
+    bucket (in the oracle's bucketing), cut into tiles of bm consecutive CSR pairs, the tokens of
+    the tile's first pair, of the last pair of its first half, of the first pair of its second
+    half and of its last pair; plus the batch's last token. Sorted, without duplicates."""
+    import oracle
+    ids = np.asarray(ids)
+    T, k = ids.shape
+    off, pairs, act, _, _ = oracle.route_bucket(ids, E, expert_base)
+    tok = {T - 1}
+    for e in act:
+        q0, m = int(off[e]), int(off[e + 1] - off[e])
+        for m0 in range(0, m, bm):
+            last = min(m0 + bm, m) - 1
+            for c in (m0, m0 + bm // 2 - 1, m0 + bm // 2, last):
+                if m0 <= c <= last:
+                    tok.add(int(pairs[q0 + c]) // k)
+    return np.array(sorted(tok), dtype=np.int64)

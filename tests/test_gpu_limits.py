@@ -70,3 +70,53 @@ def test_layer_at_max_width(seed, H, F):
     assert st == moe.MOE_ESHAPE
     ref = oracle.ffn_union(case)
     assert_parity(dc.run(moe.MOE_PATH_AUTO), ref, f"max width H={H} F={F}")
+
+
+def test_decode_pairs_beyond_lds_plan():
+    """More routed pairs than the decode kernels' start-up reads into LDS (4096): the plan takes
+    its pair ids from memory instead. 128 tokens x top-40 over 512 experts through AUTO."""
+    print("[case] decode P>4096 T=128 k=40 E=512", flush=True)
+    case = gen.make_random_case(114, 128, 40, 512, 512, 128, scales="all", nonlocal_frac=0.05)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_AUTO)
+    assert_parity(y, oracle.ffn_union(case), "decode P>4096")
+
+
+@pytest.mark.parametrize("path", [moe.MOE_PATH_PREFILL, moe.MOE_PATH_DECODE])
+def test_tokens_beyond_grid_y_limit(path):
+    """70000 tokens (more than a grid's y dimension holds): the combine loops over tokens."""
+    T = 70000
+    print(f"[case] T={T} path={path}", flush=True)
+    case = gen.make_random_case(115, T, 1, 4, 64, 64, scales="all", nonlocal_frac=0.05)
+    dc = DeviceCase(case)
+    y = dc.run(path)
+    tok = np.concatenate([np.arange(8), np.arange(65530, 65542), np.arange(T - 8, T)])
+    assert_parity(y[tok], oracle.ffn_union(case, tokens=tok), f"T={T}")
+
+
+def test_layer_at_max_pairs():
+    """The whole layer (bucketing, GEMM path, combine) at exactly MOE_MAX_PAIRS routed pairs:
+    2^20 tokens x top-16 over 64 experts, hidden = ff = 64; sampled tokens against the oracle."""
+    T, k, E = MAX_PAIRS // 16, 16, 64
+    print(f"[case] layer at max pairs T={T} k={k} E={E}", flush=True)
+    case = gen.make_random_case(116, T, k, E, 64, 64, scales="all", nonlocal_frac=0.01)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_AUTO)
+    tok = np.concatenate([np.random.default_rng(5).choice(T, 40, replace=False), [T - 1]])
+    assert_parity(y[tok], oracle.ffn_union(case, tokens=tok), "max pairs")
+
+
+@pytest.mark.parametrize("seed,T,k,E,H,F,fused", [
+    (201, 5, 3, 6, 320, 64, False), (202, 24, 4, 9, 576, 192, True),
+    (203, 40, 10, 32, 2624, 640, True), (204, 200, 2, 3, 64, 128, False)])
+def test_hidden_multiple_of_64(seed, T, k, E, H, F, fused):
+    """Hidden sizes that are multiples of 64 but not of 256 (rows not whole 16-byte chunks) on
+    every path that takes them."""
+    print(f"[case] hidden%64 seed={seed} T={T} k={k} E={E} H={H} F={F}", flush=True)
+    case = gen.make_random_case(seed, T, k, E, H, F, scales="all", nonlocal_frac=0.1, fused=fused)
+    ref = oracle.ffn_union(case)
+    dc = DeviceCase(case)
+    paths = [moe.MOE_PATH_PREFILL, moe.MOE_PATH_AUTO] + ([moe.MOE_PATH_DECODE] if T <= 128 else [])
+    for path in paths:
+        dc.y.fill_(float("nan"))
+        assert_parity(dc.run(path), ref, f"H={H} path {path}")

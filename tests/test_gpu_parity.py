@@ -12,7 +12,7 @@ import torch
 import gen
 import oracle
 import routed_moe_expert_amd as moe
-from gpu_util import DeviceCase, assert_parity
+from gpu_util import DeviceCase, assert_parity, tile_tokens
 
 pytestmark = pytest.mark.gpu
 
@@ -109,26 +109,20 @@ def _workload(name, T, U=None):
     return _WL[key]
 
 
-@pytest.mark.parametrize("name,T,U,n_check", [
-    ("tiny_decode", 1, None, None), ("verify_chunk", 6, 10, None), ("verify_chunk", 6, 30, None),
-    ("verify_chunk", 6, 60, None), ("e256_plateau", 16, None, None),
-    ("e256_plateau", 128, None, 12), ("skewed_prefill", 16, None, None),
-    ("full_prefill", 8, None, None)])
-def test_decode_workloads(name, T, U, n_check):
-    """Full-size decode workloads; the largest compares a sample of tokens one by one."""
+@pytest.mark.parametrize("name,T,U", [
+    ("tiny_decode", 1, None), ("verify_chunk", 6, 10), ("verify_chunk", 6, 30),
+    ("verify_chunk", 6, 60), ("e256_plateau", 16, None), ("e256_plateau", 32, None),
+    ("e256_plateau", 64, None), ("e256_plateau", 80, None), ("e256_plateau", 128, None),
+    ("skewed_prefill", 16, None), ("full_prefill", 8, None)])
+def test_decode_workloads(name, T, U):
+    """Every decode workload at full size through AUTO (the decode path at these T), every token
+    compared with the oracle."""
     _print_case("decode_workload", name=name, T=T, U=U)
     case = _workload(name, T, U)
     dc = DeviceCase(case)
-    y = dc.run(moe.MOE_PATH_DECODE)
+    y = dc.run(moe.MOE_PATH_AUTO)
     _check_bucket(dc)
-    if n_check is None:
-        ref = oracle.ffn_per_slot(case)
-        assert_parity(y, ref, name)
-    else:
-        tok = np.random.default_rng(T).choice(T, size=n_check, replace=False)
-        tok[0] = T - 1
-        ref = oracle.ffn_per_slot(case, tokens=tok)
-        assert_parity(y[tok], ref, name)
+    assert_parity(y, oracle.ffn_union(case), name)
 
 
 def test_decode_beyond_slice_width_uses_gemm_path():
@@ -200,21 +194,26 @@ def test_prefill_small(seed, T, k, E, H, F, scales, frac, base, fused):
     assert_parity(y, oracle.ffn_union(case), "prefill_small")
 
 
-@pytest.mark.parametrize("name,T,n_check", [("skewed_prefill", 512, 24),
-                                            ("skewed_prefill", 4096, 16),
-                                            ("full_prefill", 4096, 12),
-                                            ("e256_plateau", 128, 12)])
-def test_prefill_workloads(name, T, n_check):
-    """Full-size prefill workloads (and the E256 decode shape forced through the GEMM path),
-    compared on sampled tokens, always including the last token."""
+@pytest.mark.parametrize("name,T", [("skewed_prefill", 512), ("skewed_prefill", 2048),
+                                    ("skewed_prefill", 4096), ("full_prefill", 4096)])
+def test_prefill_workloads(name, T):
+    """Full-size prefill workloads through AUTO (the GEMM path), compared on the tokens that
+    cover every M tile: each tile's first and last pair and both ends of its halves."""
     _print_case("prefill_workload", name=name, T=T)
     case = _workload(name, T)
     dc = DeviceCase(case)
-    y = dc.run(moe.MOE_PATH_PREFILL)
-    tok = np.random.default_rng(T + 1).choice(T, size=n_check, replace=False)
-    tok[0] = T - 1
-    ref = oracle.ffn_per_slot(case, tokens=tok)
-    assert_parity(y[tok], ref, name)
+    y = dc.run(moe.MOE_PATH_AUTO)
+    _check_bucket(dc)
+    tok = tile_tokens(case["ids"], dc.E)
+    print(f"[case] comparing {tok.size} tokens", flush=True)
+    assert_parity(y[tok], oracle.ffn_union(case, tokens=tok), name)
+
+
+def test_e256_forced_through_gemm_path():
+    """The E256 decode shape forced through the GEMM path, every token compared."""
+    case = _workload("e256_plateau", 128)
+    dc = DeviceCase(case)
+    assert_parity(dc.run(moe.MOE_PATH_PREFILL), oracle.ffn_union(case), "e256 gemm path")
 
 
 def test_prefill_deterministic_and_matches_decode():
