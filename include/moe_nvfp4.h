@@ -156,6 +156,25 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
                   moe_stream_t stream);
 
 /*
+ * moe_ffn_nvfp4 without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The workspace is a library-owned device array of MOE_STATIC_WS_BYTES per GPU (held from the
+ * library's first use on that GPU until the process ends); the call allocates nothing.
+ * Arguments, outputs and errors are those of moe_ffn_nvfp4, plus MOE_EWS when
+ * moe_ffn_nvfp4_ws(T, k, E, H, F) exceeds MOE_STATIC_WS_BYTES (checked on the host before
+ * anything is enqueued), and MOE_ELAUNCH if the array's device address cannot be found.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time on one GPU (on
+ * different streams, or from several threads without ordering) race and give undefined results.
+ * The array's content is not carried from one call to the next.
+ */
+#define MOE_STATIC_WS_BYTES (128u << 20)
+int moe_ffn_nvfp4_static(const uint16_t *x, const float *topk_w, const int32_t *offsets,
+                         const int32_t *pair_ids, const int32_t *active, const int32_t *counts,
+                         moe_bank gate, moe_bank up, moe_bank down, int32_t T, int32_t k,
+                         int32_t E, int32_t H, int32_t F, float *y, int32_t path,
+                         moe_stream_t stream);
+
+/*
  * Router step (the step before moe_route_bucket; the pages route each token to k distinct experts
  * with softmax router weights -- the Rocket post's E512 top-10, the moe_sk_repro.rs top-8 -- but
  * leave the router itself unspecified; the reading implemented here is the plain one):

@@ -50,6 +50,9 @@ def _load():
     l.moe_ffn_nvfp4.restype = ctypes.c_int
     l.moe_ffn_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
                                 i32, i32, i32, i32, i32, vp, i32, vp, sz, vp]
+    l.moe_ffn_nvfp4_static.restype = ctypes.c_int
+    l.moe_ffn_nvfp4_static.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
+                                       i32, i32, i32, i32, i32, vp, i32, vp]
     l.moe_router_topk.restype = ctypes.c_int
     l.moe_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     l.moe_profile_kernel.restype = ctypes.c_int
@@ -129,6 +132,18 @@ def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, 
                            _ptr(counts), gate, up, down, T, k, E, H, F, _ptr(y), path, _ptr(ws),
                            ws_bytes, _stream(stream))
     return _check("moe_ffn_nvfp4", st, raise_on_error)
+
+
+MOE_STATIC_WS_BYTES = 128 << 20
+
+
+def moe_ffn_nvfp4_static(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank,
+                         up: moe_bank, down: moe_bank, T: int, k: int, E: int, H: int, F: int, y,
+                         path: int = MOE_PATH_AUTO, stream=None, raise_on_error: bool = True) -> int:
+    st = lib.moe_ffn_nvfp4_static(_ptr(x), _ptr(topk_w), _ptr(offsets), _ptr(pair_ids),
+                                  _ptr(active), _ptr(counts), gate, up, down, T, k, E, H, F,
+                                  _ptr(y), path, _stream(stream))
+    return _check("moe_ffn_nvfp4_static", st, raise_on_error)
 
 
 def moe_router_topk(logits, T: int, E: int, k: int, topk_ids, topk_w, stream=None,
