@@ -1,15 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the routed NVFP4 MoE layer on one MI355X.
 
-One step = one layer: moe_route_bucket + moe_ffn_nvfp4 over one batch of synthetic input that is
-already resident in HBM. The default workload is the verify chunk (E=512 experts, hidden 2560,
+One step = one layer over one batch of synthetic input that is already resident in HBM: one call
+of moe_layer_nvfp4 (routed ids -> y; the same as moe_route_bucket + moe_ffn_nvfp4, which is timed
+beside it as `two_call_layer_us`). The headline workload is the verify chunk (E=512 experts, hidden 2560,
 ff 640, top-10, 6 tokens = 60 routed slots, union of 60 distinct experts), the decode shape the
 moe_union_probe page prices. Consecutive steps use routing over disjoint expert windows so that
 every step streams its experts' weights from HBM, not from the 256 MB Infinity Cache.
 
+Every timed region is queued behind a bounded sleep kernel, so all of its launches are enqueued
+before the GPU reaches the first one: the HIP events then time the GPU alone, not the host's
+launch rate.
+
 Prints one JSON line: value = unique-expert weight bytes per second (decode workloads) or useful
 TFLOP/s (prefill workloads), the dominant kernel's roofline from HIP events recorded around its
-launches, and the fp64 oracle timed on a bounded sample on the host cores.
+launches, the fp64 oracle timed on a bounded sample on the host cores, and `rows`: the same
+measurement for every configuration of the layer (tiny decode, verify chunk at three union
+sizes, the rank-local E256 plateau at five token counts, the skewed prefill at three, the
+full-width prefill).
 """
 import argparse
 import ctypes
@@ -25,32 +33,28 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed-MoE layer µs + HBM GB/s (% of 8 TB/s) at T=1..128; TFLOP/s at T=4096"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0    # MI355X dense MFMA, f16 and bf16 alike (the GEMMs run f16)
+F16_PEAK_TFLOPS = 2500.0     # MI355X dense MFMA, f16 and bf16 alike (the GEMMs run f16)
 COPY_BYTES = 1 << 30
 
 # HBM traffic of the dominant kernel, per launch, from two rocprofv3 --pmc passes over
-# `bench.py --steps 20 --warmup 5 --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE, KiB per
-# dispatch, mean over the dispatches). Each counter is scaled by what it reads for
-# `bench.py --copy-calib` (a 1 GiB copy): FETCH_SIZE read 524301 KiB for 1048576 KiB moved, so x2.0;
-# WRITE_SIZE read 1048576 KiB, so x1.0. Keyed by the SHA-256 of the kernel's sources: once they
-# change, the entry no longer applies and traffic is reported as null until measured again.
+# `bench.py --steps 20 --warmup 5 --rows none --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch, mean over the dispatches). Each counter is scaled by what it reads for
+# `bench.py --copy-calib` (a 1 GiB copy): FETCH_SIZE read 524301 KiB for 1048576 KiB moved, so
+# x2.0; WRITE_SIZE read 1048576 KiB, so x1.0. Keyed by the SHA-256 of the kernel's sources: once
+# they change, the entry no longer applies and traffic is reported as null until measured again.
 FETCH_SCALE = 1048576.0 / 524301.2
 WRITE_SCALE = 1.0
-TRAFFIC = {
-    ("gu_decode_kernel", "verify_chunk", 6, 60): {
-        "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
-                    "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "e7a723f1467c7a4b04c79c0b729cb65f901f1608de4f57ce3edf8f7762b65dda",
-        "fetch_kib": 54326.5, "write_kib": 169.0,
-    },
-    # (`bench.py --workload full_prefill --steps 4 --warmup 1 --no-cpu-baseline`)
-    ("gemm_kernel<false>", "full_prefill", 4096, None): {
-        "sources": ["routed_moe_expert_amd/csrc/ffn_prefill.hip",
-                    "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "faa674bc3b45a1d3ac93801fa75855425e55c45c2b9b495e671e2cc1fbfec7a8",
-        "fetch_kib": 1339114.5, "write_kib": 175615.4,
-    },
-}
+TRAFFIC = {}
+
+# every configuration of the layer: (workload, tokens, union size for the verify chunk)
+ROWS = [("tiny_decode", 1, None), ("verify_chunk", 6, 10), ("verify_chunk", 6, 30),
+        ("verify_chunk", 6, 60), ("e256_plateau", 16, None), ("e256_plateau", 32, None),
+        ("e256_plateau", 64, None), ("e256_plateau", 80, None), ("e256_plateau", 128, None),
+        ("skewed_prefill", 512, None), ("skewed_prefill", 2048, None),
+        ("skewed_prefill", 4096, None), ("full_prefill", 4096, None)]
+
+DEFAULT_T = {"verify_chunk": 6, "tiny_decode": 1, "e256_plateau": 128, "skewed_prefill": 4096,
+             "full_prefill": 4096, "shared_expert": 128}
 
 
 def measured_traffic(kname, workload, T, U):
@@ -87,6 +91,8 @@ def parse():
     ap.add_argument("--workload", default="verify_chunk",
                     choices=["verify_chunk", "tiny_decode", "e256_plateau", "skewed_prefill",
                              "full_prefill", "shared_expert", "router"])
+    ap.add_argument("--rows", default="all", choices=["all", "none"],
+                    help="also time every configuration of the layer (the `rows` key)")
     ap.add_argument("--E", type=int, default=288, help="experts (router workload)")
     ap.add_argument("--k", type=int, default=8, help="top-k (router workload)")
     ap.add_argument("--T", type=int, default=None, help="tokens (workload default if unset)")
@@ -113,38 +119,131 @@ def copy_calibration(torch):
     print(json.dumps({"copy_bytes_per_launch": COPY_BYTES, "launches": 5}), flush=True)
 
 
-DEFAULT_T = {"verify_chunk": 6, "tiny_decode": 1, "e256_plateau": 128, "skewed_prefill": 4096,
-             "full_prefill": 4096, "shared_expert": 128}
+# ----------------------------------------------------------------------------------- timing
+
+class Queue:
+    """Times GPU work free of host launch overhead: a bounded sleep kernel is queued first, long
+    enough for the host to enqueue the whole timed region behind it."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        # GPU time per sleep cycle, measured once
+        a, b = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        torch.cuda.synchronize()
+        a.record(self.stream)
+        torch.cuda._sleep(2_000_000)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        self.ms_per_cycle = max(a.elapsed_time(b), 1e-3) / 2_000_000
+
+    def run(self, enqueue, host_ms_hint):
+        """Sleep, then enqueue(); returns (host enqueue ms, sleep ms, whether the sleep outlasted
+        the enqueue). host_ms_hint: expected host time to enqueue."""
+        torch = self.torch
+        want_ms = min(max(3.0 * host_ms_hint + 2.0, 5.0), 2000.0)
+        cycles = int(want_ms / self.ms_per_cycle)
+        s0, s1 = (torch.cuda.Event(enable_timing=True) for _ in range(2))
+        torch.cuda.synchronize()
+        s0.record(self.stream)
+        torch.cuda._sleep(cycles)
+        s1.record(self.stream)
+        t0 = time.perf_counter()
+        enqueue()
+        host_ms = (time.perf_counter() - t0) * 1e3
+        torch.cuda.synchronize()
+        sleep_ms = s0.elapsed_time(s1)
+        return host_ms, sleep_ms, host_ms < sleep_ms
 
 
-def build_inputs(args, torch, gen, moe):
-    """Host generation + upload. Returns (steps callables data, description dict)."""
+def time_steps(q, step, K, first):
+    """Per-step GPU ms of K steps (step(first + i)), queued behind a sleep."""
+    torch = q.torch
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    t0 = time.perf_counter()
+    step(first)
+    torch.cuda.synchronize()
+    hint = (time.perf_counter() - t0) * 1e3 * K
+
+    def enqueue():
+        for i in range(K):
+            evs[i].record(q.stream)
+            step(first + i)
+        evs[K].record(q.stream)
+
+    host_ms, sleep_ms, ahead = q.run(enqueue, hint)
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
+    return per, {"host_enqueue_ms": host_ms, "sleep_ms": sleep_ms, "queued_ahead": ahead}
+
+
+def kernel_avg_ms(q, moe, kid, step, K, first):
+    """Average GPU ms of kernel `kid` over K steps: HIP events the library records around each
+    of its launches (on the launch stream), queued behind a sleep."""
+    hip = _hip()
+    starts, stops = [], []
+    for _ in range(K):
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        hip.hipEventCreate(ctypes.byref(a))
+        hip.hipEventCreate(ctypes.byref(b))
+        starts.append(a.value)
+        stops.append(b.value)
+
+    def enqueue():
+        moe.moe_profile_kernel(kid, starts, stops)
+        for i in range(K):
+            step(first + i)
+
+    t0 = time.perf_counter()
+    step(first)
+    q.torch.cuda.synchronize()
+    q.run(enqueue, (time.perf_counter() - t0) * 1e3 * K)
+    n_rec = moe.moe_profile_count()
+    moe.moe_profile_kernel(moe.MOE_KERNEL_NONE, [], [])
+    kms = []
+    for i in range(n_rec):
+        f = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(starts[i]),
+                                ctypes.c_void_p(stops[i]))
+        kms.append(f.value)
+    for a, b in zip(starts, stops):
+        hip.hipEventDestroy(ctypes.c_void_p(a))
+        hip.hipEventDestroy(ctypes.c_void_p(b))
+    return (sum(kms) / len(kms) if kms else float("nan")), len(kms)
+
+
+# ----------------------------------------------------------------------------------- inputs
+
+def make_banks_host(gen, name):
+    w = gen.WORKLOADS[name]
+    return gen.make_banks(w["E"], w["H"], w["F"], w["fused"], w["seed"])
+
+
+def build_inputs(name, T, U, warm, virtual, torch, gen, moe, host_banks=None):
+    """Host generation + upload of one workload at T tokens."""
     import numpy as np
 
-    name = args.workload
     w = gen.WORKLOADS[name]
     E, H, F, k, seed = w["E"], w["H"], w["F"], w["k"], w["seed"]
-    T = args.T or DEFAULT_T[name]
-    U = None
     copies = 1
-    virtual = 0
     if name == "verify_chunk":
-        U = args.U
         variants = [gen.route_union_rotated(seed, T, k, E, U, v)
-                    for v in range(1 if args.warm else math.ceil(2 * E / U) + 1)]
+                    for v in range(1 if warm else math.ceil(2 * E / U) + 1)]
     elif name == "tiny_decode":
         U = k
-        copies = 1 if args.warm else 3          # 3 bank copies x disjoint windows > 2 x 256 MB
+        copies = 1 if warm else 3          # 3 bank copies x disjoint windows > 2 x 256 MB
         variants = [gen.route_union_rotated(seed, T, k, E, k, v)
-                    for v in range(1 if args.warm else E // k)]
+                    for v in range(1 if warm else E // k)]
     elif name == "shared_expert":
         # the one expert as G virtual experts (pointer tables onto its one copy), tokens dealt
         # round-robin: the same dense SwiGLU with G times the work items
-        virtual = args.virtual or max(1, math.ceil(T / 16))
+        virtual = virtual or max(1, math.ceil(T / 16))
         variants = [gen.shared_virtual_routing(T, virtual)[0]]
     else:
         variants = [gen.make_routing(name, T)[0]]
-    banks = gen.make_banks(E, H, F, w["fused"], seed)
+        virtual = 0
+    if name != "shared_expert":
+        virtual = 0
+    banks = host_banks if host_banks is not None else make_banks_host(gen, name)
     x = gen.bf16_normal(seed, (T, H))
     wts = gen.make_routing(name, T)[1] if name == "shared_expert" else gen.router_weights(seed, T, k)
 
@@ -153,33 +252,165 @@ def build_inputs(args, torch, gen, moe):
                                    else np.ascontiguousarray(a)).to(dev)
     rbh, rbf = H // 64 * 36, F // 64 * 36
     bank_sets = []
-    for c in range(copies):
+    for _ in range(copies):
         if w["fused"]:
             gu = t(banks["gate_up"])
             gate, up = moe.bank(gu, 2 * F * rbh), moe.bank(gu, 2 * F * rbh, F * rbh)
-            keep = [gu]
         else:
             g_, u_ = t(banks["gate"]), t(banks["up"])
             gate, up = moe.bank(g_, F * rbh), moe.bank(u_, F * rbh)
-            keep = [g_, u_]
-        d_ = t(banks["down"])
-        down = moe.bank(d_, H * rbf)
-        keep.append(d_)
+        down = moe.bank(t(banks["down"]), H * rbf)
         if virtual:
+            strided = (gate, up, down)
             tabs = [torch.full((virtual,), b.base, dtype=torch.int64, device=dev)
-                    for b in (gate, up, down)]
+                    for b in strided]
             gate, up, down = (moe.bank(None, 0, experts=tb) for tb in tabs)
-            keep += tabs
-        bank_sets.append((gate, up, down, keep))
-    del banks
+            gate._keep += (strided,)   # the tables point into these banks' tensors
+        bank_sets.append((gate, up, down))
     ids_dev = [t(v.reshape(-1).astype(np.int32)) for v in variants]
     uniq = [1] if virtual else [int(np.unique(v).size) for v in variants]
     out = dict(name=name, E=virtual or E, H=H, F=F, k=k, T=T, U=U, copies=copies,
                variants=variants, ids=ids_dev, uniq=uniq, x=t(x), w=t(wts.reshape(-1)),
-               bank_sets=bank_sets, host=dict(x=x, w=wts), virtual=virtual)
+               bank_sets=bank_sets, host=dict(x=x, w=wts, banks=banks), virtual=virtual)
     if virtual:   # the oracle takes the plain one-expert form
         out.update(oracle_E=E, oracle_ids=np.zeros((T, 1), dtype=np.int32))
     return out
+
+
+class Layer:
+    """Device buffers and the step function for one workload."""
+
+    def __init__(self, D, path, torch, moe, fused=True):
+        E, H, k, T = D["E"], D["H"], D["k"], D["T"]
+        P = T * k
+        dev = torch.device("cuda")
+        self.D, self.moe = D, moe
+        self.path = path
+        self.fused = fused
+        self.lws = moe.moe_layer_nvfp4_ws(T, k, E, H, D["F"])
+        self.layer_ws = torch.empty(self.lws if fused else 1, dtype=torch.uint8, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.pair_ids = torch.empty(P, dtype=torch.int32, device=dev)
+        self.active = torch.empty(E, dtype=torch.int32, device=dev)
+        self.counts = torch.empty(2, dtype=torch.int32, device=dev)
+        self.bws = moe.moe_route_bucket_ws(T, k, E)
+        self.bucket_ws = torch.empty(max(self.bws, 1), dtype=torch.uint8, device=dev)
+        self.fws = moe.moe_ffn_nvfp4_ws(T, k, E, H, D["F"])
+        self.ws = torch.empty(self.fws, dtype=torch.uint8, device=dev)
+        self.y = torch.empty(T, H, dtype=torch.float32, device=dev)
+        self.sh = torch.cuda.current_stream().cuda_stream
+
+    def step(self, i):
+        D, moe = self.D, self.moe
+        nv, nc = len(D["ids"]), D["copies"]
+        ids = D["ids"][i % nv]
+        gate, up, down = D["bank_sets"][(i // nv) % nc if nc > 1 else 0]
+        E, H, F, k, T = D["E"], D["H"], D["F"], D["k"], D["T"]
+        if self.fused:   # one call: routed ids -> y
+            moe.moe_layer_nvfp4(ids, 0, D["x"], D["w"], gate, up, down, T, k, E, H, F, self.y,
+                                self.path, self.layer_ws, self.lws, stream=self.sh)
+            return
+        moe.moe_route_bucket(ids, T, k, E, 0, self.offsets, self.pair_ids, self.active,
+                             self.counts, self.bucket_ws, self.bws, stream=self.sh)
+        moe.moe_ffn_nvfp4(D["x"], D["w"], self.offsets, self.pair_ids, self.active, self.counts,
+                          gate, up, down, T, k, E, H, F, self.y, self.path, self.ws, self.fws,
+                          stream=self.sh)
+
+
+def kernel_table(D, decode):
+    """(id, name, amount per launch, unit, peak) of the two big kernels of the path: algorithmic
+    HBM bytes for the decode kernels, useful flops for the GEMMs."""
+    import routed_moe_expert_amd as moe
+    E, H, F, k, T = D["E"], D["H"], D["F"], D["k"], D["T"]
+    P = T * k
+    rbh, rbf = H // 64 * 36, F // 64 * 36
+    uniq = statistics.mean(D["uniq"])
+    if decode:
+        return [(moe.MOE_KERNEL_GU_DECODE, "gu_decode_kernel",
+                 uniq * 2 * F * rbh + T * H * 2 + P * F * 4, "GB/s", HBM_PEAK_GBS),
+                (moe.MOE_KERNEL_DN_DECODE, "dn_decode_kernel",
+                 uniq * H * rbf + P * F * 4 + P * H * 4, "GB/s", HBM_PEAK_GBS)]
+    return [(moe.MOE_KERNEL_GU_PREFILL, "gemm_kernel<false>", 4.0 * P * H * F, "TFLOP/s",
+             F16_PEAK_TFLOPS),
+            (moe.MOE_KERNEL_DN_PREFILL, "gemm_kernel<true>", 2.0 * P * H * F, "TFLOP/s",
+             F16_PEAK_TFLOPS)]
+
+
+def hbm_note(D, warm):
+    E = D["E"]
+    rbh, rbf = D["H"] // 64 * 36, D["F"] // 64 * 36
+    per_expert = 2 * D["F"] * rbh + D["H"] * rbf
+    cycled = min(E, sum(D["uniq"])) * per_expert * D["copies"]
+    if warm:
+        return "warm (one routing reused)"
+    if cycled < 256e6:
+        return (f"cache-resident: {cycled / 1e6:.1f} MB of weights in rotation, under the "
+                "256 MB Infinity Cache")
+    if len(D["ids"]) > 1 or D["copies"] > 1:
+        return (f"cold ({len(D['ids'])} routings over disjoint expert windows x "
+                f"{D['copies']} bank copies, {cycled / 1e6:.0f} MB of weights in rotation)")
+    return f"cold ({cycled / 1e6:.0f} MB of weights per step, over 2 x the Infinity Cache)"
+
+
+def measure(D, path_flag, K, W, q, torch, moe, kernels=True):
+    """Times one workload: per-layer GPU times over K steps of the one-call layer
+    (moe_layer_nvfp4), the path's two big kernels, and for comparison the layer as two calls
+    (moe_route_bucket + moe_ffn_nvfp4)."""
+    T = D["T"]
+    two = Layer(D, path_flag, torch, moe, fused=False)
+    for i in range(W):
+        two.step(i)
+    torch.cuda.synchronize()
+    per2, _ = time_steps(q, two.step, K, W)
+    del two
+    lay = Layer(D, path_flag, torch, moe)
+    for i in range(W):
+        lay.step(i)
+    torch.cuda.synchronize()
+    per, qinfo = time_steps(q, lay.step, K, W)
+    decode = path_flag == moe.MOE_PATH_DECODE or (path_flag == moe.MOE_PATH_AUTO and T <= 128)
+    H, F, k = D["H"], D["F"], D["k"]
+    rbh, rbf = H // 64 * 36, F // 64 * 36
+    per_expert = 2 * F * rbh + H * rbf
+    uniq = statistics.mean(D["uniq"])
+    mean_ms = sum(per) / len(per)
+    med = statistics.median(per)
+    s = mean_ms * 1e-3
+    res = {
+        "layer_us": {"mean": mean_ms * 1e3, "min": min(per) * 1e3, "median": med * 1e3,
+                     "spread": (max(per) - min(per)) / med if med > 0 else None},
+        "ms_per_step": mean_ms, "decode": decode, "queue": qinfo,
+        "two_call_layer_us": {"mean": sum(per2) / len(per2) * 1e3,
+                              "median": statistics.median(per2) * 1e3, "min": min(per2) * 1e3},
+        "unique_expert_bytes": uniq * per_expert,
+        "unique_gbs": uniq * per_expert / s / 1e9,
+        "hbm_frac_unique": uniq * per_expert / s / 1e9 / HBM_PEAK_GBS,
+        "useful_tflops": 6.0 * T * k * H * F / s / 1e12,
+        "mfma_frac_useful": 6.0 * T * k * H * F / s / 1e12 / F16_PEAK_TFLOPS,
+        "kernels": {},
+    }
+    if kernels:
+        for kid, kname, amount, unit, peak in kernel_table(D, decode):
+            avg_ms, n = kernel_avg_ms(q, moe, kid, lay.step, K, W + K)
+            ach = amount / (avg_ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+            res["kernels"][kname] = {"avg_launch_us": avg_ms * 1e3, "launches": n,
+                                     "per_launch": amount, "achieved": ach, "unit": unit,
+                                     "peak": peak, "frac": ach / peak}
+    del lay
+    return res
+
+
+# ----------------------------------------------------------------------------------- main
+
+def describe(D):
+    E, H, F, k, T = D["E"], D["H"], D["F"], D["k"], D["T"]
+    return {"verify_chunk": f"verify chunk: E={E} H={H} F={F} top-{k} T={T}, union U={D['U']}",
+            "tiny_decode": f"tiny decode: E={E} H={H} F={F} top-{k} T={T}",
+            "e256_plateau": f"rank-local E256 plateau: E={E} H={H} F={F} top-{k} T={T}",
+            "skewed_prefill": f"skewed prefill: E={E} H={H} F={F} top-{k} T={T}",
+            "full_prefill": f"full-width prefill: E={E} H={H} F={F} top-{k} T={T}",
+            "shared_expert": f"shared expert (dense SwiGLU, every token): H={H} F={F} T={T}, "
+                             f"as {D['virtual']} virtual experts over its one weight copy"}[D["name"]]
 
 
 def main():
@@ -191,7 +422,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     if args.copy_calib:
@@ -205,184 +435,80 @@ def main():
     if args.workload == "router":
         bench_router(args, torch, gen, moe)
         return
-    D = build_inputs(args, torch, gen, moe)
-    E, H, F, k, T = D["E"], D["H"], D["F"], D["k"], D["T"]
-    P = T * k
+    q = Queue(torch)
     path = {"auto": moe.MOE_PATH_AUTO, "decode": moe.MOE_PATH_DECODE,
             "prefill": moe.MOE_PATH_PREFILL}[args.path]
-    eff_path = path if path else (moe.MOE_PATH_DECODE if T <= 128 else moe.MOE_PATH_PREFILL)
-    decode = eff_path == moe.MOE_PATH_DECODE
+    K, W = args.steps, args.warmup
 
-    dev = torch.device("cuda")
-    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    pair_ids = torch.empty(P, dtype=torch.int32, device=dev)
-    active = torch.empty(E, dtype=torch.int32, device=dev)
-    counts = torch.empty(2, dtype=torch.int32, device=dev)
-    bws = moe.moe_route_bucket_ws(T, k, E)
-    bucket_ws = torch.empty(max(bws, 1), dtype=torch.uint8, device=dev)
-    fws = moe.moe_ffn_nvfp4_ws(T, k, E, H, F)
-    ws = torch.empty(fws, dtype=torch.uint8, device=dev)
-    y = torch.empty(T, H, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    nv, nc = len(D["ids"]), D["copies"]
-
-    def step(i):
-        ids = D["ids"][i % nv]
-        gate, up, down, _ = D["bank_sets"][(i // nv) % nc if nc > 1 else 0]
-        moe.moe_route_bucket(ids, T, k, E, 0, offsets, pair_ids, active, counts, bucket_ws, bws,
-                             stream=sh)
-        moe.moe_ffn_nvfp4(D["x"], D["w"], offsets, pair_ids, active, counts, gate, up, down, T,
-                          k, E, H, F, y, path, ws, fws, stream=sh)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    # timed region: K steps, an event before each step for per-layer times
-    K = args.steps
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        evs[i].record(stream)
-        step(args.warmup + i)
-    evs[K].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
-    ms_per_step = evs[0].elapsed_time(evs[K]) / K
-
-    # dominant kernel: HIP events recorded by the library around each of its launches, over a
-    # second pass of the same K steps
-    hip = _hip()
-    kid = moe.MOE_KERNEL_GU_DECODE if decode else moe.MOE_KERNEL_GU_PREFILL
-    kname = "gu_decode_kernel" if decode else "gemm_kernel<false>"   # gate/up + SiLU
-    starts, stops = [], []
-    for _ in range(K):
-        a, b = ctypes.c_void_p(), ctypes.c_void_p()
-        hip.hipEventCreate(ctypes.byref(a))
-        hip.hipEventCreate(ctypes.byref(b))
-        starts.append(a.value)
-        stops.append(b.value)
-    torch.cuda.synchronize()
-    moe.moe_profile_kernel(kid, starts, stops)
-    for i in range(K):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    n_rec = moe.moe_profile_count()
-    moe.moe_profile_kernel(moe.MOE_KERNEL_NONE, [], [])
-    kms = []
-    for i in range(n_rec):
-        f = ctypes.c_float()
-        hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(starts[i]), ctypes.c_void_p(stops[i]))
-        kms.append(f.value)
-    for a, b in zip(starts, stops):
-        hip.hipEventDestroy(ctypes.c_void_p(a))
-        hip.hipEventDestroy(ctypes.c_void_p(b))
-    k_avg_s = (sum(kms) / len(kms)) * 1e-3 if kms else float("nan")
-
-    rbh, rbf = H // 64 * 36, F // 64 * 36
-    per_expert = 2 * F * rbh + H * rbf
-    uniq = statistics.mean(D["uniq"])
-    unique_bytes = uniq * per_expert
-    useful_flops = 6.0 * P * H * F
-    s = ms_per_step * 1e-3
-    med = statistics.median(per)
-    layer = {"us_mean": ms_per_step * 1e3, "us_min": min(per) * 1e3, "us_median": med * 1e3,
-             "spread": (max(per) - min(per)) / med if med > 0 else None}
+    name = args.workload
+    T = args.T or DEFAULT_T[name]
+    t_wall = time.perf_counter()
+    D = build_inputs(name, T, args.U if name == "verify_chunk" else None, args.warm, args.virtual,
+                     torch, gen, moe)
+    res = measure(D, path, K, W, q, torch, moe)
+    decode = res["decode"]
+    kname = "gu_decode_kernel" if decode else "gemm_kernel<false>"   # gate/up (+ SiLU)
+    kr = res["kernels"][kname]
     if decode:
-        value, unit = unique_bytes / s / 1e9, "GB/s"
-        gu_bytes = uniq * 2 * F * rbh + T * H * 2 + P * F * 4
-        roof = {"bound": "hbm", "kernel": kname, "achieved": gu_bytes / k_avg_s / 1e9,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "bytes_per_launch": gu_bytes, "avg_launch_us": k_avg_s * 1e6, "launches": len(kms)}
-        roof["frac"] = roof["achieved"] / roof["peak"]
+        value, unit = res["unique_gbs"], "GB/s"
+        roof = {"bound": "hbm", "kernel": kname, "achieved": kr["achieved"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "bytes_per_launch": kr["per_launch"]}
     else:
-        value, unit = useful_flops / s / 1e12, "TFLOP/s"
-        gu_flops = 4.0 * P * H * F
-        roof = {"bound": "mfma", "kernel": kname, "achieved": gu_flops / k_avg_s / 1e12,
-                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": gu_flops,
-                "avg_launch_us": k_avg_s * 1e6, "launches": len(kms)}
-        roof["frac"] = roof["achieved"] / roof["peak"]
+        value, unit = res["useful_tflops"], "TFLOP/s"
+        roof = {"bound": "mfma", "kernel": kname, "achieved": kr["achieved"],
+                "peak": F16_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": kr["per_launch"]}
+    roof.update(frac=kr["frac"], avg_launch_us=kr["avg_launch_us"], launches=kr["launches"])
     tr = measured_traffic(kname, D["name"], T, D["U"] if D["name"] == "verify_chunk" else None)
     roof["traffic"] = tr["bytes"] if tr else None
     if tr:
-        # prefill gate/up: the unique experts' gate and up weights, x (f16) once, h hi + lo
-        alg = gu_bytes if decode else uniq * 2 * F * rbh + T * H * 2 + P * F * 4
         roof["traffic_detail"] = tr
-        roof["traffic_over_algorithmic"] = tr["bytes"] / alg
 
+    desc, note = describe(D), hbm_note(D, args.warm)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, D, gen, unit, per_expert)
+        cpu = cpu_baseline(args, D, unit)
 
-    # weights cycled through by the steps: a cyclic sweep larger than the 256 MB Infinity Cache
-    # misses it; a smaller one can stay resident
-    cycled = min(E, sum(D["uniq"])) * per_expert * D["copies"]
-    if args.warm:
-        hbm_note = "warm (one routing reused)"
-    elif cycled < 256e6:
-        hbm_note = (f"cache-resident: {cycled / 1e6:.1f} MB of weights in rotation, under the "
-                    "256 MB Infinity Cache")
-    else:
-        hbm_note = (f"cold ({len(D['ids'])} routings over disjoint expert windows x "
-                    f"{D['copies']} bank copies, {cycled / 1e6:.0f} MB of weights in rotation)")
-    wl = D["name"]
-    desc = {"verify_chunk": f"verify chunk: E={E} H={H} F={F} top-{k} T={T}, union U={D['U']}",
-            "tiny_decode": f"tiny decode: E={E} H={H} F={F} top-{k} T={T}",
-            "e256_plateau": f"rank-local E256 plateau: E={E} H={H} F={F} top-{k} T={T}",
-            "skewed_prefill": f"skewed prefill: E={E} H={H} F={F} top-{k} T={T}",
-            "full_prefill": f"full-width prefill: E={E} H={H} F={F} top-{k} T={T}",
-            "shared_expert": f"shared expert (dense SwiGLU, every token): H={H} F={F} T={T}, "
-                             f"as {D['virtual']} virtual experts over its one weight copy"}[wl]
+    rows = []
+    if args.rows == "all":
+        host_banks = {name: D["host"]["banks"]}
+        del D
+        torch.cuda.empty_cache()
+        for wl, Tr, Ur in ROWS:
+            if wl not in host_banks:
+                host_banks = {wl: make_banks_host(gen, wl)}   # one workload's banks at a time
+            Dr = build_inputs(wl, Tr, Ur, args.warm, 0, torch, gen, moe, host_banks[wl])
+            r = measure(Dr, moe.MOE_PATH_AUTO, K, W, q, torch, moe)
+            r.update(workload=describe(Dr), name=wl, T=Tr, U=Dr["U"], E=Dr["E"], H=Dr["H"],
+                     F=Dr["F"], top_k=Dr["k"], path="decode" if r["decode"] else "prefill",
+                     hbm=hbm_note(Dr, args.warm))
+            del r["decode"]
+            rows.append(r)
+            print(f"[row] {r['workload']}: {r['layer_us']['median']:.1f} us median, "
+                  f"{r['unique_gbs']:.0f} GB/s unique, {r['useful_tflops']:.1f} TFLOP/s",
+                  file=sys.stderr, flush=True)
+            del Dr
+            torch.cuda.empty_cache()
+
     out = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "warmup": W, "ms_per_step": res["ms_per_step"], "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": desc, "E": E, "H": H, "F": F, "top_k": k, "T": T,
-                   "path": "decode" if decode else "prefill",
-                   "hbm": hbm_note},
-        "layer": layer,
-        "unique_expert_bytes": unique_bytes,
-        "per_slot_bytes": P * per_expert,   # what a per-slot path would stream
-        "hbm_frac_unique": (unique_bytes / s / 1e9) / HBM_PEAK_GBS,
-        "useful_tflops": useful_flops / s / 1e12,
+        "config": {"workload": desc, "T": T, "path": "decode" if decode else "prefill",
+                   "hbm": note},
+        "layer": res["layer_us"],
+        "two_call_layer_us": res["two_call_layer_us"],
+        "unique_expert_bytes": res["unique_expert_bytes"],
+        "hbm_frac_unique": res["hbm_frac_unique"],
+        "useful_tflops": res["useful_tflops"],
+        "queue": res["queue"],
         "roofline": roof,
+        "kernels": res["kernels"],
         "cpu_baseline": cpu,
-        "wall_s_timed": wall,
+        "rows": rows,
+        "wall_s": time.perf_counter() - t_wall,
     }
     print(json.dumps(out), flush=True)
-
-
-def kernel_times_ms(moe, kid, K, step):
-    """Average of the library's HIP-event times of kernel `kid` over K more calls of step(i)."""
-    import torch
-    hip = _hip()
-    starts, stops = [], []
-    for _ in range(K):
-        a, b = ctypes.c_void_p(), ctypes.c_void_p()
-        hip.hipEventCreate(ctypes.byref(a))
-        hip.hipEventCreate(ctypes.byref(b))
-        starts.append(a.value)
-        stops.append(b.value)
-    torch.cuda.synchronize()
-    moe.moe_profile_kernel(kid, starts, stops)
-    for i in range(K):
-        step(i)
-    torch.cuda.synchronize()
-    n_rec = moe.moe_profile_count()
-    moe.moe_profile_kernel(moe.MOE_KERNEL_NONE, [], [])
-    kms = []
-    for i in range(n_rec):
-        f = ctypes.c_float()
-        hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(starts[i]), ctypes.c_void_p(stops[i]))
-        kms.append(f.value)
-    for a, b in zip(starts, stops):
-        hip.hipEventDestroy(ctypes.c_void_p(a))
-        hip.hipEventDestroy(ctypes.c_void_p(b))
-    return (sum(kms) / len(kms) if kms else float("nan")), len(kms)
 
 
 def bench_router(args, torch, gen, moe):
@@ -393,6 +519,7 @@ def bench_router(args, torch, gen, moe):
     import numpy as np
     import oracle
 
+    q = Queue(torch)
     T, E, k = args.T or 4096, args.E, args.k
     logits = gen.router_logits(11, T, E)
     lb = T * E * 4
@@ -410,18 +537,9 @@ def bench_router(args, torch, gen, moe):
     for i in range(args.warmup):
         step(i)
     K = args.steps
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(K):
-        step(args.warmup + i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / K
-    k_ms, n_k = kernel_times_ms(moe, moe.MOE_KERNEL_ROUTER, K, step)
+    per, qinfo = time_steps(q, step, K, args.warmup)
+    ms_per_step = sum(per) / K
+    k_ms, n_k = kernel_avg_ms(q, moe, moe.MOE_KERNEL_ROUTER, step, K, args.warmup + K)
     nbytes = lb + T * k * 8
     s = ms_per_step * 1e-3
     roof = {"bound": "hbm", "kernel": "router_topk_kernel", "achieved": nbytes / (k_ms * 1e-3) / 1e9,
@@ -442,7 +560,7 @@ def bench_router(args, torch, gen, moe):
         sec = el / reps * T / n
         cpu = {"value": nbytes / sec / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"{n} of the {T} tokens per repetition, scaled to the batch",
-               "seconds_per_batch": sec, "reps": reps}
+               "seconds_per_batch": sec, "reps": reps, **host_info()}
     out = {
         "metric": "router step µs + GB/s of logits read and ids/weights written",
         "value": nbytes / s / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
@@ -450,66 +568,79 @@ def bench_router(args, torch, gen, moe):
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"router top-{k}: E={E} T={T}, N(0,1) fp32 logits", "E": E,
                    "top_k": k, "T": T, "hbm": f"{copies} logits copies in rotation"},
-        "step_us": ms_per_step * 1e3,
+        "step_us": ms_per_step * 1e3, "queue": qinfo,
         "roofline": roof,
         "cpu_baseline": cpu,
-        "wall_s_timed": wall,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(args, D, gen, unit, per_expert):
-    """The fp64 oracle (union form) timed on the host cores on a bounded sample of the same
-    workload, scaled to the metric's unit."""
+def host_info():
+    """CPU model and core counts of this host."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_available": avail}
+
+
+def cpu_baseline(args, D, unit):
+    """The fp64 oracle (union form: each active expert decoded once, the experts shared out over
+    the threads) timed on the host cores on a bounded sample of the same workload, scaled to the
+    metric's unit; and once on one thread on the first token, for comparison. Threads: every
+    core this process may run on, up to OMP_NUM_THREADS when that is set (the host's CPU share)."""
     import numpy as np
 
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(os.cpu_count() or 1, 16)
+    hi = host_info()
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    threads = min(hi["cpus_available"], cap) if cap > 0 else hi["cpus_available"]
     name = D["name"]
-    w = gen.WORKLOADS[name]
     E, H, F, k, T = D.get("oracle_E", D["E"]), D["H"], D["F"], D["k"], D["T"]
-    banks = gen.make_banks(E, H, F, w["fused"], w["seed"])
     ids = D.get("oracle_ids", D["variants"][0])
-    if T * k <= 160 or name != "skewed_prefill" and name != "full_prefill":
+    per_expert = 2 * F * (H // 64 * 36) + H * (F // 64 * 36)
+    case = dict(E=E, H=H, F=F, k=k, T=T, ids=ids, w=D["host"]["w"], x=D["host"]["x"],
+                **D["host"]["banks"])
+    if T * k <= 1280:
         tok = None
-        sample = f"whole layer (all {T} tokens, {T * k} routed slots), union form"
+        sample = f"whole layer (all {T} tokens, {T * k} routed slots)"
     else:
         tok = np.arange(8)
-        sample = "8 of the layer's tokens (64 routed slots), per-slot form"
-    case = dict(E=E, H=H, F=F, k=k, T=T, ids=ids, w=D["host"]["w"], x=D["host"]["x"], **banks)
+        sample = f"8 of the layer's {T} tokens ({8 * k} routed slots)"
+
+    def rate(sec_, tokens):
+        sel = ids if tokens is None else ids[tokens]
+        if unit == "GB/s":
+            return len(np.unique(sel)) * per_expert / sec_ / 1e9
+        return 6.0 * sel.size * H * F / sec_ / 1e12
+
     t0 = time.perf_counter()
     reps = 0
     while True:
-        if tok is None:
-            oracle.ffn_union(case, threads=threads)
-        else:
-            oracle.ffn_per_slot(case, tokens=tok, threads=threads)
+        oracle.ffn_union(case, threads=threads, tokens=tok)
         reps += 1
         el = time.perf_counter() - t0
         if el >= args.cpu_seconds or el * (reps + 1) / reps > 30.0:
             break
     sec = el / reps
-
-    def rate(sec_, ids_, n_pairs):
-        if unit == "GB/s":
-            return len(np.unique(ids_)) * per_expert / sec_ / 1e9
-        return 6.0 * n_pairs * H * F / sec_ / 1e12
-
-    v = rate(sec, ids, T * k if tok is None else len(tok) * k)
-    # one thread, on the first token's slots (same form as above), once
     t1 = time.perf_counter()
-    if tok is None:
-        one = dict(case, T=1, ids=ids[:1], w=D["host"]["w"][:1], x=D["host"]["x"][:1])
-        oracle.ffn_union(one, threads=1)
-    else:
-        oracle.ffn_per_slot(case, tokens=np.arange(1), threads=1)
+    one = np.arange(1)
+    oracle.ffn_union(case, threads=1, tokens=one)
     sec1 = time.perf_counter() - t1
-    single = {"value": rate(sec1, ids[:1], k), "cores": 1,
-              "sample": f"the first token ({k} routed slots), "
-                        f"{'union' if tok is None else 'per-slot'} form, once",
-              "seconds_per_sample": sec1}
-    return {"value": v, "unit": unit, "cores": threads, "kind": "oracle", "sample": sample,
-            "seconds_per_sample": sec, "reps": reps, "single_thread": single}
+    single = {"value": rate(sec1, one), "cores": 1,
+              "sample": f"the first token ({k} routed slots), once", "seconds_per_sample": sec1}
+    return {"value": rate(sec, tok), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": sample + ", union form", "seconds_per_sample": sec, "reps": reps,
+            "single_thread": single, **hi}
 
 
 if __name__ == "__main__":

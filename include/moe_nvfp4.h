@@ -156,6 +156,32 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
                   moe_stream_t stream);
 
 /*
+ * Workspace bytes moe_layer_nvfp4 needs (for any path).
+ */
+size_t moe_layer_nvfp4_ws(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
+
+/*
+ * The whole routed layer in one call: moe_route_bucket followed by moe_ffn_nvfp4, from the routed
+ * expert ids to y (moe_sk_repro.rs, its host bucketing and the three grouped calls;
+ * moe_union_probe.rs, the fused gate/up + SiLU and down kernels it prices), without the CSR as
+ * an output. On the decode path with at most 2048 routed pairs and at most 1024 experts, the
+ * decode kernels bucket the pairs themselves (each workgroup in its LDS, into the same stable
+ * expert-first CSR) and no bucketing launch is made; otherwise the bucketing kernel runs first,
+ * into the workspace.
+ *   topk_ids, expert_base  as for moe_route_bucket (ids outside [expert_base, expert_base + E)
+ *                      are not routed).
+ *   x, topk_w, gate, up, down, T, k, E, H, F, y, path  as for moe_ffn_nvfp4.
+ *   ws, ws_bytes (device) scratch of at least moe_layer_nvfp4_ws(T, k, E, H, F) bytes, 256-byte
+ *                      aligned.
+ * y equals, bit for bit, what moe_route_bucket + moe_ffn_nvfp4 give on the same path (both
+ * paths are deterministic). Errors: as for moe_ffn_nvfp4 (MOE_EINVAL also for a null topk_ids).
+ */
+int moe_layer_nvfp4(const int32_t *topk_ids, int32_t expert_base, const uint16_t *x,
+                    const float *topk_w, moe_bank gate, moe_bank up, moe_bank down, int32_t T,
+                    int32_t k, int32_t E, int32_t H, int32_t F, float *y, int32_t path, void *ws,
+                    size_t ws_bytes, moe_stream_t stream);
+
+/*
  * moe_ffn_nvfp4 without a workspace argument, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
  * The workspace is a library-owned device array of MOE_STATIC_WS_BYTES per GPU (held from the

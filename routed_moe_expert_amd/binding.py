@@ -50,6 +50,11 @@ def _load():
     l.moe_ffn_nvfp4.restype = ctypes.c_int
     l.moe_ffn_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
                                 i32, i32, i32, i32, i32, vp, i32, vp, sz, vp]
+    l.moe_layer_nvfp4_ws.restype = sz
+    l.moe_layer_nvfp4_ws.argtypes = [i32, i32, i32, i32, i32]
+    l.moe_layer_nvfp4.restype = ctypes.c_int
+    l.moe_layer_nvfp4.argtypes = [vp, i32, vp, vp, moe_bank, moe_bank, moe_bank, i32, i32, i32,
+                                  i32, i32, vp, i32, vp, sz, vp]
     l.moe_ffn_nvfp4_static.restype = ctypes.c_int
     l.moe_ffn_nvfp4_static.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
                                        i32, i32, i32, i32, i32, vp, i32, vp]
@@ -132,6 +137,19 @@ def moe_ffn_nvfp4(x, topk_w, offsets, pair_ids, active, counts, gate: moe_bank, 
                            _ptr(counts), gate, up, down, T, k, E, H, F, _ptr(y), path, _ptr(ws),
                            ws_bytes, _stream(stream))
     return _check("moe_ffn_nvfp4", st, raise_on_error)
+
+
+def moe_layer_nvfp4_ws(T: int, k: int, E: int, H: int, F: int) -> int:
+    return int(lib.moe_layer_nvfp4_ws(T, k, E, H, F))
+
+
+def moe_layer_nvfp4(topk_ids, expert_base: int, x, topk_w, gate: moe_bank, up: moe_bank,
+                    down: moe_bank, T: int, k: int, E: int, H: int, F: int, y,
+                    path: int = MOE_PATH_AUTO, ws=None, ws_bytes: int = 0, stream=None,
+                    raise_on_error: bool = True) -> int:
+    st = lib.moe_layer_nvfp4(_ptr(topk_ids), expert_base, _ptr(x), _ptr(topk_w), gate, up, down,
+                             T, k, E, H, F, _ptr(y), path, _ptr(ws), ws_bytes, _stream(stream))
+    return _check("moe_layer_nvfp4", st, raise_on_error)
 
 
 MOE_STATIC_WS_BYTES = 128 << 20

@@ -79,6 +79,65 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
     return path == MOE_PATH_DECODE ? launch_decode(a, s) : launch_prefill(a, s);
 }
 
+namespace {
+inline size_t a256(size_t b) { return (b + 255) & ~size_t(255); }
+// The fused layer's workspace: the CSR of its fallback path (offsets, pair_ids, active, counts,
+// the bucketing's own workspace), then the FFN's.
+size_t layer_csr_bytes(int32_t T, int32_t k, int32_t E) {
+    const size_t P = (size_t)T * k;
+    return a256(4 * ((size_t)E + 1)) + a256(4 * P) + a256(4 * (size_t)E) + 256 +
+           a256(bucket_ws_bytes(T, k, E));
+}
+}  // namespace
+
+size_t moe_layer_nvfp4_ws(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
+    if (T < 0 || k < 1 || E < 1 || H < 1 || F < 1) return 0;
+    return layer_csr_bytes(T, k, E) + moe_ffn_nvfp4_ws(T, k, E, H, F);
+}
+
+int moe_layer_nvfp4(const int32_t *topk_ids, int32_t expert_base, const uint16_t *x,
+                    const float *topk_w, moe_bank gate, moe_bank up, moe_bank down, int32_t T,
+                    int32_t k, int32_t E, int32_t H, int32_t F, float *y, int32_t path, void *ws,
+                    size_t ws_bytes, moe_stream_t stream) {
+    int st = check_common(T, k, E);
+    if (st != MOE_OK) return st;
+    if (H < 64 || F < 64 || H % 64 || F % 64) return MOE_EINVAL;
+    if (H > MOE_MAX_HIDDEN || F > MOE_MAX_FF) return MOE_ESHAPE;
+    if (path < MOE_PATH_AUTO || path > MOE_PATH_PREFILL) return MOE_EINVAL;
+    if (T == 0) return MOE_OK;
+    if (!topk_ids || !x || !topk_w || !y || !ws) return MOE_EINVAL;
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return MOE_EINVAL;
+    if (!bank_ok(gate) || !bank_ok(up) || !bank_ok(down)) return MOE_EINVAL;
+    if (ws_bytes < moe_layer_nvfp4_ws(T, k, E, H, F)) return MOE_EWS;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const size_t csr = layer_csr_bytes(T, k, E);
+    uint8_t *b = static_cast<uint8_t *>(ws);
+    int32_t *offsets = reinterpret_cast<int32_t *>(b);
+    int32_t *pair_ids = reinterpret_cast<int32_t *>(b + a256(4 * ((size_t)E + 1)));
+    int32_t *active = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(pair_ids) +
+                                                  a256(4 * (size_t)T * k));
+    int32_t *counts = reinterpret_cast<int32_t *>(reinterpret_cast<uint8_t *>(active) +
+                                                  a256(4 * (size_t)E));
+    void *bws = reinterpret_cast<uint8_t *>(counts) + 256;
+    FfnArgs a{x, topk_w, offsets, pair_ids, active, counts, gate, up, down, T, k, E, H, F, y,
+              b + csr, ws_bytes - csr};
+    if (path == MOE_PATH_AUTO)
+        path = (T <= 128 && decode_supported(a)) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    if (path == MOE_PATH_DECODE) {
+        // bucketed inside the decode kernels when the routed pairs fit their LDS plan
+        FfnArgs f = a;
+        f.offsets = f.pair_ids = f.active = f.counts = nullptr;
+        f.ids = topk_ids;
+        f.expert_base = expert_base;
+        if (decode_fused_supported(f)) return launch_decode(f, s);
+        if (!decode_supported(a)) return MOE_ESHAPE;
+    }
+    // otherwise the bucketing kernel first, then the FFN over its CSR
+    st = launch_bucket(topk_ids, T, k, E, expert_base, offsets, pair_ids, active, counts, bws, s);
+    if (st != MOE_OK) return st;
+    return path == MOE_PATH_DECODE ? launch_decode(a, s) : launch_prefill(a, s);
+}
+
 int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
                     float *topk_w, moe_stream_t stream) {
     if (T < 0 || E < 1 || k < 1 || k > E) return MOE_EINVAL;

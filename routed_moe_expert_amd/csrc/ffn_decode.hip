@@ -309,6 +309,14 @@ __device__ __forceinline__ void item_range(int n_active, int tiles, int &i0, int
 __host__ __device__ inline int gu_pitch(int rb) { return rb % 16 == 0 ? rb + 16 : rb; }
 constexpr int kMaxTileInst = 10;   // loads per wave for one padded tile (hidden <= 4096)
 
+// Wait for every outstanding vector-memory operation with a real s_waitcnt (the builtin, which
+// the compiler's wait insertion understands, unlike an asm statement): registers loaded before
+// it are then known to be complete, and their first use after later direct-to-LDS loads does not
+// wait for those.
+__device__ __forceinline__ void wait_vm_all() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited on
+}
+
 __device__ __forceinline__ void dma16(const void *g, void *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
 }
@@ -318,8 +326,9 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
 // (1 when a bank has none).
 constexpr int kMaxMeta = 32;   // experts per workgroup range; grids are sized so this holds
 struct Meta {
-    int n_active;
+    int n_active, n_local;
     int e[kMaxMeta], q0[kMaxMeta], m[kMaxMeta], pid[kMaxMeta][kCols];
+    int pbase[kMaxMeta];   // first entry of expert a's pairs in the pair list (see plist_of)
     float s2a[kMaxMeta], s2b[kMaxMeta];
     const uint8_t *pa[kMaxMeta], *pb[kMaxMeta];
 };
@@ -388,6 +397,7 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
         meta.s2b[tid] = s2b ? s2b[e] : 1.f;
         meta.pa[tid] = expert_rows(wa, sa, ta, e);
         meta.pb[tid] = (wb || tb) ? expert_rows(wb, sb, tb, e) : nullptr;
+        meta.pbase[tid] = q0;   // the pair list is the CSR's pair_ids
         // an active expert has m >= 1: entries past m re-read entry m - 1 and are then zeroed
         if (pairs_in_lds) {
 #pragma unroll
@@ -406,10 +416,222 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
     lds_barrier();
 }
 
-// Pair id of column n of token chunk c of expert a (chunks beyond the first read the CSR).
-__device__ __forceinline__ int chunk_pid(const Meta &meta, const int32_t *pair_ids, int a, int c,
+// The fused layer (moe_layer_nvfp4): the decode kernels bucket the routed pairs themselves, in
+// each workgroup's LDS, from the routed expert ids -- the same stable expert-first CSR as
+// moe_route_bucket (moe_sk_repro.rs, its host bucketing) -- so the layer needs no bucketing
+// launch. Up to kIdsMaxPairs pairs and kIdsMaxExperts experts.
+constexpr int kIdsMaxPairs = 2048;
+constexpr int kIdsMaxExperts = 1024;
+constexpr int kIdsPer = kIdsMaxPairs / kThreads;   // routed ids per thread
+
+// LDS of the fused plan. The early part (phase A only) lies in the ring region, which no tile
+// has reached yet: counts [E], offsets [E+1], active list [E], scan partials. The late part
+// (phase B, while the first tiles stream into the ring) lies after the partials and the pair
+// list: keys [P], active ranks [E], per-wave counts [kWaves][kMaxMeta], cursors [kMaxMeta].
+inline size_t ids_early_bytes(int E) { return 4 * (3 * (size_t)E + 1 + 16); }
+inline size_t ids_late_bytes(int E, int P) {
+    return 4 * ((size_t)P + (size_t)E + (kWaves + 1) * kMaxMeta);
+}
+
+struct IdsLds {
+    int32_t *cnt, *off, *act, *wsum;   // early
+    int32_t *key, *rank, *wc, *cur;    // late
+};
+
+__device__ __forceinline__ IdsLds ids_lds(uint8_t *ring, int32_t *late, int E, int P) {
+    IdsLds l;
+    l.cnt = reinterpret_cast<int32_t *>(ring);
+    l.off = l.cnt + E;
+    l.act = l.off + E + 1;
+    l.wsum = l.act + E;
+    l.key = late;
+    l.rank = l.key + P;
+    l.wc = l.rank + E;
+    l.cur = l.wc + kWaves * kMaxMeta;
+    return l;
+}
+
+// Exclusive scan of one int per thread over the workgroup; *total gets the sum. wsum: kWaves ints.
+__device__ int wg_exclusive_scan(int v, int *wsum, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    lds_barrier();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; w++) {
+        const int ws = wsum[w];
+        before += w < wave ? ws : 0;
+        tot += ws;
+    }
+    *total = tot;
+    lds_barrier();
+    return before + x - v;
+}
+
+// Phase A of the plan from the routed ids: load the P ids (one round trip) and histogram the
+// local expert of each pair; scan the counts into the CSR offsets and the non-empty flags into
+// the ascending active list (one scan: count and flag packed in one int, P <= 2^16); take the
+// item range and the experts' entries -- all that addressing the weight tiles needs.
+// An expert's CSR slots are offsets[e] + the rank of the pair among its pairs, as
+// moe_route_bucket lays them out.
+__device__ void plan_ids_a(Meta &meta, const IdsLds &l, const int32_t *__restrict__ ids,
+                           int expert_base, const uint8_t *wa, int64_t sa,
+                           const uint8_t *const *ta, const float *__restrict__ s2a,
+                           const uint8_t *wb, int64_t sb, const uint8_t *const *tb,
+                           const float *__restrict__ s2b, int E, int P, int tiles, int &i0,
+                           int &i1, int &a_first, int &na) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int key[kIdsPer];
+#pragma unroll
+    for (int u = 0; u < kIdsPer; u++) {   // one round trip; past P re-read ids[0]
+        const int p = u * kThreads + tid;
+        key[u] = ids[p < P ? p : 0];
+    }
+    for (int i = tid; i < E; i += kThreads) l.cnt[i] = 0;
+    lds_barrier();
+#pragma unroll
+    for (int u = 0; u < kIdsPer; u++) {
+        const int p = u * kThreads + tid;
+        const int64_t e = (int64_t)key[u] - expert_base;
+        const int kk = (e >= 0 && e < E) ? (int)e : -1;
+        if (p < P) {
+            l.key[p] = kk;
+            if (kk >= 0) atomicAdd(&l.cnt[kk], 1);
+        }
+    }
+    lds_barrier();
+    // each thread a contiguous run of experts; counts in the low 16 bits, flags above
+    const int per = (E + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, E), hi = min(lo + per, E);
+    int mine = 0;
+    for (int i = lo; i < hi; i++) {
+        const int c = l.cnt[i];
+        mine += c + (c > 0 ? 1 << 16 : 0);
+    }
+    int tot;
+    const int ex = wg_exclusive_scan(mine, l.wsum, &tot);
+    int run = ex & 0xffff, fl = ex >> 16;
+    for (int i = lo; i < hi; i++) {
+        const int c = l.cnt[i];
+        l.off[i] = run;
+        l.rank[i] = fl;
+        if (c > 0) l.act[fl++] = i;
+        run += c;
+    }
+    if (tid == 0) {
+        l.off[E] = tot & 0xffff;
+        meta.n_active = tot >> 16;
+        meta.n_local = tot & 0xffff;
+    }
+    lds_barrier();
+    item_range(meta.n_active, tiles, i0, i1);
+    a_first = i0 / tiles;
+    na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
+    if (wave == 0) {
+        const int e = lane < na ? l.act[a_first + lane] : 0;
+        const int m = lane < na ? l.cnt[e] : 0;
+        int x = m;   // inclusive scan of m over the workgroup's experts (na <= 32 lanes)
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (lane < na) {
+            meta.e[lane] = e;
+            meta.q0[lane] = l.off[e];
+            meta.m[lane] = m;
+            meta.pbase[lane] = x - m;
+            l.cur[lane] = x - m;
+            meta.s2a[lane] = s2a ? s2a[e] : 1.f;
+            meta.s2b[lane] = s2b ? s2b[e] : 1.f;
+            meta.pa[lane] = expert_rows(wa, sa, ta, e);
+            meta.pb[lane] = (wb || tb) ? expert_rows(wb, sb, tb, e) : nullptr;
+        }
+    }
+    lds_barrier();
+}
+
+// Phase B: list the pairs of the workgroup's own experts (a contiguous run of the active list) in
+// ascending pair id, expert by expert, into plist: per 256-pair step, a pair's rank among its
+// expert's pairs of the step is the population of a wave ballot below its lane plus the counts
+// of the waves before it, added to the expert's running cursor.
+// With pos != nullptr (gate/up), the workgroup that holds tile 0 of an expert writes the pair ->
+// CSR slot map of that expert's pairs, and workgroup 0 marks the non-local pairs and writes the
+// number of local pairs to *n_local.
+__device__ void plan_ids_b(Meta &meta, const IdsLds &l, int32_t *plist, int P, int tiles, int i0,
+                           int i1, int a_first, int na, int32_t *__restrict__ pos,
+                           int32_t *__restrict__ n_local) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    for (int c0 = 0; c0 < P; c0 += kThreads) {
+        const int p = c0 + tid;
+        int al = -1;   // the pair's expert among the workgroup's, or -1
+        if (p < P) {
+            const int kk = l.key[p];
+            if (kk >= 0) {
+                const int r = l.rank[kk] - a_first;
+                al = (r >= 0 && r < na) ? r : -1;
+            }
+        }
+        int rank = 0;
+        for (int a = 0; a < na; a++) {
+            const uint64_t mk = __ballot(al == a);
+            if (al == a) rank = __popcll(mk & below);
+            if (lane == 0) l.wc[wave * kMaxMeta + a] = __popcll(mk);
+        }
+        lds_barrier();
+        if (al >= 0) {
+            int at = l.cur[al] + rank;
+            for (int w = 0; w < wave; w++) at += l.wc[w * kMaxMeta + al];
+            plist[at] = p;
+        }
+        lds_barrier();
+        if (tid < na) {
+            int add = 0;
+#pragma unroll
+            for (int w = 0; w < kWaves; w++) add += l.wc[w * kMaxMeta + tid];
+            l.cur[tid] += add;
+        }
+        lds_barrier();
+    }
+    if (tid < na) {
+        const int m = meta.m[tid], b = meta.pbase[tid];
+#pragma unroll
+        for (int j = 0; j < kCols; j++) {   // entries past m re-read entry m - 1, then zeroed
+            const int v = plist[b + min(j, m - 1)];
+            meta.pid[tid][j] = j < m ? v : 0;
+        }
+    }
+    if (pos != nullptr) {
+        // pair -> CSR slot: by the holder of each expert's tile 0; non-local pairs by workgroup 0
+        for (int a = 0; a < na; a++) {
+            const int it0 = (a_first + a) * tiles;
+            if (it0 < i0 || it0 >= i1) continue;
+            const int m = meta.m[a], b = meta.pbase[a], q0 = meta.q0[a];
+            for (int j = tid; j < m; j += kThreads) pos[plist[b + j]] = q0 + j;
+        }
+        if (blockIdx.x == 0) {
+            for (int p = tid; p < P; p += kThreads)
+                if (l.key[p] < 0) pos[p] = 0x7fffffff;
+            if (tid == 0) *n_local = meta.n_local;
+        }
+    }
+    lds_barrier();
+}
+
+// Pair id of column n of token chunk c of expert a: chunk 0 from the plan, later chunks from the
+// pair list (the CSR's pair_ids, or the workgroup's LDS list of the fused layer).
+__device__ __forceinline__ int chunk_pid(const Meta &meta, const int32_t *plist, int a, int c,
                                          int n) {
-    return c == 0 ? meta.pid[a][n] : pair_ids[meta.q0[a] + c * kCols + n];
+    return c == 0 ? meta.pid[a][n] : plist[meta.pbase[a] + c * kCols + n];
 }
 
 // Gate/up + SiLU * up over the union of active experts; the four waves split K = hidden. A unit
@@ -427,7 +649,9 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const uint8_t *const *__restrict__ gate_tab, const uint8_t *__restrict__ up, int64_t up_stride,
     const uint8_t *const *__restrict__ up_tab, const float *__restrict__ gate_s2,
     const float *__restrict__ up_s2, int32_t k, int32_t P, int32_t E, int32_t H, int32_t F,
-    int32_t nbuf, int32_t ring_bytes, float *__restrict__ h, int32_t *__restrict__ pos) {
+    int32_t nbuf, int32_t ring_bytes, float *__restrict__ h, int32_t *__restrict__ pos,
+    const int32_t *__restrict__ ids, int32_t expert_base, int32_t T, int32_t tokcols,
+    int32_t *__restrict__ n_local) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = H / kBlockWeights * kBlockBytes;
     const int side = kGuO * rb;
@@ -441,11 +665,27 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     // K slices of NB blocks; a last slice may run past the row (reads clamp, operands zero)
     const int nblk = H / kBlockWeights, blk0 = wave * NB;
     const int tiles = F / kGuO;
+    // fused layer: the pair list and the plan's late scratch live in LDS behind the partials;
+    // else the pair list is the CSR's
+    const bool fused = ids != nullptr;
+    int32_t *lds_list = reinterpret_cast<int32_t *>(smem + ring_bytes + kRedBytes);
+    const int32_t *plist = fused ? lds_list : pair_ids;
+    const IdsLds il = ids_lds(smem, lds_list + P, E, P);
 
-    int i0, i1, a_first;
-    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, gate,
-              gate_stride, gate_tab, gate_s2, up, up_stride, up_tab, up_s2, E, P, tiles, i0, i1,
-              a_first);
+    // token columns (T <= 16): the B operand is every token's row of x, column n = token n, the
+    // same for every expert, so it is loaded now, beside the plan's loads; each expert then keeps
+    // the columns of its own pairs' tokens
+    u32x4_t xb[NB][2];
+    if (tokcols) fetch_x_operands<NB>(xb, n < T ? x + (int64_t)n * H : nullptr, blk0, nblk, q);
+
+    int i0, i1, a_first, na = 0;
+    if (fused)
+        plan_ids_a(meta, il, ids, expert_base, gate, gate_stride, gate_tab, gate_s2, up,
+                   up_stride, up_tab, up_s2, E, P, tiles, i0, i1, a_first, na);
+    else
+        load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, gate,
+                  gate_stride, gate_tab, gate_s2, up, up_stride, up_tab, up_s2, E, P, tiles, i0,
+                  i1, a_first);
     // load k of this wave moves LDS chunk p = 64 wave + 256 k + lane of the tile; its source
     // offset within the gate or up rows of the tile (sign bit: up) is the same for every tile.
     // Padded pitch: chunk p is chunk p % cpr of row p / cpr (the last one a copy of chunk 0).
@@ -453,16 +693,21 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const bool padded = pitch != rb;
     const int cpr = rb / 16 + 1, half = kGuO * rb / 16;
     const int units = padded ? 2 * kGuO * cpr : 2 * half;
+    // (row, chunk) of p stepped along kk without a division: p grows by kThreads per step
     int32_t src_off[kMaxTileInst];
+    {
+        int p = wave * 64 + lane, r = 0, c = p;
+        while (c >= cpr) { c -= cpr; r++; }
 #pragma unroll
-    for (int kk = 0; kk < kMaxTileInst; kk++) {
-        const int p = wave * 64 + kk * kThreads + lane;
-        if (padded) {
-            const int r = p / cpr, c = p - r * cpr;
-            src_off[kk] = ((r & (kGuO - 1)) * rb + (c == cpr - 1 ? 0 : c) * 16) |
-                          (r >= kGuO ? (int32_t)0x80000000 : 0);
-        } else {
-            src_off[kk] = p < half ? p * 16 : ((p - half) * 16) | (int32_t)0x80000000;
+        for (int kk = 0; kk < kMaxTileInst; kk++) {
+            if (padded)
+                src_off[kk] = ((r & (kGuO - 1)) * rb + (c == cpr - 1 ? 0 : c) * 16) |
+                              (r >= kGuO ? (int32_t)0x80000000 : 0);
+            else
+                src_off[kk] = p < half ? p * 16 : ((p - half) * 16) | (int32_t)0x80000000;
+            p += kThreads;
+            c += kThreads;
+            while (c >= cpr) { c -= cpr; r++; }
         }
     }
     const int n_inst = stage_async_count<kThreads>(units * 16);
@@ -485,19 +730,21 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
         if (++is == nbuf) is = 0;
     };
 
-    // reduction of a unit by one wave: lane -> (feature f, token column nn). One wave (rotating)
-    // takes it while the others go on, which measured faster than a quarter per wave.
+    // reduction of a unit by one wave: lane -> (feature f, pair nn of the unit). One wave
+    // (rotating) takes it while the others go on, which measured faster than a quarter per wave.
+    // A pair's column is its place in the token chunk, or with token columns its token.
     // (a_: the unit's expert index, for its first CSR slot and second-level gate and up scales)
     auto reduce = [&](const float *rp, int a_, int c, int t, int mt) {
         const int q0 = meta.q0[a_];
         const float sg = meta.s2a[a_], su = meta.s2b[a_];
         for (int o = lane; o < kGuO * mt; o += 64) {
             const int f = o & (kGuO - 1), nn = o / kGuO;
+            const int col = tokcols ? chunk_pid(meta, plist, a_, nn / kCols, nn % kCols) / k : nn;
             float g = 0.f, u = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; w++) {
-                g += rp[(w * kCols + nn) * 16 + f];
-                u += rp[(w * kCols + nn) * 16 + f + kGuO];
+                g += rp[(w * kCols + col) * 16 + f];
+                u += rp[(w * kCols + col) * 16 + f + kGuO];
             }
             g *= sg;
             u *= su;
@@ -505,33 +752,47 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
         }
     };
 
-    u32x4_t xb[NB][2];
     int xs = 0, cur_a = -1, cur_c = -1;
     auto fetch_x = [&](int a_, int c_) {   // token rows of chunk c_ of expert a_
         const int mt = min(kCols, meta.m[a_] - c_ * kCols);
         const uint16_t *row = nullptr;
-        if (n < mt) row = x + (int64_t)(chunk_pid(meta, pair_ids, a_, c_, n) / k) * H;
+        if (n < mt) row = x + (int64_t)(chunk_pid(meta, plist, a_, c_, n) / k) * H;
         fetch_x_operands<NB>(xb, row, blk0, nblk, q);
         cur_a = a_;
         cur_c = c_;
     };
-    // the token rows of the first unit are loaded with the first tile, before the rest of the
-    // ring: waiting for them then waits for one tile, not for every buffer in flight
-    if (i0 < i1) {
-        fetch_x(0, 0);
-        issue_next();
-        xs = convert_x_operands<NB>(xb, blk0, nblk);
+    // Start-up order: the token rows are complete (and the compiler told so by a real wait)
+    // before tile 0 is issued, so that their conversion to f16 -- about a thousand VALU
+    // instructions per wave -- runs while tile 0 is in flight (after a direct-to-LDS load the
+    // compiler would otherwise wait for everything outstanding before the first use of x). With
+    // token columns x was loaded beside the plan and the whole ring is issued at once (so that a
+    // workgroup's later tiles travel with every workgroup's first); otherwise the token rows come
+    // after the fused plan's phase B (pair lists) and the rest of the ring follows.
+    if (tokcols) {
+        if (i0 < i1) wait_vm_all();   // x landed with the plan's loads
+        for (int i = i0; i < min(i0 + nbuf, i1); i++) issue_next();   // the whole ring at once
+        if (i0 < i1) xs = convert_x_operands<NB>(xb, blk0, nblk);    // overlaps the ring
+        if (fused) plan_ids_b(meta, il, lds_list, P, tiles, i0, i1, a_first, na, pos, n_local);
+    } else {
+        if (fused) plan_ids_b(meta, il, lds_list, P, tiles, i0, i1, a_first, na, pos, n_local);
+        if (i0 < i1) {
+            fetch_x(0, 0);
+            wait_vm_all();   // the token rows first, so that their conversion overlaps tile 0
+            issue_next();
+            xs = convert_x_operands<NB>(xb, blk0, nblk);
+        }
+        for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
     }
-    for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
 
     int unit = 0, p_a = 0, p_c = 0, p_t = 0, p_mt = 0;
     int a = 0, t = i0 - a_first * tiles, slot = 0;   // item i: expert index, row tile, ring slot
     for (int i = i0; i < i1; i++) {
-        const int q0 = meta.q0[a], m = meta.m[a];
+        const int m = meta.m[a];
+        const int nch = tokcols ? 1 : (m + kCols - 1) / kCols;   // units of this item
         const uint8_t *wt = wb + slot * tile_bytes + n * pitch;   // this lane's row of the tile
-        for (int c = 0; c * kCols < m; c++, unit++) {
-            const int mt = min(kCols, m - c * kCols);
-            if (a != cur_a || c != cur_c) {   // token rows of this chunk
+        for (int c = 0; c < nch; c++, unit++) {
+            const int mt = tokcols ? m : min(kCols, m - c * kCols);
+            if (!tokcols && (a != cur_a || c != cur_c)) {   // token rows of this chunk
                 fetch_x(a, c);
                 xs = convert_x_operands<NB>(xb, blk0, nblk);
             }
@@ -541,7 +802,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
             lds_barrier();   // tile i and the previous unit's partials visible to all
             SliceA<NB> sa;
             read_slice<NB>(wt, blk0, nblk, q, sa);
-            if ((c + 1) * kCols >= m && i + nbuf < i1) {
+            if (c == nch - 1 && i + nbuf < i1) {
                 lds_barrier();   // tile i is in every wave's registers: refill its buffer
                 issue_next();
             }
@@ -571,9 +832,10 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
         if (wave == (unit - 1) % kWaves)
             reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
     }
-    // pair -> CSR slot map for the combine (not needed before it)
-    for (int q2 = blockIdx.x * kThreads + tid; q2 < P; q2 += gridDim.x * kThreads)
-        pos[pair_ids[q2]] = q2;
+    // pair -> CSR slot map for the combine (not needed before it; the fused plan wrote it)
+    if (!fused)
+        for (int q2 = blockIdx.x * kThreads + tid; q2 < P; q2 += gridDim.x * kThreads)
+            pos[pair_ids[q2]] = q2;
 }
 
 // Down projection over the union of active experts, same streaming scheme; an item is 16*RT
@@ -588,7 +850,8 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const uint8_t *__restrict__ down, int64_t down_stride,
     const uint8_t *const *__restrict__ down_tab, const float *__restrict__ down_s2,
     int32_t P, int32_t E, int32_t H, int32_t F, int32_t RT, int32_t nbuf, int32_t ring_bytes,
-    const float *__restrict__ h, float *__restrict__ ypair) {
+    const float *__restrict__ h, float *__restrict__ ypair, const int32_t *__restrict__ ids,
+    int32_t expert_base) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int rb = F / kBlockWeights * kBlockBytes;
     const int rows = 16 * RT, tile_bytes = rows * rb;
@@ -603,10 +866,21 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int nblk = F / kBlockWeights, blk0 = ks * NB;
     const int tiles = H / rows;
 
-    int i0, i1, a_first;
-    load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, down,
-              down_stride, down_tab, down_s2, nullptr, 0, nullptr, nullptr, E, P, tiles, i0, i1,
-              a_first);
+    // fused layer: the plan from the routed ids, the pair list and the plan's late scratch in
+    // LDS behind the partials
+    const bool fused = ids != nullptr;
+    int32_t *lds_list = reinterpret_cast<int32_t *>(smem + ring_bytes + kRedBytes);
+    const int32_t *plist = fused ? lds_list : pair_ids;
+    const IdsLds il = ids_lds(smem, lds_list + P, E, P);
+
+    int i0, i1, a_first, na = 0;
+    if (fused)
+        plan_ids_a(meta, il, ids, expert_base, down, down_stride, down_tab, down_s2, nullptr, 0,
+                   nullptr, nullptr, E, P, tiles, i0, i1, a_first, na);
+    else
+        load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, down,
+                  down_stride, down_tab, down_s2, nullptr, 0, nullptr, nullptr, E, P, tiles, i0,
+                  i1, a_first);
     if (i0 >= i1) return;
     const int n_inst = stage_async_count<kThreads>(tile_bytes);
     int ia = 0, it = i0 - a_first * tiles, is = 0;   // stream cursor
@@ -637,14 +911,21 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     auto locate_h = [&](int a_, int c_) {   // h row and pair id of column n of chunk c_ of a_
         const int mt = min(kCols, meta.m[a_] - c_ * kCols);
         h_row = n < mt ? h + (int64_t)(meta.q0[a_] + c_ * kCols + n) * F : nullptr;
-        pid_n = n < mt ? chunk_pid(meta, pair_ids, a_, c_, n) : 0;
+        pid_n = n < mt ? chunk_pid(meta, plist, a_, c_, n) : 0;
         cur_a = a_;
         cur_c = c_;
     };
-    // the h rows of the first unit are loaded with the first tile, before the rest of the ring
-    locate_h(0, 0);
+    // the h rows of the first unit (their CSR slots are known from phase A) are loaded with the
+    // first tile, before the rest of the ring; the fused plan's phase B (pair lists, for the
+    // output rows) runs while they stream in
+    {
+        const int mt = min(kCols, meta.m[0]);
+        h_row = n < mt ? h + (int64_t)(meta.q0[0] + n) * F : nullptr;
+    }
     fetch_h_operands<NB>(hh, hl, h_row, blk0, nblk, q);
     issue_next();
+    if (fused) plan_ids_b(meta, il, lds_list, P, tiles, i0, i1, a_first, na, nullptr, nullptr);
+    locate_h(0, 0);
     hs = convert_h_operands<NB>(hh, hl, blk0, nblk);
     for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
 
@@ -713,13 +994,13 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
 // One thread per 4 consecutive outputs of a token row; the grid's y dimension steps over the
 // tokens (it is capped on the host, so any T launches).
 __global__ __launch_bounds__(kThreads) void combine_kernel(
-    const float *__restrict__ w, const int32_t *__restrict__ pos, const int32_t *__restrict__ offsets,
-    int32_t E, const float *__restrict__ ypair, int32_t T, int32_t k, int32_t H,
-    float *__restrict__ y) {
+    const float *__restrict__ w, const int32_t *__restrict__ pos,
+    const int32_t *__restrict__ n_local_ptr, const float *__restrict__ ypair, int32_t T, int32_t k,
+    int32_t H, float *__restrict__ y) {
     constexpr int kJ = 16;  // slots whose loads are issued together (one round trip for k <= 16)
     const int r = (blockIdx.x * kThreads + threadIdx.x) * 4;
     if (r >= H) return;
-    const int n_local = offsets[E];
+    const int n_local = *n_local_ptr;
     for (int t = blockIdx.y; t < T; t += gridDim.y) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
         for (int j0 = 0; j0 < k; j0 += kJ) {
@@ -751,9 +1032,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(
 }
 
 struct DecodeWs {
-    int32_t *pos;   // [P]
-    float *h;       // [P][F]
-    float *ypair;   // [P][H]
+    int32_t *pos;       // [P]
+    int32_t *n_local;   // [1] local pairs (fused layer: written by the gate/up kernel)
+    float *h;           // [P][F]
+    float *ypair;       // [P][H]
 };
 
 inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
@@ -763,6 +1045,8 @@ DecodeWs carve(void *ws, int32_t P, int32_t H, int32_t F) {
     DecodeWs d;
     d.pos = reinterpret_cast<int32_t *>(b);
     b += align256(sizeof(int32_t) * (size_t)P);
+    d.n_local = reinterpret_cast<int32_t *>(b);
+    b += 256;
     d.h = reinterpret_cast<float *>(b);
     b += align256(sizeof(float) * (size_t)P * F);
     d.ypair = reinterpret_cast<float *>(b);
@@ -783,17 +1067,17 @@ bool set_lds_attr(const void *fn, size_t total) {
 size_t decode_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
     (void)E;
     const size_t P = (size_t)T * k;
-    return align256(sizeof(int32_t) * P) + align256(sizeof(float) * P * F) +
+    return align256(sizeof(int32_t) * P) + 256 + align256(sizeof(float) * P * F) +
            align256(sizeof(float) * P * H);
 }
 
-int launch_combine(const float *w, const int32_t *pos, const int32_t *offsets, int32_t E,
-                   const float *ypair, int32_t T, int32_t k, int32_t H, float *y, hipStream_t s) {
+int launch_combine(const float *w, const int32_t *pos, const int32_t *n_local, const float *ypair,
+                   int32_t T, int32_t k, int32_t H, float *y, hipStream_t s) {
     // grid.y is limited to 65535: tokens beyond it are looped over inside the kernel
     dim3 grid((H / 4 + kThreads - 1) / kThreads, std::min<int32_t>(T, 32768));
     prof_start(MOE_KERNEL_COMBINE, s);
-    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, w, pos, offsets, E, ypair, T,
-                       k, H, y);
+    hipLaunchKernelGGL(combine_kernel, grid, dim3(kThreads), 0, s, w, pos, n_local, ypair, T, k,
+                       H, y);
     prof_stop(MOE_KERNEL_COMBINE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
@@ -814,9 +1098,11 @@ int64_t max_experts(int64_t n_items, int64_t tiles, int grid) {
 // Two workgroups per CU with two tile buffers each when the LDS holds them (both in flight while
 // a tile is computed from registers: measured as fast as three, the streaming rate being set
 // elsewhere), else one with as many as fit (at most kMaxBuf). The ring region also holds the
-// start-up scratch, so it is at least that large. Returns the dynamic LDS bytes (0: does not fit).
-size_t ring_plan(size_t tile, size_t scratch, int &nbuf, int &ring_bytes, int &wgs) {
-    const size_t fixed = kRedBytes + sizeof(Meta);
+// start-up scratch, so it is at least that large; `extra` bytes (the fused layer's pair list and
+// late plan scratch) follow the partials. Returns the dynamic LDS bytes (0: does not fit).
+size_t ring_plan(size_t tile, size_t scratch, size_t extra, int &nbuf, int &ring_bytes,
+                 int &wgs) {
+    const size_t fixed = kRedBytes + sizeof(Meta) + extra;
     const size_t scr = (scratch + 15) & ~size_t(15);
     if (2 * (std::max(2 * tile, scr) + fixed) <= kLds) {
         nbuf = 2;
@@ -829,112 +1115,128 @@ size_t ring_plan(size_t tile, size_t scratch, int &nbuf, int &ring_bytes, int &w
     const size_t ring = std::max(nbuf * tile, scr);
     if (ring + fixed > kLds) return 0;
     ring_bytes = (int)ring;
-    return ring + kRedBytes;
+    return ring + kRedBytes + extra;
+}
+
+// Everything the two decode launches need, settled on the host before either is enqueued.
+struct DecodeCfg {
+    int nb_gu, nb_dn, rt;
+    bool fused, tokcols;
+    int gu_nbuf, gu_ring, gu_grid, dn_nbuf, dn_ring, dn_grid;
+    size_t gu_lds, dn_lds;
+};
+
+// Gate/up: the four waves split hidden into slices of NB = ceil(blocks / 4) NVFP4 blocks.
+// Down: the smallest K split KS in {1, 2, 4} with at most kMaxDnBlocks blocks per slice, and
+// RT = 4 / KS row tiles per item; H must hold whole items, and two tiles plus the start-up
+// scratch must fit in LDS. fused: the plan is built from the routed ids (a.ids).
+int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
+    const int bh = a.H / kBlockWeights, bf = a.F / kBlockWeights;
+    c.nb_gu = (bh + kWaves - 1) / kWaves;
+    int ks = 1;
+    while (ks < kWaves && (bf + ks - 1) / ks > kMaxDnBlocks) ks *= 2;
+    c.nb_dn = (bf + ks - 1) / ks;
+    c.rt = kWaves / ks;
+    if (c.nb_gu > kMaxGuBlocks || c.nb_dn > kMaxDnBlocks || a.H % (16 * c.rt)) return MOE_ESHAPE;
+    const int32_t P = a.T * a.k;
+    if (fused && (P > kIdsMaxPairs || a.E > kIdsMaxExperts)) return MOE_ESHAPE;
+    c.fused = fused;
+    c.tokcols = a.T <= kCols;
+    const size_t scratch = fused ? ids_early_bytes(a.E) : plan_scratch_bytes(a.E, P);
+    const size_t extra = fused ? sizeof(int32_t) * (size_t)P + ids_late_bytes(a.E, P) : 0;
+    const int max_active = (int)std::min<int64_t>(a.E, (int64_t)P);
+    int wgs;
+    c.gu_lds = ring_plan(2 * kGuO * (size_t)gu_pitch((int)row_bytes(a.H)), scratch, extra,
+                         c.gu_nbuf, c.gu_ring, wgs);
+    if (!c.gu_lds) return MOE_ESHAPE;
+    const int gu_tiles = a.F / kGuO;
+    c.gu_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * gu_tiles);
+    if (max_experts((int64_t)max_active * gu_tiles, gu_tiles, c.gu_grid) > kMaxMeta)
+        return MOE_ESHAPE;
+    const int rows = 16 * c.rt;
+    c.dn_lds = ring_plan(rows * (size_t)row_bytes(a.F), scratch, extra, c.dn_nbuf, c.dn_ring, wgs);
+    if (!c.dn_lds) return MOE_ESHAPE;
+    const int dn_tiles = a.H / rows;
+    c.dn_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * dn_tiles);
+    if (max_experts((int64_t)max_active * dn_tiles, dn_tiles, c.dn_grid) > kMaxMeta)
+        return MOE_ESHAPE;
+    return MOE_OK;
 }
 
 template <int NB>
-int launch_gu(const FfnArgs &a, const DecodeWs &d, int max_active, hipStream_t s) {
+int launch_gu(const FfnArgs &a, const DecodeWs &d, const DecodeCfg &c, hipStream_t s) {
     auto kern = gu_decode_kernel<NB>;
-    const int32_t P = a.T * a.k;
-    int nbuf, ring_bytes, wgs;
-    const size_t lds = ring_plan(2 * kGuO * (size_t)gu_pitch((int)row_bytes(a.H)),
-                                 plan_scratch_bytes(a.E, P), nbuf, ring_bytes, wgs);
-    if (!lds) return MOE_ESHAPE;
     static bool attr = false;
     if (!attr) {
         if (!set_lds_attr(reinterpret_cast<const void *>(kern), kLds)) return MOE_ELAUNCH;
         attr = true;
     }
-    const int tiles = a.F / kGuO;
-    const int grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * tiles);
-    if (max_experts((int64_t)max_active * tiles, tiles, grid) > kMaxMeta) return MOE_ESHAPE;
     prof_start(MOE_KERNEL_GU_DECODE, s);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.x, a.offsets, a.pair_ids,
-                       a.active, a.counts, a.gate.base, a.gate.expert_stride, a.gate.experts,
-                       a.up.base, a.up.expert_stride, a.up.experts, a.gate.scale2, a.up.scale2, a.k,
-                       P, a.E, a.H, a.F, nbuf,
-                       ring_bytes, d.h, d.pos);
+    hipLaunchKernelGGL(kern, dim3(c.gu_grid), dim3(kThreads), c.gu_lds, s, a.x, a.offsets,
+                       a.pair_ids, a.active, a.counts, a.gate.base, a.gate.expert_stride,
+                       a.gate.experts, a.up.base, a.up.expert_stride, a.up.experts, a.gate.scale2,
+                       a.up.scale2, a.k, a.T * a.k, a.E, a.H, a.F, c.gu_nbuf, c.gu_ring, d.h, d.pos,
+                       a.ids, a.expert_base, a.T, c.tokcols ? 1 : 0, d.n_local);
     prof_stop(MOE_KERNEL_GU_DECODE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
 template <int NB>
-int launch_dn(const FfnArgs &a, const DecodeWs &d, int max_active, int RT, hipStream_t s) {
+int launch_dn(const FfnArgs &a, const DecodeWs &d, const DecodeCfg &c, hipStream_t s) {
     auto kern = dn_decode_kernel<NB>;
-    const int32_t P = a.T * a.k;
-    const int rows = 16 * RT;
-    int nbuf, ring_bytes, wgs;
-    const size_t lds = ring_plan(rows * (size_t)row_bytes(a.F), plan_scratch_bytes(a.E, P), nbuf,
-                                 ring_bytes, wgs);
-    if (!lds) return MOE_ESHAPE;
     static bool attr = false;
     if (!attr) {
         if (!set_lds_attr(reinterpret_cast<const void *>(kern), kLds)) return MOE_ELAUNCH;
         attr = true;
     }
-    const int tiles = a.H / rows;
-    const int grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * tiles);
-    if (max_experts((int64_t)max_active * tiles, tiles, grid) > kMaxMeta) return MOE_ESHAPE;
     prof_start(MOE_KERNEL_DN_DECODE, s);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a.offsets, a.pair_ids, a.active,
-                       a.counts, a.down.base, a.down.expert_stride, a.down.experts, a.down.scale2,
-                       P, a.E, a.H,
-                       a.F, RT, nbuf, ring_bytes, d.h, d.ypair);
+    hipLaunchKernelGGL(kern, dim3(c.dn_grid), dim3(kThreads), c.dn_lds, s, a.offsets, a.pair_ids,
+                       a.active, a.counts, a.down.base, a.down.expert_stride, a.down.experts,
+                       a.down.scale2, a.T * a.k, a.E, a.H, a.F, c.rt, c.dn_nbuf, c.dn_ring, d.h,
+                       d.ypair, a.ids, a.expert_base);
     prof_stop(MOE_KERNEL_DN_DECODE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-// Gate/up: the four waves split hidden into slices of NB = ceil(blocks / 4) NVFP4 blocks.
-// Down: the smallest K split KS in {1, 2, 4} with at most kMaxDnBlocks blocks per slice, and
-// RT = 4 / KS row tiles per item; H must hold whole items, and two tiles plus the start-up
-// scratch must fit in LDS.
-int decode_plan(const FfnArgs &a, int &nb_gu, int &nb_dn, int &rt) {
-    const int bh = a.H / kBlockWeights, bf = a.F / kBlockWeights;
-    nb_gu = (bh + kWaves - 1) / kWaves;
-    int ks = 1;
-    while (ks < kWaves && (bf + ks - 1) / ks > kMaxDnBlocks) ks *= 2;
-    nb_dn = (bf + ks - 1) / ks;
-    rt = kWaves / ks;
-    if (nb_gu > kMaxGuBlocks || nb_dn > kMaxDnBlocks || a.H % (16 * rt)) return MOE_ESHAPE;
-    const int32_t P = a.T * a.k;
-    int nbuf, ring, wgs;
-    if (!ring_plan(2 * kGuO * (size_t)gu_pitch((int)row_bytes(a.H)), plan_scratch_bytes(a.E, P), nbuf,
-                   ring, wgs) ||
-        !ring_plan(16 * rt * (size_t)row_bytes(a.F), plan_scratch_bytes(a.E, P), nbuf, ring, wgs))
-        return MOE_ESHAPE;
-    return MOE_OK;
-}
-
-}  // namespace
-
-bool decode_supported(const FfnArgs &a) {
-    int g, d, r;
-    return decode_plan(a, g, d, r) == MOE_OK;
-}
-
-int launch_decode(const FfnArgs &a, hipStream_t s) {
-    int nb_gu, nb_dn, rt;
-    if (int st = decode_plan(a, nb_gu, nb_dn, rt)) return st;
+int run_decode(const FfnArgs &a, const DecodeCfg &c, hipStream_t s) {
     const DecodeWs d = carve(a.ws, a.T * a.k, a.H, a.F);
-    const int max_active = (int)std::min<int64_t>(a.E, (int64_t)a.T * a.k);
     int st = MOE_OK;
-    switch (nb_gu) {
-#define MOE_GU(nb) case nb: st = launch_gu<nb>(a, d, max_active, s); break;
+    switch (c.nb_gu) {
+#define MOE_GU(nb) case nb: st = launch_gu<nb>(a, d, c, s); break;
         MOE_GU(1) MOE_GU(2) MOE_GU(3) MOE_GU(4) MOE_GU(5) MOE_GU(6) MOE_GU(7) MOE_GU(8)
         MOE_GU(9) MOE_GU(10) MOE_GU(11) MOE_GU(12) MOE_GU(13) MOE_GU(14) MOE_GU(15) MOE_GU(16)
 #undef MOE_GU
     default: return MOE_ESHAPE;
     }
     if (st != MOE_OK) return st;
-    switch (nb_dn) {
-#define MOE_DN(nb) case nb: st = launch_dn<nb>(a, d, max_active, rt, s); break;
+    switch (c.nb_dn) {
+#define MOE_DN(nb) case nb: st = launch_dn<nb>(a, d, c, s); break;
         MOE_DN(1) MOE_DN(2) MOE_DN(3) MOE_DN(4) MOE_DN(5)
         MOE_DN(6) MOE_DN(7) MOE_DN(8) MOE_DN(9) MOE_DN(10)
 #undef MOE_DN
     default: return MOE_ESHAPE;
     }
     if (st != MOE_OK) return st;
-    return launch_combine(a.w, d.pos, a.offsets, a.E, d.ypair, a.T, a.k, a.H, a.y, s);
+    return launch_combine(a.w, d.pos, c.fused ? d.n_local : a.offsets + a.E, d.ypair, a.T, a.k,
+                          a.H, a.y, s);
+}
+
+}  // namespace
+
+bool decode_supported(const FfnArgs &a) {
+    DecodeCfg c;
+    return decode_plan(a, false, c) == MOE_OK;
+}
+
+bool decode_fused_supported(const FfnArgs &a) {
+    DecodeCfg c;
+    return decode_plan(a, true, c) == MOE_OK;
+}
+
+int launch_decode(const FfnArgs &a, hipStream_t s) {
+    DecodeCfg c;
+    if (int st = decode_plan(a, a.ids != nullptr, c)) return st;
+    return run_decode(a, c, s);
 }
 
 }  // namespace moe

@@ -598,7 +598,7 @@ int launch_prefill(const FfnArgs &a, hipStream_t s) {
     if (st != MOE_OK) return st;
     st = launch_gemm<true>(a, w, mt, s);
     if (st != MOE_OK) return st;
-    return launch_combine(a.w, w.pos, a.offsets, a.E, w.ypair, a.T, a.k, a.H, a.y, s);
+    return launch_combine(a.w, w.pos, a.offsets + a.E, w.ypair, a.T, a.k, a.H, a.y, s);
 }
 
 }  // namespace moe

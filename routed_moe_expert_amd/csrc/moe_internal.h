@@ -110,25 +110,28 @@ int launch_bucket(const int32_t *ids, int32_t T, int32_t k, int32_t E, int32_t e
 struct FfnArgs {
     const uint16_t *x;
     const float *w;
-    const int32_t *offsets, *pair_ids, *active, *counts;
+    const int32_t *offsets, *pair_ids, *active, *counts;   // the CSR (null in the fused layer)
     moe_bank gate, up, down;
     int32_t T, k, E, H, F;
     float *y;
     void *ws;
     size_t ws_bytes;
+    const int32_t *ids = nullptr;   // fused layer: the routed expert ids, bucketed in-kernel
+    int32_t expert_base = 0;
 };
 
 size_t decode_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
 size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
-bool decode_supported(const FfnArgs &a);   // shape within the decode kernels' limits
+bool decode_supported(const FfnArgs &a);         // shape within the decode kernels' limits
+bool decode_fused_supported(const FfnArgs &a);   // ... and the in-kernel bucketing's
 int launch_decode(const FfnArgs &a, hipStream_t s);
 int launch_prefill(const FfnArgs &a, hipStream_t s);
 
 int launch_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids,
                        float *w, hipStream_t s);
 
-// y[t] = sum_j w[t,j] * ypair[pos[t*k+j]] over local slots; pos[p] >= n_local means non-local.
-int launch_combine(const float *w, const int32_t *pos, const int32_t *offsets, int32_t E,
-                   const float *ypair, int32_t T, int32_t k, int32_t H, float *y, hipStream_t s);
+// y[t] = sum_j w[t,j] * ypair[t*k+j] over local slots; pos[p] >= *n_local means non-local.
+int launch_combine(const float *w, const int32_t *pos, const int32_t *n_local, const float *ypair,
+                   int32_t T, int32_t k, int32_t H, float *y, hipStream_t s);
 
 }  // namespace moe

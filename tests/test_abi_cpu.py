@@ -169,3 +169,31 @@ def test_bank_keeps_its_tensors_alive():
     del b
     gc.collect()
     assert all(r() is None for r in refs)
+
+
+def _layer(**over):
+    a = dict(ids=FAKE, base=0, x=FAKE, topk_w=FAKE, gate=_bank(), up=_bank(), down=_bank(), T=4,
+             k=2, E=8, H=256, F=64, y=FAKE, path=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    return moe.moe_layer_nvfp4(a["ids"], a["base"], a["x"], a["topk_w"], a["gate"], a["up"],
+                               a["down"], a["T"], a["k"], a["E"], a["H"], a["F"], a["y"],
+                               a["path"], a["ws"], a["ws_bytes"], stream=0, raise_on_error=False)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(ids=0), moe.MOE_EINVAL), (dict(x=0), moe.MOE_EINVAL), (dict(y=0), moe.MOE_EINVAL),
+    (dict(ws=0), moe.MOE_EINVAL), (dict(T=-1), moe.MOE_EINVAL), (dict(k=0), moe.MOE_EINVAL),
+    (dict(H=96), moe.MOE_EINVAL), (dict(F=32), moe.MOE_EINVAL), (dict(path=3), moe.MOE_EINVAL),
+    (dict(up=_bank(FAKE + 8)), moe.MOE_EINVAL), (dict(ws=FAKE + 64), moe.MOE_EINVAL),
+    (dict(E=4096), moe.MOE_ESHAPE), (dict(T=1 << 22, k=8), moe.MOE_ESHAPE),
+    (dict(ws_bytes=1024), moe.MOE_EWS), (dict(T=0), moe.MOE_OK), (dict(T=0, ids=0), moe.MOE_OK),
+])
+def test_layer_host_checks(over, status):
+    assert _layer(**over) == status
+
+
+def test_layer_workspace_covers_the_two_calls():
+    for T, k, E, H, F in [(6, 10, 512, 2560, 640), (4096, 8, 288, 4096, 1280), (1, 1, 1, 64, 64)]:
+        ws = moe.moe_layer_nvfp4_ws(T, k, E, H, F)
+        assert ws >= moe.moe_ffn_nvfp4_ws(T, k, E, H, F) + moe.moe_route_bucket_ws(T, k, E)
+        assert ws >= 4 * (E + 1 + T * k + E + 2)
