@@ -1141,7 +1141,10 @@ int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     const int32_t P = a.T * a.k;
     if (fused && (P > kIdsMaxPairs || a.E > kIdsMaxExperts)) return MOE_ESHAPE;
     c.fused = fused;
-    c.tokcols = a.T <= kCols;
+    // token columns when most tokens hit each active expert (dense routing, e.g. a shared
+    // expert): every workgroup then loads all T token rows, which costs more than it saves when
+    // an expert holds only a pair or two (measured: tiny decode, the verify chunk, E256 T=16)
+    c.tokcols = a.T <= kCols && 2 * (int64_t)P >= (int64_t)a.T * std::min<int64_t>(a.E, P);
     const size_t scratch = fused ? ids_early_bytes(a.E) : plan_scratch_bytes(a.E, P);
     const size_t extra = fused ? sizeof(int32_t) * (size_t)P + ids_late_bytes(a.E, P) : 0;
     const int max_active = (int)std::min<int64_t>(a.E, (int64_t)P);
