@@ -37,14 +37,21 @@ F16_PEAK_TFLOPS = 2500.0     # MI355X dense MFMA, f16 and bf16 alike (the GEMMs 
 COPY_BYTES = 1 << 30
 
 # HBM traffic of the dominant kernel, per launch, from two rocprofv3 --pmc passes over
-# `bench.py --steps 20 --warmup 5 --rows none --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE,
-# KiB per dispatch, mean over the dispatches). Each counter is scaled by what it reads for
-# `bench.py --copy-calib` (a 1 GiB copy): FETCH_SIZE read 524301 KiB for 1048576 KiB moved, so
-# x2.0; WRITE_SIZE read 1048576 KiB, so x1.0. Keyed by the SHA-256 of the kernel's sources: once
+# `bench.py --rows none --no-cpu-baseline --layer-only --steps 20 --warmup 5` (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch, mean over the dispatches). Each counter is scaled by what it reads
+# for `bench.py --copy-calib` (a 1 GiB copy): FETCH_SIZE read 524302 KiB for 1048576 KiB moved,
+# so x2.0; WRITE_SIZE read 1048576 KiB, so x1.0. Keyed by the SHA-256 of the kernel's sources: once
 # they change, the entry no longer applies and traffic is reported as null until measured again.
-FETCH_SCALE = 1048576.0 / 524301.2
+FETCH_SCALE = 1048576.0 / 524302.3
 WRITE_SCALE = 1.0
-TRAFFIC = {}
+TRAFFIC = {
+    ("gu_decode_kernel", "verify_chunk", 6, 60): {
+        "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
+                    "routed_moe_expert_amd/csrc/moe_internal.h"],
+        "sha256": "aa57533171065ba870ad466847760c80132472999863ba926f33bc4534bfc03c",
+        "fetch_kib": 54383.3, "write_kib": 168.7,
+    },
+}
 
 # every configuration of the layer: (workload, tokens, union size for the verify chunk)
 ROWS = [("tiny_decode", 1, None), ("verify_chunk", 6, 10), ("verify_chunk", 6, 30),
@@ -101,6 +108,8 @@ def parse():
                     help="shared_expert: virtual experts over its one weight copy (0: T/16)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--warm", action="store_true", help="reuse one routing (cache-warm numbers)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="time only the one-call layer (not also the two calls), e.g. under a profiler")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calib", action="store_true",
@@ -352,17 +361,19 @@ def hbm_note(D, warm):
     return f"cold ({cycled / 1e6:.0f} MB of weights per step, over 2 x the Infinity Cache)"
 
 
-def measure(D, path_flag, K, W, q, torch, moe, kernels=True):
+def measure(D, path_flag, K, W, q, torch, moe, kernels=True, two_calls=True):
     """Times one workload: per-layer GPU times over K steps of the one-call layer
     (moe_layer_nvfp4), the path's two big kernels, and for comparison the layer as two calls
     (moe_route_bucket + moe_ffn_nvfp4)."""
     T = D["T"]
-    two = Layer(D, path_flag, torch, moe, fused=False)
-    for i in range(W):
-        two.step(i)
-    torch.cuda.synchronize()
-    per2, _ = time_steps(q, two.step, K, W)
-    del two
+    per2 = None
+    if two_calls:
+        two = Layer(D, path_flag, torch, moe, fused=False)
+        for i in range(W):
+            two.step(i)
+        torch.cuda.synchronize()
+        per2, _ = time_steps(q, two.step, K, W)
+        del two
     lay = Layer(D, path_flag, torch, moe)
     for i in range(W):
         lay.step(i)
@@ -380,8 +391,9 @@ def measure(D, path_flag, K, W, q, torch, moe, kernels=True):
         "layer_us": {"mean": mean_ms * 1e3, "min": min(per) * 1e3, "median": med * 1e3,
                      "spread": (max(per) - min(per)) / med if med > 0 else None},
         "ms_per_step": mean_ms, "decode": decode, "queue": qinfo,
-        "two_call_layer_us": {"mean": sum(per2) / len(per2) * 1e3,
-                              "median": statistics.median(per2) * 1e3, "min": min(per2) * 1e3},
+        "two_call_layer_us": None if per2 is None else {
+            "mean": sum(per2) / len(per2) * 1e3, "median": statistics.median(per2) * 1e3,
+            "min": min(per2) * 1e3},
         "unique_expert_bytes": uniq * per_expert,
         "unique_gbs": uniq * per_expert / s / 1e9,
         "hbm_frac_unique": uniq * per_expert / s / 1e9 / HBM_PEAK_GBS,
@@ -445,7 +457,7 @@ def main():
     t_wall = time.perf_counter()
     D = build_inputs(name, T, args.U if name == "verify_chunk" else None, args.warm, args.virtual,
                      torch, gen, moe)
-    res = measure(D, path, K, W, q, torch, moe)
+    res = measure(D, path, K, W, q, torch, moe, two_calls=not args.layer_only)
     decode = res["decode"]
     kname = "gu_decode_kernel" if decode else "gemm_kernel<false>"   # gate/up (+ SiLU)
     kr = res["kernels"][kname]
@@ -477,7 +489,7 @@ def main():
             if wl not in host_banks:
                 host_banks = {wl: make_banks_host(gen, wl)}   # one workload's banks at a time
             Dr = build_inputs(wl, Tr, Ur, args.warm, 0, torch, gen, moe, host_banks[wl])
-            r = measure(Dr, moe.MOE_PATH_AUTO, K, W, q, torch, moe)
+            r = measure(Dr, moe.MOE_PATH_AUTO, K, W, q, torch, moe, two_calls=not args.layer_only)
             r.update(workload=describe(Dr), name=wl, T=Tr, U=Dr["U"], E=Dr["E"], H=Dr["H"],
                      F=Dr["F"], top_k=Dr["k"], path="decode" if r["decode"] else "prefill",
                      hbm=hbm_note(Dr, args.warm))
