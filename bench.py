@@ -105,7 +105,8 @@ def parse():
     ap.add_argument("--T", type=int, default=None, help="tokens (workload default if unset)")
     ap.add_argument("--U", type=int, default=60, help="union size for verify_chunk")
     ap.add_argument("--virtual", type=int, default=0,
-                    help="shared_expert: virtual experts over its one weight copy (0: T/16)")
+                    help="shared_expert: route it as G caller-side virtual experts over its one "
+                         "weight copy (0: the one expert, E=1)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
     ap.add_argument("--warm", action="store_true", help="reuse one routing (cache-warm numbers)")
     ap.add_argument("--layer-only", action="store_true",
@@ -243,10 +244,10 @@ def build_inputs(name, T, U, warm, virtual, torch, gen, moe, host_banks=None):
         variants = [gen.route_union_rotated(seed, T, k, E, k, v)
                     for v in range(1 if warm else E // k)]
     elif name == "shared_expert":
-        # the one expert as G virtual experts (pointer tables onto its one copy), tokens dealt
-        # round-robin: the same dense SwiGLU with G times the work items
-        virtual = virtual or max(1, math.ceil(T / 16))
-        variants = [gen.shared_virtual_routing(T, virtual)[0]]
+        # the one expert (E = 1), or with virtual = G as G virtual experts (pointer tables onto
+        # its one copy, tokens dealt round-robin): the same dense SwiGLU
+        variants = [gen.shared_virtual_routing(T, virtual)[0] if virtual
+                    else np.zeros((T, 1), dtype=np.int32)]
     else:
         variants = [gen.make_routing(name, T)[0]]
         virtual = 0
@@ -421,8 +422,9 @@ def describe(D):
             "e256_plateau": f"rank-local E256 plateau: E={E} H={H} F={F} top-{k} T={T}",
             "skewed_prefill": f"skewed prefill: E={E} H={H} F={F} top-{k} T={T}",
             "full_prefill": f"full-width prefill: E={E} H={H} F={F} top-{k} T={T}",
-            "shared_expert": f"shared expert (dense SwiGLU, every token): H={H} F={F} T={T}, "
-                             f"as {D['virtual']} virtual experts over its one weight copy"}[D["name"]]
+            "shared_expert": f"shared expert (dense SwiGLU, every token): H={H} F={F} T={T}" +
+                             (f", as {D['virtual']} caller-side virtual experts over its one "
+                              f"weight copy" if D["virtual"] else ", E=1")}[D["name"]]
 
 
 def main():

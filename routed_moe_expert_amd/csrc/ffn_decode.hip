@@ -1,10 +1,15 @@
 // Decode path of the routed NVFP4 FFN (few tokens per expert, weight-stream bound).
 //
 // The union gather (moe_union_probe.rs: read each distinct expert's NVFP4 bytes once per call
-// instead of once per routed slot): work items are (active expert, tile of weight rows); each
-// item's NVFP4 tile is read from HBM once and contracted against every token routed to that
-// expert on the matrix cores, 16 tokens per MFMA column tile, so the cost of an item does not
-// grow with the expert's token count up to 16.
+// instead of once per routed slot): work items are (virtual expert, tile of weight rows); each
+// item's NVFP4 tile is read once and contracted against up to 16 tokens routed to that expert on
+// the matrix cores, one MFMA column tile, so the cost of an item does not grow with the expert's
+// token count up to 16. A virtual expert is a run of at most 16 of an expert's pairs in CSR
+// order: an expert with more tokens (a hot expert, a shared expert) becomes several, whose items
+// are dealt out like any others and run side by side on different CUs. The same tile is then
+// read once per virtual expert, close together in time (an L2 or last-level-cache hit for all
+// but the first), instead of one workgroup reloading its token rows -- behind every tile in
+// flight -- per 16-token chunk.
 //
 //   gu_decode: items of 8 gate rows + the 8 matching up rows = one 16-row MFMA A tile. The
 //              four waves split K = hidden into four slices. Each lane decodes the E2M1 codes
@@ -30,14 +35,15 @@
 // two steps per block.
 //
 // Both FFN kernels are persistent: a grid of one or two 256-thread workgroups per CU, read from
-// the device CSR (nothing is read back on the host). The (expert, tile) items are dealt out in
-// contiguous ranges over per-CU slots: each expert's tiles over a group of slots of its own where
-// there are no more active experts than slots and that costs at most one item over an even cut,
-// else an even cut of the item list; the two workgroups sharing a CU split their slot's range unevenly, since the
-// first dispatched runs ahead. Tiles stream through a ring of LDS buffers with direct-to-LDS loads (two per
-// workgroup with two workgroups per CU, up to six with one). Each wave copies its share of a
-// tile into registers first thing, and the buffer is refilled as soon as every wave has done
-// so, so all buffers are in flight while a tile is computed.
+// the device CSR (nothing is read back on the host). The (virtual expert, tile) items are dealt
+// out in contiguous ranges over per-CU slots: each virtual expert's tiles over a group of slots
+// of its own where there are no more of them than slots and that costs at most one item over an
+// even cut, else an even cut of the item list; the two workgroups sharing a CU split their
+// slot's range unevenly, since the first dispatched runs ahead. Tiles stream through a ring of
+// LDS buffers with direct-to-LDS loads (two per workgroup with two workgroups per CU, up to six
+// with one). Each wave copies its share of a tile into registers first thing, and the buffer is
+// refilled as soon as every wave has done so, so all buffers are in flight while a tile is
+// computed.
 #include <algorithm>
 
 #include "moe_internal.h"
@@ -254,7 +260,7 @@ __device__ __forceinline__ f32x4_t unscale(f32x4_t acc, int s) {
     return f32x4_t{ldexpf(acc[0], s), ldexpf(acc[1], s), ldexpf(acc[2], s), ldexpf(acc[3], s)};
 }
 
-// Item range of this workgroup: items are (active expert a, row tile t) in a-major order.
+// Item range of this workgroup: items are (virtual expert a, row tile t) in a-major order.
 //
 // Ranges are dealt to "slots": with a grid of two workgroups per CU, hardware places workgroups
 // 0..255 one per CU and 256..511 beside them, and under oldest-first issue arbitration the first
@@ -262,7 +268,7 @@ __device__ __forceinline__ f32x4_t unscale(f32x4_t acc, int s) {
 // finishes about 19% later than the first). So slot u is the pair (u, u + 256), and its range is
 // cut so that the first member takes kLeadNum / kLeadDen of it. Otherwise a slot is a workgroup.
 //
-// When the slots number at least the active experts without costing balance, each expert's tiles
+// When the slots number at least the virtual experts without costing balance, each one's tiles
 // are split over g slots and no workgroup changes expert: its token rows are loaded once, before
 // its stream of tiles starts, instead of at an expert change, where the load (vector memory
 // completes in issue order) would wait for every tile in flight. Otherwise the items are split
@@ -321,17 +327,27 @@ __device__ __forceinline__ void dma16(const void *g, void *lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_void_t *)lds, 16, 0, 0);
 }
 
-// The CSR entries a workgroup needs: its experts, their first CSR slot, pair count and first 16
-// pair ids, and for up to two banks the experts' first weight rows and second-level weight scales
-// (1 when a bank has none).
-constexpr int kMaxMeta = 32;   // experts per workgroup range; grids are sized so this holds
+// The CSR entries a workgroup needs, per virtual expert of its range: the expert, the first CSR
+// slot and pair count (at most kCols) of its run of pairs and their pair ids, and for up to two
+// banks the expert's first weight rows and second-level weight scales (1 when a bank has none).
+constexpr int kMaxMeta = 32;   // virtual experts per workgroup range; grids are sized so this holds
 struct Meta {
-    int n_active, n_local;
+    int n_active, n_local, n_real;   // n_active: virtual experts; n_real: see plan_ids_a
     int e[kMaxMeta], q0[kMaxMeta], m[kMaxMeta], pid[kMaxMeta][kCols];
-    int pbase[kMaxMeta];   // first entry of expert a's pairs in the pair list (see plist_of)
+    int pbase[kMaxMeta];   // first entry of the run's pairs in the fused plan's pair list
     float s2a[kMaxMeta], s2b[kMaxMeta];
     const uint8_t *pa[kMaxMeta], *pb[kMaxMeta];
 };
+
+// Virtual experts of an expert with m pairs: runs of kCols pairs, the last one shorter.
+__host__ __device__ inline int n_virtual(int m) { return (m + kCols - 1) / kCols; }
+
+// At most as many virtual experts as pairs, and at most one per active expert plus one per
+// kCols further pairs (the count a grid is sized for).
+__host__ __device__ inline int max_virtual(int E, int P) {
+    const int v = (E < P ? E : P) + P / kCols;
+    return v < P ? v : P;
+}
 
 // Expert e's first weight row in a bank: from the bank's per-expert pointer table when it has one,
 // else at base + e * stride.
@@ -342,113 +358,10 @@ __device__ __forceinline__ const uint8_t *expert_rows(const uint8_t *base, int64
 
 constexpr int kPairCap = 4096;   // pair ids read whole at start up to this many
 
-// LDS scratch of load_plan: the active list, the offsets and (up to kPairCap) the pair ids.
+// LDS scratch of load_plan: the active list, the offsets, (up to kPairCap) the pair ids, scan
+// partials and the workgroup's virtual experts (expert, run).
 inline size_t plan_scratch_bytes(int E, int P) {
-    return 4 * (2 * (size_t)E + 1 + (P <= kPairCap ? P : 0));
-}
-
-// This workgroup's item range and CSR entries. The counts, the whole active list, the whole
-// offsets array and (when short) all pair ids are fetched at once into LDS scratch, so start up
-// costs one round trip to memory instead of the chain counts -> active -> offsets -> pair ids.
-__device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restrict__ counts,
-                          const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
-                          const int32_t *__restrict__ pair_ids, const uint8_t *wa, int64_t sa,
-                          const uint8_t *const *ta, const float *__restrict__ s2a,
-                          const uint8_t *wb, int64_t sb, const uint8_t *const *tb,
-                          const float *__restrict__ s2b, int E, int P, int tiles, int &i0,
-                          int &i1, int &a_first) {
-    const int tid = threadIdx.x;
-    int32_t *s_act = scratch, *s_off = scratch + E, *s_pair = scratch + 2 * E + 1;
-    const bool pairs_in_lds = P <= kPairCap;
-    if (tid == 0) meta.n_active = counts[0];
-    // scratch[j] for j < total is entry j of active ++ offsets ++ pair_ids; each thread issues
-    // all of its loads of a batch before storing any, so the batch costs one memory round trip
-    constexpr int kBatch = 8;
-    const int total = 2 * E + 1 + (pairs_in_lds ? P : 0);
-    for (int base = 0; base < total; base += kBatch * kThreads) {
-        int32_t v[kBatch];
-#pragma unroll
-        for (int u = 0; u < kBatch; u++) {
-            const int j = base + u * kThreads + tid;
-            // a pointer select and one unconditional load (past the end: counts, always valid)
-            const int32_t *src = j < E       ? active + j
-                                 : j <= 2 * E ? offsets + (j - E)
-                                 : j < total  ? pair_ids + (j - 2 * E - 1)
-                                              : counts;
-            v[u] = *src;
-        }
-#pragma unroll
-        for (int u = 0; u < kBatch; u++) {
-            const int j = base + u * kThreads + tid;
-            if (j < total) scratch[j] = v[u];
-        }
-    }
-    lds_barrier();
-    item_range(meta.n_active, tiles, i0, i1);
-    a_first = i0 / tiles;
-    const int na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
-    if (tid < na) {
-        const int e = s_act[a_first + tid];
-        const int q0 = s_off[e], m = s_off[e + 1] - q0;
-        meta.e[tid] = e;
-        meta.q0[tid] = q0;
-        meta.m[tid] = m;
-        meta.s2a[tid] = s2a ? s2a[e] : 1.f;
-        meta.s2b[tid] = s2b ? s2b[e] : 1.f;
-        meta.pa[tid] = expert_rows(wa, sa, ta, e);
-        meta.pb[tid] = (wb || tb) ? expert_rows(wb, sb, tb, e) : nullptr;
-        meta.pbase[tid] = q0;   // the pair list is the CSR's pair_ids
-        // an active expert has m >= 1: entries past m re-read entry m - 1 and are then zeroed
-        if (pairs_in_lds) {
-#pragma unroll
-            for (int j = 0; j < kCols; j++) {
-                const int v = s_pair[q0 + min(j, m - 1)];
-                meta.pid[tid][j] = j < m ? v : 0;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < kCols; j++) {
-                const int v = pair_ids[q0 + min(j, m - 1)];
-                meta.pid[tid][j] = j < m ? v : 0;
-            }
-        }
-    }
-    lds_barrier();
-}
-
-// The fused layer (moe_layer_nvfp4): the decode kernels bucket the routed pairs themselves, in
-// each workgroup's LDS, from the routed expert ids -- the same stable expert-first CSR as
-// moe_route_bucket (moe_sk_repro.rs, its host bucketing) -- so the layer needs no bucketing
-// launch. Up to kIdsMaxPairs pairs and kIdsMaxExperts experts.
-constexpr int kIdsMaxPairs = 2048;
-constexpr int kIdsMaxExperts = 1024;
-constexpr int kIdsPer = kIdsMaxPairs / kThreads;   // routed ids per thread
-
-// LDS of the fused plan. The early part (phase A only) lies in the ring region, which no tile
-// has reached yet: counts [E], offsets [E+1], active list [E], scan partials. The late part
-// (phase B, while the first tiles stream into the ring) lies after the partials and the pair
-// list: keys [P], active ranks [E], per-wave counts [kWaves][kMaxMeta], cursors [kMaxMeta].
-inline size_t ids_early_bytes(int E) { return 4 * (3 * (size_t)E + 1 + 16); }
-inline size_t ids_late_bytes(int E, int P) {
-    return 4 * ((size_t)P + (size_t)E + (kWaves + 1) * kMaxMeta);
-}
-
-struct IdsLds {
-    int32_t *cnt, *off, *act, *wsum;   // early
-    int32_t *key, *rank, *wc, *cur;    // late
-};
-
-__device__ __forceinline__ IdsLds ids_lds(uint8_t *ring, int32_t *late, int E, int P) {
-    IdsLds l;
-    l.cnt = reinterpret_cast<int32_t *>(ring);
-    l.off = l.cnt + E;
-    l.act = l.off + E + 1;
-    l.wsum = l.act + E;
-    l.key = late;
-    l.rank = l.key + P;
-    l.wc = l.rank + E;
-    l.cur = l.wc + kWaves * kMaxMeta;
-    return l;
+    return 4 * (2 * (size_t)E + 1 + (P <= kPairCap ? P : 0) + 16 + 2 * kMaxMeta);
 }
 
 // Exclusive scan of one int per thread over the workgroup; *total gets the sum. wsum: kWaves ints.
@@ -474,12 +387,147 @@ __device__ int wg_exclusive_scan(int v, int *wsum, int *total) {
     return before + x - v;
 }
 
+// This workgroup's item range and CSR entries. The counts, the whole active list, the whole
+// offsets array and (when short) all pair ids are fetched at once into LDS scratch, so start up
+// costs one round trip to memory instead of the chain counts -> active -> offsets -> pair ids.
+// The virtual experts are then numbered by a scan of their counts over the active list (each
+// thread a contiguous run of it), and each thread enters those of its run that fall in the
+// workgroup's range.
+__device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restrict__ counts,
+                          const int32_t *__restrict__ active, const int32_t *__restrict__ offsets,
+                          const int32_t *__restrict__ pair_ids, const uint8_t *wa, int64_t sa,
+                          const uint8_t *const *ta, const float *__restrict__ s2a,
+                          const uint8_t *wb, int64_t sb, const uint8_t *const *tb,
+                          const float *__restrict__ s2b, int E, int P, int tiles, int &i0,
+                          int &i1, int &a_first) {
+    const int tid = threadIdx.x;
+    const bool pairs_in_lds = P <= kPairCap;
+    int32_t *s_act = scratch, *s_off = scratch + E, *s_pair = scratch + 2 * E + 1;
+    int32_t *s_wsum = s_pair + (pairs_in_lds ? P : 0), *s_ve = s_wsum + 16,
+            *s_vc = s_ve + kMaxMeta;
+    if (tid == 0) meta.n_real = counts[0];
+    // scratch[j] for j < total is entry j of active ++ offsets ++ pair_ids; each thread issues
+    // all of its loads of a batch before storing any, so the batch costs one memory round trip
+    constexpr int kBatch = 8;
+    const int total = 2 * E + 1 + (pairs_in_lds ? P : 0);
+    for (int base = 0; base < total; base += kBatch * kThreads) {
+        int32_t v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const int j = base + u * kThreads + tid;
+            // a pointer select and one unconditional load (past the end: counts, always valid)
+            const int32_t *src = j < E       ? active + j
+                                 : j <= 2 * E ? offsets + (j - E)
+                                 : j < total  ? pair_ids + (j - 2 * E - 1)
+                                              : counts;
+            v[u] = *src;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; u++) {
+            const int j = base + u * kThreads + tid;
+            if (j < total) scratch[j] = v[u];
+        }
+    }
+    lds_barrier();
+    const int n_act = meta.n_real;
+    const int per = (n_act + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, n_act), hi = min(lo + per, n_act);
+    int mine = 0;
+    for (int j = lo; j < hi; j++) {
+        const int e = s_act[j];
+        mine += n_virtual(s_off[e + 1] - s_off[e]);
+    }
+    int nv;
+    int v = wg_exclusive_scan(mine, s_wsum, &nv);
+    item_range(nv, tiles, i0, i1);
+    a_first = i0 / tiles;
+    const int na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
+    for (int j = lo; j < hi && v < a_first + na; j++) {
+        const int e = s_act[j], nch = n_virtual(s_off[e + 1] - s_off[e]);
+        for (int c = max(0, a_first - v); c < nch && v + c < a_first + na; c++) {
+            s_ve[v + c - a_first] = e;
+            s_vc[v + c - a_first] = c;
+        }
+        v += nch;
+    }
+    if (tid == 0) meta.n_active = nv;
+    lds_barrier();
+    if (tid < na) {
+        const int e = s_ve[tid], c = s_vc[tid];
+        const int q0 = s_off[e] + c * kCols, m = min(kCols, s_off[e + 1] - q0);
+        meta.e[tid] = e;
+        meta.q0[tid] = q0;
+        meta.m[tid] = m;
+        meta.s2a[tid] = s2a ? s2a[e] : 1.f;
+        meta.s2b[tid] = s2b ? s2b[e] : 1.f;
+        meta.pa[tid] = expert_rows(wa, sa, ta, e);
+        meta.pb[tid] = (wb || tb) ? expert_rows(wb, sb, tb, e) : nullptr;
+        // a run has m >= 1: entries past m re-read entry m - 1 and are then zeroed
+        if (pairs_in_lds) {
+#pragma unroll
+            for (int j = 0; j < kCols; j++) {
+                const int pv = s_pair[q0 + min(j, m - 1)];
+                meta.pid[tid][j] = j < m ? pv : 0;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kCols; j++) {
+                const int pv = pair_ids[q0 + min(j, m - 1)];
+                meta.pid[tid][j] = j < m ? pv : 0;
+            }
+        }
+    }
+    lds_barrier();
+}
+
+// The fused layer (moe_layer_nvfp4): the decode kernels bucket the routed pairs themselves, in
+// each workgroup's LDS, from the routed expert ids -- the same stable expert-first CSR as
+// moe_route_bucket (moe_sk_repro.rs, its host bucketing) -- so the layer needs no bucketing
+// launch. Up to kIdsMaxPairs pairs and kIdsMaxExperts experts.
+constexpr int kIdsMaxPairs = 2048;
+constexpr int kIdsMaxExperts = 1024;
+constexpr int kIdsPer = kIdsMaxPairs / kThreads;   // routed ids per thread
+
+// LDS of the fused plan. The early part (phase A only) lies in the ring region, which no tile
+// has reached yet: counts [E], offsets [E+1], the virtual expert list [max_virtual], scan
+// partials. The late part (phase B, while the first tiles stream into the ring) lies after the
+// partials and the pair list: keys [P], the workgroup's expert ranks [E], per-wave counts
+// [kWaves][kMaxMeta], cursors [kMaxMeta].
+inline size_t ids_early_bytes(int E, int P) {
+    return 4 * (2 * (size_t)E + 1 + (size_t)max_virtual(E, P) + 16);
+}
+inline size_t ids_late_bytes(int E, int P) {
+    return 4 * ((size_t)P + (size_t)E + (kWaves + 1) * kMaxMeta);
+}
+
+struct IdsLds {
+    int32_t *cnt, *off, *act, *wsum;   // early
+    int32_t *key, *rank, *wc, *cur;    // late
+};
+
+__device__ __forceinline__ IdsLds ids_lds(uint8_t *ring, int32_t *late, int E, int P) {
+    IdsLds l;
+    l.cnt = reinterpret_cast<int32_t *>(ring);
+    l.off = l.cnt + E;
+    l.act = l.off + E + 1;
+    l.wsum = l.act + max_virtual(E, P);
+    l.key = late;
+    l.rank = l.key + P;
+    l.wc = l.rank + E;
+    l.cur = l.wc + kWaves * kMaxMeta;
+    return l;
+}
+
 // Phase A of the plan from the routed ids: load the P ids (one round trip) and histogram the
-// local expert of each pair; scan the counts into the CSR offsets and the non-empty flags into
-// the ascending active list (one scan: count and flag packed in one int, P <= 2^16); take the
-// item range and the experts' entries -- all that addressing the weight tiles needs.
+// local expert of each pair; scan the counts into the CSR offsets and the virtual expert counts
+// into the ascending virtual expert list (one scan: both packed in one int, P <= 2^16), entries
+// expert | run << 16; take the item range and the virtual experts' entries -- all that
+// addressing the weight tiles needs.
 // An expert's CSR slots are offsets[e] + the rank of the pair among its pairs, as
-// moe_route_bucket lays them out.
+// moe_route_bucket lays them out. For phase B, the experts the workgroup's virtual experts belong
+// to (its "real" experts, a contiguous run of the active experts, so in ascending order) get
+// indices 0 .. n_real - 1 in rank[], and each the first entry of its whole pair list in cur[]
+// (pair lists of real experts follow each other; a run's pairs start kCols * run further in).
 __device__ void plan_ids_a(Meta &meta, const IdsLds &l, const int32_t *__restrict__ ids,
                            int expert_base, const uint8_t *wa, int64_t sa,
                            const uint8_t *const *ta, const float *__restrict__ s2a,
@@ -507,22 +555,21 @@ __device__ void plan_ids_a(Meta &meta, const IdsLds &l, const int32_t *__restric
         }
     }
     lds_barrier();
-    // each thread a contiguous run of experts; counts in the low 16 bits, flags above
+    // each thread a contiguous run of experts; pair counts in the low 16 bits, virtual counts above
     const int per = (E + kThreads - 1) / kThreads;
     const int lo = min(tid * per, E), hi = min(lo + per, E);
     int mine = 0;
     for (int i = lo; i < hi; i++) {
         const int c = l.cnt[i];
-        mine += c + (c > 0 ? 1 << 16 : 0);
+        mine += c + (n_virtual(c) << 16);
     }
     int tot;
     const int ex = wg_exclusive_scan(mine, l.wsum, &tot);
-    int run = ex & 0xffff, fl = ex >> 16;
+    int run = ex & 0xffff, v = ex >> 16;
     for (int i = lo; i < hi; i++) {
         const int c = l.cnt[i];
         l.off[i] = run;
-        l.rank[i] = fl;
-        if (c > 0) l.act[fl++] = i;
+        for (int r = 0; r < n_virtual(c); r++) l.act[v++] = i | r << 16;
         run += c;
     }
     if (tid == 0) {
@@ -535,54 +582,64 @@ __device__ void plan_ids_a(Meta &meta, const IdsLds &l, const int32_t *__restric
     a_first = i0 / tiles;
     na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
     if (wave == 0) {
-        const int e = lane < na ? l.act[a_first + lane] : 0;
-        const int m = lane < na ? l.cnt[e] : 0;
-        int x = m;   // inclusive scan of m over the workgroup's experts (na <= 32 lanes)
+        const int ent = lane < na ? l.act[a_first + lane] : 0;
+        const int e = ent & 0xffff, r = ent >> 16;
+        const int me = lane < na ? l.cnt[e] : 0;   // pairs of the whole expert
+        // a real expert starts at lane 0 and at every run 0
+        const bool start = lane < na && (lane == 0 || r == 0);
+        const uint64_t sm = __ballot(start);
+        const int ri = __popcll(sm & (~0ull >> (63 - lane))) - 1;   // its index
+        int x = start ? me : 0;   // inclusive scan over the lanes: lists of the real experts
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int y = __shfl_up(x, d, 64);
             if (lane >= d) x += y;
         }
         if (lane < na) {
+            const int first = x - me;   // the real expert's first list entry
             meta.e[lane] = e;
-            meta.q0[lane] = l.off[e];
-            meta.m[lane] = m;
-            meta.pbase[lane] = x - m;
-            l.cur[lane] = x - m;
+            meta.q0[lane] = l.off[e] + r * kCols;
+            meta.m[lane] = min(kCols, me - r * kCols);
+            meta.pbase[lane] = first + r * kCols;
             meta.s2a[lane] = s2a ? s2a[e] : 1.f;
             meta.s2b[lane] = s2b ? s2b[e] : 1.f;
             meta.pa[lane] = expert_rows(wa, sa, ta, e);
             meta.pb[lane] = (wb || tb) ? expert_rows(wb, sb, tb, e) : nullptr;
+            if (start) {
+                l.rank[e] = ri;
+                l.cur[ri] = first;
+            }
         }
+        if (lane == 0) meta.n_real = __popcll(sm);
     }
     lds_barrier();
 }
 
-// Phase B: list the pairs of the workgroup's own experts (a contiguous run of the active list) in
-// ascending pair id, expert by expert, into plist: per 256-pair step, a pair's rank among its
-// expert's pairs of the step is the population of a wave ballot below its lane plus the counts
-// of the waves before it, added to the expert's running cursor.
-// With pos != nullptr (gate/up), the workgroup that holds tile 0 of an expert writes the pair ->
-// CSR slot map of that expert's pairs, and workgroup 0 marks the non-local pairs and writes the
-// number of local pairs to *n_local.
+// Phase B: list the pairs of the workgroup's real experts in ascending pair id, expert by
+// expert, into plist: per 256-pair step, a pair's rank among its expert's pairs of the step is
+// the population of a wave ballot below its lane plus the counts of the waves before it, added
+// to the expert's running cursor. The workgroup's real experts are the active experts with ids
+// from its first virtual expert's to its last one's.
+// With pos != nullptr (gate/up), the workgroup that holds tile 0 of a virtual expert writes the
+// pair -> CSR slot map of that run's pairs, and workgroup 0 marks the non-local pairs and writes
+// the number of local pairs to *n_local.
 __device__ void plan_ids_b(Meta &meta, const IdsLds &l, int32_t *plist, int P, int tiles, int i0,
                            int i1, int a_first, int na, int32_t *__restrict__ pos,
                            int32_t *__restrict__ n_local) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int nr = na > 0 ? meta.n_real : 0;
+    const int e_lo = na > 0 ? meta.e[0] : 0, e_hi = na > 0 ? meta.e[na - 1] : -1;
     for (int c0 = 0; c0 < P; c0 += kThreads) {
         const int p = c0 + tid;
-        int al = -1;   // the pair's expert among the workgroup's, or -1
+        int al = -1;   // the pair's expert among the workgroup's real experts, or -1
         if (p < P) {
             const int kk = l.key[p];
-            if (kk >= 0) {
-                const int r = l.rank[kk] - a_first;
-                al = (r >= 0 && r < na) ? r : -1;
-            }
+            if (kk >= e_lo && kk <= e_hi) al = l.rank[kk];
         }
         int rank = 0;
-        for (int a = 0; a < na; a++) {
+        for (int a = 0; a < nr; a++) {
             const uint64_t mk = __ballot(al == a);
             if (al == a) rank = __popcll(mk & below);
             if (lane == 0) l.wc[wave * kMaxMeta + a] = __popcll(mk);
@@ -594,7 +651,7 @@ __device__ void plan_ids_b(Meta &meta, const IdsLds &l, int32_t *plist, int P, i
             plist[at] = p;
         }
         lds_barrier();
-        if (tid < na) {
+        if (tid < nr) {
             int add = 0;
 #pragma unroll
             for (int w = 0; w < kWaves; w++) add += l.wc[w * kMaxMeta + tid];
@@ -611,7 +668,7 @@ __device__ void plan_ids_b(Meta &meta, const IdsLds &l, int32_t *plist, int P, i
         }
     }
     if (pos != nullptr) {
-        // pair -> CSR slot: by the holder of each expert's tile 0; non-local pairs by workgroup 0
+        // pair -> CSR slot: by the holder of each run's tile 0; non-local pairs by workgroup 0
         for (int a = 0; a < na; a++) {
             const int it0 = (a_first + a) * tiles;
             if (it0 < i0 || it0 >= i1) continue;
@@ -627,18 +684,11 @@ __device__ void plan_ids_b(Meta &meta, const IdsLds &l, int32_t *plist, int P, i
     lds_barrier();
 }
 
-// Pair id of column n of token chunk c of expert a: chunk 0 from the plan, later chunks from the
-// pair list (the CSR's pair_ids, or the workgroup's LDS list of the fused layer).
-__device__ __forceinline__ int chunk_pid(const Meta &meta, const int32_t *plist, int a, int c,
-                                         int n) {
-    return c == 0 ? meta.pid[a][n] : plist[meta.pbase[a] + c * kCols + n];
-}
-
-// Gate/up + SiLU * up over the union of active experts; the four waves split K = hidden. A unit
-// of work is one item (or, past 16 tokens of an expert, one token chunk of it). A unit's first
-// barrier publishes tile i and the previous unit's partial tiles (double-buffered); once every
-// wave holds its slice of tile i in registers, a second barrier hands the buffer back to the
-// stream. One wave (rotating) then sums the previous unit's partials while the others contract.
+// Gate/up + SiLU * up over the union of active experts; the four waves split K = hidden. An
+// item's first barrier publishes tile i and the previous item's partial tiles (double-buffered);
+// once every wave holds its slice of tile i in registers, a second barrier hands the buffer back
+// to the stream. One wave (rotating) then sums the previous item's partials while the others
+// contract.
 // Tile i is awaited with "at most the memory operations issued after it outstanding": vector
 // memory operations complete in issue order, so that wait covers tile i and nothing newer.
 template <int NB>
@@ -669,7 +719,6 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     // else the pair list is the CSR's
     const bool fused = ids != nullptr;
     int32_t *lds_list = reinterpret_cast<int32_t *>(smem + ring_bytes + kRedBytes);
-    const int32_t *plist = fused ? lds_list : pair_ids;
     const IdsLds il = ids_lds(smem, lds_list + P, E, P);
 
     // token columns (T <= 16): the B operand is every token's row of x, column n = token n, the
@@ -730,16 +779,16 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
         if (++is == nbuf) is = 0;
     };
 
-    // reduction of a unit by one wave: lane -> (feature f, pair nn of the unit). One wave
+    // reduction of an item by one wave: lane -> (feature f, pair nn of the run). One wave
     // (rotating) takes it while the others go on, which measured faster than a quarter per wave.
-    // A pair's column is its place in the token chunk, or with token columns its token.
-    // (a_: the unit's expert index, for its first CSR slot and second-level gate and up scales)
-    auto reduce = [&](const float *rp, int a_, int c, int t, int mt) {
+    // A pair's column is its place in the run, or with token columns its token.
+    // (a_: the item's virtual expert, for its first CSR slot and second-level gate and up scales)
+    auto reduce = [&](const float *rp, int a_, int t, int mt) {
         const int q0 = meta.q0[a_];
         const float sg = meta.s2a[a_], su = meta.s2b[a_];
         for (int o = lane; o < kGuO * mt; o += 64) {
             const int f = o & (kGuO - 1), nn = o / kGuO;
-            const int col = tokcols ? chunk_pid(meta, plist, a_, nn / kCols, nn % kCols) / k : nn;
+            const int col = tokcols ? meta.pid[a_][nn] / k : nn;
             float g = 0.f, u = 0.f;
 #pragma unroll
             for (int w = 0; w < kWaves; w++) {
@@ -748,18 +797,16 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
             }
             g *= sg;
             u *= su;
-            h[(int64_t)(q0 + c * kCols + nn) * F + t * kGuO + f] = silu(g) * u;
+            h[(int64_t)(q0 + nn) * F + t * kGuO + f] = silu(g) * u;
         }
     };
 
-    int xs = 0, cur_a = -1, cur_c = -1;
-    auto fetch_x = [&](int a_, int c_) {   // token rows of chunk c_ of expert a_
-        const int mt = min(kCols, meta.m[a_] - c_ * kCols);
+    int xs = 0, cur_a = -1;
+    auto fetch_x = [&](int a_) {   // token rows of virtual expert a_
         const uint16_t *row = nullptr;
-        if (n < mt) row = x + (int64_t)(chunk_pid(meta, plist, a_, c_, n) / k) * H;
+        if (n < meta.m[a_]) row = x + (int64_t)(meta.pid[a_][n] / k) * H;
         fetch_x_operands<NB>(xb, row, blk0, nblk, q);
         cur_a = a_;
-        cur_c = c_;
     };
     // Start-up order: the token rows are complete (and the compiler told so by a real wait)
     // before tile 0 is issued, so that their conversion to f16 -- about a thousand VALU
@@ -776,7 +823,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     } else {
         if (fused) plan_ids_b(meta, il, lds_list, P, tiles, i0, i1, a_first, na, pos, n_local);
         if (i0 < i1) {
-            fetch_x(0, 0);
+            fetch_x(0);
             wait_vm_all();   // the token rows first, so that their conversion overlaps tile 0
             issue_next();
             xs = convert_x_operands<NB>(xb, blk0, nblk);
@@ -784,53 +831,49 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
         for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
     }
 
-    int unit = 0, p_a = 0, p_c = 0, p_t = 0, p_mt = 0;
-    int a = 0, t = i0 - a_first * tiles, slot = 0;   // item i: expert index, row tile, ring slot
+    int p_a = 0, p_t = 0, p_mt = 0;
+    int a = 0, t = i0 - a_first * tiles, slot = 0;   // item i: virtual expert, row tile, ring slot
     for (int i = i0; i < i1; i++) {
-        const int m = meta.m[a];
-        const int nch = tokcols ? 1 : (m + kCols - 1) / kCols;   // units of this item
+        const int mt = meta.m[a];
         const uint8_t *wt = wb + slot * tile_bytes + n * pitch;   // this lane's row of the tile
-        for (int c = 0; c < nch; c++, unit++) {
-            const int mt = tokcols ? m : min(kCols, m - c * kCols);
-            if (!tokcols && (a != cur_a || c != cur_c)) {   // token rows of this chunk
-                fetch_x(a, c);
-                xs = convert_x_operands<NB>(xb, blk0, nblk);
-            }
-            // tile i landed: issued after it are at least the tiles behind it (the reducing
-            // wave's h stores are not counted: they only make its wait stricter)
-            if (c == 0) vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst);
-            lds_barrier();   // tile i and the previous unit's partials visible to all
-            SliceA<NB> sa;
-            read_slice<NB>(wt, blk0, nblk, q, sa);
-            if (c == nch - 1 && i + nbuf < i1) {
-                lds_barrier();   // tile i is in every wave's registers: refill its buffer
-                issue_next();
-            }
-            if (unit > 0 && wave == (unit - 1) % kWaves)
-                reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
-            // two independent accumulation chains (K steps 0 and 1 of each block) halve the
-            // dependent MFMA latency
-            f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-            for (int j = 0; j < NB; j++) {
-                const f16x2_t S = scale_f16x2(sa.s[j]);
-                acc0 = mfma16(dequant8(sa.c[j][0], S), __builtin_bit_cast(f16x8_t, xb[j][0]), acc0);
-                acc1 = mfma16(dequant8(sa.c[j][1], S), __builtin_bit_cast(f16x8_t, xb[j][1]), acc1);
-            }
-            *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats + (wave * kCols + n) * 16 +
-                                         4 * q) = unscale(acc0 + acc1, xs);
-            p_a = a;
-            p_c = c;
-            p_t = t;
-            p_mt = mt;
+        if (!tokcols && a != cur_a) {   // token rows of this virtual expert
+            fetch_x(a);
+            xs = convert_x_operands<NB>(xb, blk0, nblk);
         }
+        // tile i landed: issued after it are at least the tiles behind it (the reducing wave's h
+        // stores are not counted: they only make its wait stricter)
+        vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst);
+        lds_barrier();   // tile i and the previous item's partials visible to all
+        SliceA<NB> sa;
+        read_slice<NB>(wt, blk0, nblk, q, sa);
+        if (i + nbuf < i1) {
+            lds_barrier();   // tile i is in every wave's registers: refill its buffer
+            issue_next();
+        }
+        const int u = i - i0;
+        if (u > 0 && wave == (u - 1) % kWaves)
+            reduce(red + ((u - 1) & 1) * kRedFloats, p_a, p_t, p_mt);
+        // two independent accumulation chains (K steps 0 and 1 of each block) halve the
+        // dependent MFMA latency
+        f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+            const f16x2_t S = scale_f16x2(sa.s[j]);
+            acc0 = mfma16(dequant8(sa.c[j][0], S), __builtin_bit_cast(f16x8_t, xb[j][0]), acc0);
+            acc1 = mfma16(dequant8(sa.c[j][1], S), __builtin_bit_cast(f16x8_t, xb[j][1]), acc1);
+        }
+        *reinterpret_cast<f32x4_t *>(red + (u & 1) * kRedFloats + (wave * kCols + n) * 16 +
+                                     4 * q) = unscale(acc0 + acc1, xs);
+        p_a = a;
+        p_t = t;
+        p_mt = mt;
         if (++t == tiles) { t = 0; ++a; }
         if (++slot == nbuf) slot = 0;
     }
-    if (unit > 0) {
+    if (i1 > i0) {
+        const int u = i1 - i0;
         lds_barrier();
-        if (wave == (unit - 1) % kWaves)
-            reduce(red + ((unit - 1) & 1) * kRedFloats, p_a, p_c, p_t, p_mt);
+        if (wave == (u - 1) % kWaves) reduce(red + ((u - 1) & 1) * kRedFloats, p_a, p_t, p_mt);
     }
     // pair -> CSR slot map for the combine (not needed before it; the fused plan wrote it)
     if (!fused)
@@ -842,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
 // down rows, wave w takes row tile w % RT and K slice w / RT of ff. With one K slice (RT = 4,
 // ff up to 640) every wave owns whole rows and stores them from registers; otherwise the slices
 // are summed through LDS like gate/up, a quarter of the outputs per wave. Either way every wave
-// issues at least one store per unit, which the ring waits count.
+// issues at least one store per item, which the ring waits count.
 template <int NB>
 __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
@@ -858,7 +901,7 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     uint8_t *wb = smem;                                                // [nbuf][rows]
     float *red = reinterpret_cast<float *>(smem + ring_bytes);         // [2][wave][col][16 rows]
     __shared__ Meta meta;
-    __shared__ int s_pid[2][kCols];   // pair ids of the token columns of the last two units
+    __shared__ int s_pid[2][kCols];   // pair ids of the token columns of the last two items
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;
@@ -870,7 +913,6 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
     // LDS behind the partials
     const bool fused = ids != nullptr;
     int32_t *lds_list = reinterpret_cast<int32_t *>(smem + ring_bytes + kRedBytes);
-    const int32_t *plist = fused ? lds_list : pair_ids;
     const IdsLds il = ids_lds(smem, lds_list + P, E, P);
 
     int i0, i1, a_first, na = 0;
@@ -899,95 +941,93 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
         for (int l = lane; l < Q; l += 64) {
             const int u = wave * Q + l, r = u % rows, nn = u / rows;
             float v = 0.f;
-            for (int s2 = 0; s2 < KS; s2++) v += rp[((s2 * RT + r / 16) * kCols + nn) * 16 + r % 16];
+            for (int s2 = 0; s2 < KS; s2++)
+                v += rp[((s2 * RT + r / 16) * kCols + nn) * 16 + r % 16];
             ypair[(int64_t)pids[nn] * H + t * rows + r] = v * sd;
         }
     };
 
     u32x4_t hh[NB][2], hl[NB][2];
-    int hs = 0, cur_a = -1, cur_c = -1;
-    int pid_n = 0;   // pair id of token column n of the current chunk (its ypair row)
+    int hs = 0, cur_a = -1;
+    int pid_n = 0;   // pair id of token column n of the current virtual expert (its ypair row)
     const float *h_row = nullptr;
-    auto locate_h = [&](int a_, int c_) {   // h row and pair id of column n of chunk c_ of a_
-        const int mt = min(kCols, meta.m[a_] - c_ * kCols);
-        h_row = n < mt ? h + (int64_t)(meta.q0[a_] + c_ * kCols + n) * F : nullptr;
-        pid_n = n < mt ? chunk_pid(meta, plist, a_, c_, n) : 0;
+    auto locate_h = [&](int a_) {   // h row and pair id of column n of virtual expert a_
+        const bool in = n < meta.m[a_];
+        h_row = in ? h + (int64_t)(meta.q0[a_] + n) * F : nullptr;
+        pid_n = in ? meta.pid[a_][n] : 0;
         cur_a = a_;
-        cur_c = c_;
     };
-    // the h rows of the first unit (their CSR slots are known from phase A) are loaded with the
+    // the h rows of the first item (their CSR slots are known from phase A) are loaded with the
     // first tile, before the rest of the ring; the fused plan's phase B (pair lists, for the
     // output rows) runs while they stream in
-    {
-        const int mt = min(kCols, meta.m[0]);
-        h_row = n < mt ? h + (int64_t)(meta.q0[0] + n) * F : nullptr;
-    }
+    h_row = n < meta.m[0] ? h + (int64_t)(meta.q0[0] + n) * F : nullptr;
     fetch_h_operands<NB>(hh, hl, h_row, blk0, nblk, q);
     issue_next();
     if (fused) plan_ids_b(meta, il, lds_list, P, tiles, i0, i1, a_first, na, nullptr, nullptr);
-    locate_h(0, 0);
+    locate_h(0);
     hs = convert_h_operands<NB>(hh, hl, blk0, nblk);
-    for (int i = i0 + 1; i < min(i0 + nbuf, i1); i++) issue_next();   // every buffer in flight
 
-    int unit = 0, p_t = 0, p_mt = 0;
+    int p_t = 0, p_mt = 0;
     float p_sd = 1.f;
-    int a = 0, t = i0 - a_first * tiles, slot = 0;
+    int a = 0, t = i0 - a_first * tiles, slot = 0, issued = i0 + 1;
     for (int i = i0; i < i1; i++) {
-        const int m = meta.m[a];
+        const int mt = meta.m[a], u = i - i0;
         const float sd = meta.s2a[a];
         const uint8_t *wt = wb + slot * tile_bytes + (rt * 16 + n) * rb;
-        for (int c = 0; c * kCols < m; c++, unit++) {
-            const int mt = min(kCols, m - c * kCols);
-            if (a != cur_a || c != cur_c) {
-                locate_h(a, c);
-                fetch_h_operands<NB>(hh, hl, h_row, blk0, nblk, q);
-                hs = convert_h_operands<NB>(hh, hl, blk0, nblk);
-            }
-            // tile i landed: issued after it are the tiles behind it and one store per wave and
-            // unit (from unit 1 on with KS > 1; a lower bound past one chunk or with two stores)
-            if (c == 0)
-                vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst +
-                           (KS == 1 ? min(nbuf, i - i0) : max(0, min(nbuf, i - i0 - 1))));
-            lds_barrier();
-            if (KS > 1 && wave == 0 && lane < kCols) s_pid[unit & 1][lane] = pid_n;
-            SliceA<NB> sa;
-            read_slice<NB>(wt, blk0, nblk, q, sa);
-            if ((c + 1) * kCols >= m && i + nbuf < i1) {
-                lds_barrier();   // tile i is in every wave's registers: refill its buffer
-                issue_next();
-            }
-            if (KS > 1 && unit > 0)
-                reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt, p_sd);
-            // hi and lo parts accumulate in two independent chains (half the dependent latency)
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acl = acc;
-#pragma unroll
-            for (int j = 0; j < NB; j++) {
-                const f16x2_t S = scale_f16x2(sa.s[j]);
-                const f16x8_t a0 = dequant8(sa.c[j][0], S), a1 = dequant8(sa.c[j][1], S);
-                acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hh[j][0]), acc);
-                acl = mfma16(a0, __builtin_bit_cast(f16x8_t, hl[j][0]), acl);
-                acc = mfma16(a1, __builtin_bit_cast(f16x8_t, hh[j][1]), acc);
-                acl = mfma16(a1, __builtin_bit_cast(f16x8_t, hl[j][1]), acl);
-            }
-            acc = unscale(acc + acl, hs);
-            if (KS == 1) {   // whole rows: lane holds rows 4q..4q+3 of token column n
-                if (n < mt)
-                    *reinterpret_cast<f32x4_t *>(ypair + (int64_t)pid_n * H + t * rows + rt * 16 +
-                                                 4 * q) = acc * sd;
-            } else {
-                *reinterpret_cast<f32x4_t *>(red + (unit & 1) * kRedFloats +
-                                             (wave * kCols + n) * 16 + 4 * q) = acc;
-            }
-            p_t = t;
-            p_mt = mt;
-            p_sd = sd;
+        // every buffer in flight (the rest of the ring, on the first item; filling it here
+        // rather than before the loop keeps the h operands in registers: with a separate loop
+        // the register allocator spilled them around it)
+        for (; issued < min(i + nbuf, i1); issued++) issue_next();
+        if (a != cur_a) {
+            locate_h(a);
+            fetch_h_operands<NB>(hh, hl, h_row, blk0, nblk, q);
+            hs = convert_h_operands<NB>(hh, hl, blk0, nblk);
         }
+        // tile i landed: issued after it are the tiles behind it and one store per wave and item
+        // (from item 1 on with KS > 1; a lower bound with two stores)
+        vm_wait_le(min(nbuf - 1, i1 - 1 - i) * n_inst +
+                   (KS == 1 ? min(nbuf, u) : max(0, min(nbuf, u - 1))));
+        lds_barrier();
+        if (KS > 1 && wave == 0 && lane < kCols) s_pid[u & 1][lane] = pid_n;
+        SliceA<NB> sa;
+        read_slice<NB>(wt, blk0, nblk, q, sa);
+        if (i + nbuf < i1) {
+            lds_barrier();   // tile i is in every wave's registers: refill its buffer
+            issue_next();
+            issued++;
+        }
+        if (KS > 1 && u > 0)
+            reduce(red + ((u - 1) & 1) * kRedFloats, s_pid[(u - 1) & 1], p_t, p_mt, p_sd);
+        // hi and lo parts accumulate in two independent chains (half the dependent latency)
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acl = acc;
+#pragma unroll
+        for (int j = 0; j < NB; j++) {
+            const f16x2_t S = scale_f16x2(sa.s[j]);
+            const f16x8_t a0 = dequant8(sa.c[j][0], S), a1 = dequant8(sa.c[j][1], S);
+            acc = mfma16(a0, __builtin_bit_cast(f16x8_t, hh[j][0]), acc);
+            acl = mfma16(a0, __builtin_bit_cast(f16x8_t, hl[j][0]), acl);
+            acc = mfma16(a1, __builtin_bit_cast(f16x8_t, hh[j][1]), acc);
+            acl = mfma16(a1, __builtin_bit_cast(f16x8_t, hl[j][1]), acl);
+        }
+        acc = unscale(acc + acl, hs);
+        if (KS == 1) {   // whole rows: lane holds rows 4q..4q+3 of token column n
+            if (n < mt)
+                *reinterpret_cast<f32x4_t *>(ypair + (int64_t)pid_n * H + t * rows + rt * 16 +
+                                             4 * q) = acc * sd;
+        } else {
+            *reinterpret_cast<f32x4_t *>(red + (u & 1) * kRedFloats + (wave * kCols + n) * 16 +
+                                         4 * q) = acc;
+        }
+        p_t = t;
+        p_mt = mt;
+        p_sd = sd;
         if (++t == tiles) { t = 0; ++a; }
         if (++slot == nbuf) slot = 0;
     }
     if (KS > 1) {
+        const int u = i1 - i0;
         lds_barrier();
-        reduce(red + ((unit - 1) & 1) * kRedFloats, s_pid[(unit - 1) & 1], p_t, p_mt, p_sd);
+        reduce(red + ((u - 1) & 1) * kRedFloats, s_pid[(u - 1) & 1], p_t, p_mt, p_sd);
     }
 }
 
@@ -1087,7 +1127,7 @@ namespace {
 constexpr size_t kLds = 160 * 1024;
 constexpr int kMaxBuf = 6;
 
-// Experts that one workgroup's contiguous item range can touch (its range lies within its
+// Virtual experts that one workgroup's contiguous item range can touch (its range lies within its
 // slot's).
 int64_t max_experts(int64_t n_items, int64_t tiles, int grid) {
     const int slots = paired_grid(grid) ? grid / 2 : grid;
@@ -1145,23 +1185,23 @@ int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     // expert): every workgroup then loads all T token rows, which costs more than it saves when
     // an expert holds only a pair or two (measured: tiny decode, the verify chunk, E256 T=16)
     c.tokcols = a.T <= kCols && 2 * (int64_t)P >= (int64_t)a.T * std::min<int64_t>(a.E, P);
-    const size_t scratch = fused ? ids_early_bytes(a.E) : plan_scratch_bytes(a.E, P);
+    const size_t scratch = fused ? ids_early_bytes(a.E, P) : plan_scratch_bytes(a.E, P);
     const size_t extra = fused ? sizeof(int32_t) * (size_t)P + ids_late_bytes(a.E, P) : 0;
-    const int max_active = (int)std::min<int64_t>(a.E, (int64_t)P);
+    const int max_v = max_virtual(a.E, P);   // items: virtual experts x row tiles
     int wgs;
     c.gu_lds = ring_plan(2 * kGuO * (size_t)gu_pitch((int)row_bytes(a.H)), scratch, extra,
                          c.gu_nbuf, c.gu_ring, wgs);
     if (!c.gu_lds) return MOE_ESHAPE;
     const int gu_tiles = a.F / kGuO;
-    c.gu_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * gu_tiles);
-    if (max_experts((int64_t)max_active * gu_tiles, gu_tiles, c.gu_grid) > kMaxMeta)
+    c.gu_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_v * gu_tiles);
+    if (max_experts((int64_t)max_v * gu_tiles, gu_tiles, c.gu_grid) > kMaxMeta)
         return MOE_ESHAPE;
     const int rows = 16 * c.rt;
     c.dn_lds = ring_plan(rows * (size_t)row_bytes(a.F), scratch, extra, c.dn_nbuf, c.dn_ring, wgs);
     if (!c.dn_lds) return MOE_ESHAPE;
     const int dn_tiles = a.H / rows;
-    c.dn_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_active * dn_tiles);
-    if (max_experts((int64_t)max_active * dn_tiles, dn_tiles, c.dn_grid) > kMaxMeta)
+    c.dn_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_v * dn_tiles);
+    if (max_experts((int64_t)max_v * dn_tiles, dn_tiles, c.dn_grid) > kMaxMeta)
         return MOE_ESHAPE;
     return MOE_OK;
 }

@@ -43,6 +43,9 @@ CASES = [
     (408, 128, 20, 64, 256, 64, 0.0, 0, False),      # 2560 pairs: bucketing kernel first
     (409, 8, 4, 1500, 256, 64, 0.0, 0, False),       # 1500 experts: bucketing kernel first
     (410, 5, 3, 6, 320, 64, 0.1, 0, False),          # hidden % 256 != 0
+    (412, 128, 8, 3, 256, 64, 0.0, 0, False),        # hot experts: ~340 pairs, 22 runs each
+    (413, 100, 5, 2, 512, 192, 0.25, 1, True),       # hot experts beside non-local pairs
+    (414, 128, 40, 8, 256, 64, 0.0, 0, False),       # 320 runs: ranges cut inside an expert
 ]
 
 

@@ -20,7 +20,8 @@ def _gpu():
 
 
 @pytest.mark.parametrize("T,H,F", [(1, 2560, 320), (16, 2560, 320), (128, 2560, 320),
-                                   (37, 512, 384), (600, 2560, 320)])
+                                   (37, 512, 384), (600, 2560, 320), (17, 512, 192),
+                                   (32, 512, 192), (33, 256, 64)])
 def test_shared_expert_matches_oracle(T, H, F):
     print(f"[case] shared T={T} H={H} F={F}", flush=True)
     case = gen.make_shared_case(300 + T, T, H, F)
