@@ -198,9 +198,13 @@ __device__ __forceinline__ void dma12(const void *g, void *lds) {
 __host__ __device__ constexpr int blk_lds(int b) { return 16 * (b / 12) + b % 12; }
 
 
-// LDS slot (16-byte unit) of part p (8 bf16) of token row r of a B stage: parts are XOR-swizzled
-// by the row so that the 8 lanes of a fragment read group hit 8 different bank groups.
-__device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ (r & 7)); }
+// LDS slot (16-byte unit) of part p (8 f16) of token row r of a B stage. The LDS serves a
+// 16-byte read for 16 lanes at a time from 64 banks (256 bytes): the 16 lanes of a fragment read
+// (rows r .. r + 15, one part) must fall on 16 different 16-byte bank groups, i.e. distinct slots
+// mod 16. Rows alternate between the two halves of the 256 bytes (r * 8 mod 16), so the XOR key
+// is r / 2: the 8 rows of each parity then take 8 distinct parts' places.
+__device__ __forceinline__ int b_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ b_swz(r)); }
 
 // One workgroup: N tile nt (512 weight rows) of M tile ti (gate/up: all of its up to 128 pairs;
 // down: the half hf of 64 pairs). DOWN = false: gate/up (A rows are 256 gate rows then the
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         b_on[i] = (i * kWaves + wave) * 8 < mt;   // wave-uniform
         b_lane[i] = (u >> 3) < mt;
         b_loads += b_on[i] ? 1 : 0;
-        const int r = u >> 3, p = (u & 7) ^ (r & 7);
+        const int r = u >> 3, p = (u & 7) ^ b_swz(r);
         const int64_t off = (int64_t)rowid[r] * (DOWN ? F : H) + 8 * p;
         if (DOWN) {
             bsrc[0][i] = hin_hi + off;
