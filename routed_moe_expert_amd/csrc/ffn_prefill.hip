@@ -303,20 +303,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         }
         asrc[i] = base + 12 * (u % 3);
     }
-    const int a_loads = ((kALoadsMax - 1) * kWaves + wave) * 64 < kAUnits ? kALoadsMax : kALoadsMax - 1;
+    static_assert(kAUnits == kALoadsMax * kThreads, "every lane issues kALoadsMax A loads");
     // B: lane loads 16-byte units u = (i*kWaves + wave)*64 + lane of each operand, i.e. rows
-    // 8 (i*kWaves + wave) .. +7 of the tile. Rows past the tile (r >= mt) are not loaded: their
-    // columns are never stored. A load whose 8 rows all lie past the tile is not issued at all,
-    // so a wave's loads per step (ops below) are the same at every step.
+    // 8 (i*kWaves + wave) .. +7 of the tile. Rows past the tile (r >= mt) load the row of the
+    // tile's first pair (rowid clamps them; their columns are never stored), so every wave issues
+    // the same kLoads loads at every step and its waits are compile-time counts.
     const uint16_t *bsrc[kNB][kBUnits];
-    bool b_on[kBUnits], b_lane[kBUnits];
-    int b_loads = 0;
 #pragma unroll
     for (int i = 0; i < kBUnits; i++) {
         const int u = (i * kWaves + wave) * 64 + lane;
-        b_on[i] = (i * kWaves + wave) * 8 < mt;   // wave-uniform
-        b_lane[i] = (u >> 3) < mt;
-        b_loads += b_on[i] ? 1 : 0;
         const int r = u >> 3, p = (u & 7) ^ b_swz(r);
         const int64_t off = (int64_t)rowid[r] * (DOWN ? F : H) + 8 * p;
         if (DOWN) {
@@ -326,20 +321,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
             bsrc[0][i] = x + off;
         }
     }
-    auto issue = [&](int kb) {
+    // load li of step kb: the A loads, then the B loads of each operand
+    constexpr int kLoads = kALoadsMax + kNB * kBUnits;
+    static_assert(kLoads <= 15, "waits below encode vmcnt in 4 bits");
+    auto issue_one = [&](int kb, int li) {
         uint8_t *st = smem + (kb % kStages) * kStageBytes;
-#pragma unroll
-        for (int i = 0; i < kALoadsMax; i++)
-            if (i < a_loads)
-                dma12(asrc[i] + kb * kBlockBytes, st + (i * kWaves + wave) * 1024);
-#pragma unroll
-        for (int o = 0; o < kNB; o++)
-#pragma unroll
-            for (int i = 0; i < kBUnits; i++)
-                if (b_on[i] && b_lane[i])
-                    dma16(bsrc[o][i] + kb * 64, st + kABytes + o * kBBytesW + (i * kWaves + wave) * 1024);
+        if (li < kALoadsMax) {
+            dma12(asrc[li] + kb * kBlockBytes, st + (li * kWaves + wave) * 1024);
+        } else {
+            const int o = (li - kALoadsMax) / kBUnits, i = (li - kALoadsMax) % kBUnits;
+            dma16(bsrc[o][i] + kb * 64, st + kABytes + o * kBBytesW + (i * kWaves + wave) * 1024);
+        }
     };
-    const int ops = a_loads + kNB * b_loads;   // loads per step of this wave
 
     // operands are f16: weights decoded to f16; x cast per token by xcast_kernel (gate/up), h as
     // f16 hi + lo scaled per (pair, 256-feature segment) by the gate/up epilogue (down)
@@ -365,7 +358,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
     const int c0_off = blk_lds(4 + 8 * q), c1_off = blk_lds(8 + 8 * q);
 
     const int nsteps = nblk;
-    for (int kb = 0; kb < min(kStages - 1, nsteps); kb++) issue(kb);
+    for (int kb = 0; kb < min(kStages - 1, nsteps); kb++)
+#pragma unroll
+        for (int li = 0; li < kLoads; li++) issue_one(kb, li);
     for (int kb = 0; kb < nsteps; kb++) {
         if constexpr (DOWN) {
             // a new h segment (its own scale exponent per column): rescale the running sums to
@@ -382,9 +377,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
                 }
             }
         }
-        vm_wait_le(min(kStages - 2, nsteps - 1 - kb) * ops);   // step kb landed
+        // step kb landed: at most step kb + 1's loads still outstanding (s_waitcnt vmcnt(n))
+        static_assert(kStages == 3, "one step in flight behind the one awaited");
+        if (kb + 1 < nsteps)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70);
         lds_barrier();   // visible to all; the stage of step kb-1 is free
-        if (kb + kStages - 1 < nsteps) issue(kb + kStages - 1);
+        // step kb + 2's loads go into that stage, one after each of the first kLoads of the
+        // step's eight MFMA groups (measured a few percent faster than issuing them together:
+        // a wave stalled on a full memory queue then still has MFMAs in flight)
+        const bool refill = kb + kStages - 1 < nsteps;
         const uint8_t *st = smem + (kb % kStages) * kStageBytes;
         // One K step in two sub-steps of 32. The second half of the token columns is read and
         // multiplied only when the tile reaches it (one uniform branch).
@@ -416,6 +419,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
                     for (int o = 0; o < kNB; o++)
 #pragma unroll
                         for (int c = 0; c < kC; c++) acc[f][c] = mfma_f16(af, bfr[o][c], acc[f][c]);
+                    const int li = s2 * kAT + f;   // MFMA group index, compile-time
+                    if (li < kLoads && refill) {
+                        __builtin_amdgcn_sched_barrier(0);   // keep the load at this point
+                        issue_one(kb + kStages - 1, li);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
             }
         };
