@@ -380,8 +380,9 @@ def measure(D, path_flag, K, W, q, torch, moe, kernels=True, two_calls=True):
         lay.step(i)
     torch.cuda.synchronize()
     per, qinfo = time_steps(q, lay.step, K, W)
-    decode = path_flag == moe.MOE_PATH_DECODE or (path_flag == moe.MOE_PATH_AUTO and T <= 128)
     H, F, k = D["H"], D["F"], D["k"]
+    decode = path_flag == moe.MOE_PATH_DECODE or (
+        path_flag == moe.MOE_PATH_AUTO and moe.moe_auto_path(T, k, D["E"], H, F) == moe.MOE_PATH_DECODE)
     rbh, rbf = H // 64 * 36, F // 64 * 36
     per_expert = 2 * F * rbh + H * rbf
     uniq = statistics.mean(D["uniq"])

@@ -57,7 +57,7 @@ enum {
 
 /* Path selection for moe_ffn_nvfp4. */
 enum {
-    MOE_PATH_AUTO = 0,          /* decode path for T <= 128, grouped-GEMM prefill path above */
+    MOE_PATH_AUTO = 0,          /* the path moe_auto_path() names for the sizes */
     MOE_PATH_DECODE = 1,        /* force the bandwidth-bound decode path */
     MOE_PATH_PREFILL = 2        /* force the grouped-GEMM path (f16 MFMA) */
 };
@@ -67,6 +67,7 @@ enum {
 #define MOE_MAX_HIDDEN 16384       /* H limit */
 #define MOE_MAX_FF 8192            /* F limit */
 #define MOE_MAX_ROUTER_K 64        /* k limit of moe_router_topk (one slot per wavefront lane) */
+#define MOE_AUTO_PAIRS_PER_EXPERT 24   /* MOE_PATH_AUTO's decode limit: routed pairs per expert */
 
 /*
  * One weight bank: expert e's rows start at base + e*expert_stride (bytes, device).
@@ -118,6 +119,19 @@ size_t moe_route_bucket_ws(int32_t T, int32_t k, int32_t E);
 int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, int32_t expert_base,
                      int32_t *offsets, int32_t *pair_ids, int32_t *active, int32_t *counts,
                      void *ws, size_t ws_bytes, moe_stream_t stream);
+
+/*
+ * The path MOE_PATH_AUTO takes in moe_ffn_nvfp4 and moe_layer_nvfp4 for these sizes, decided on
+ * the host alone (no device work): MOE_PATH_DECODE for T <= 128 or T*k <= MOE_AUTO_PAIRS_PER_EXPERT
+ * * E where the decode kernels can launch for (T, k, E, H, F), else MOE_PATH_PREFILL. The pages
+ * split the work the same way, a bandwidth-bound path for a few tokens per expert and grouped GEMMs
+ * for prefill (moe_sk_repro.rs, its decode and prefill regimes); the pairs-per-expert limit is where
+ * the two paths measured equal on one MI355X (22 to 43 pairs per expert on the H 2560-4096
+ * configurations; the decode kernels stream an expert's weights once per run of 16 pairs).
+ * Returns the path, or minus an MOE_E* code for sizes moe_ffn_nvfp4 would refuse (-MOE_EINVAL,
+ * -MOE_ESHAPE).
+ */
+int32_t moe_auto_path(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F);
 
 /*
  * Workspace bytes moe_ffn_nvfp4 needs (for any path).

@@ -7,7 +7,8 @@ from .binding import (MOE_EINVAL, MOE_ELAUNCH, MOE_ESHAPE, MOE_EWS, MOE_KERNEL_B
                       MOE_KERNEL_COMBINE, MOE_KERNEL_DN_DECODE, MOE_KERNEL_DN_PREFILL,
                       MOE_KERNEL_GU_DECODE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_NONE,
                       MOE_KERNEL_ROUTER, MOE_KERNEL_SCHEDULE, MOE_OK, MOE_PATH_AUTO, MOE_PATH_DECODE,
-                      MOE_PATH_PREFILL, MOE_STATIC_WS_BYTES, MoeError, bank, lib, moe_ffn_nvfp4,
+                      MOE_PATH_PREFILL, MOE_STATIC_WS_BYTES, MoeError, bank, lib, moe_auto_path,
+                      moe_ffn_nvfp4,
                       moe_ffn_nvfp4_static, moe_ffn_nvfp4_ws, moe_layer_nvfp4,
                       moe_layer_nvfp4_ws,
                       moe_profile_count, moe_profile_kernel, moe_route_bucket,

@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EWS, MOE_ESHAPE, MOE_ELAUNCH = 0, 1, 2, 3, 4
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
+MOE_AUTO_PAIRS_PER_EXPERT = 24
 (MOE_KERNEL_NONE, MOE_KERNEL_BUCKET, MOE_KERNEL_GU_DECODE, MOE_KERNEL_DN_DECODE, MOE_KERNEL_COMBINE,
  MOE_KERNEL_SCHEDULE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_DN_PREFILL, MOE_KERNEL_ROUTER) = range(9)
 
@@ -47,6 +48,8 @@ def _load():
     l.moe_route_bucket.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
     l.moe_ffn_nvfp4_ws.restype = sz
     l.moe_ffn_nvfp4_ws.argtypes = [i32, i32, i32, i32, i32]
+    l.moe_auto_path.restype = i32
+    l.moe_auto_path.argtypes = [i32, i32, i32, i32, i32]
     l.moe_ffn_nvfp4.restype = ctypes.c_int
     l.moe_ffn_nvfp4.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
                                 i32, i32, i32, i32, i32, vp, i32, vp, sz, vp]
@@ -106,6 +109,14 @@ def moe_route_bucket_ws(T: int, k: int, E: int) -> int:
 
 def moe_ffn_nvfp4_ws(T: int, k: int, E: int, H: int, F: int) -> int:
     return int(lib.moe_ffn_nvfp4_ws(T, k, E, H, F))
+
+
+def moe_auto_path(T: int, k: int, E: int, H: int, F: int) -> int:
+    """The path MOE_PATH_AUTO takes for these sizes (host only); raises on refused sizes."""
+    p = int(lib.moe_auto_path(T, k, E, H, F))
+    if p < 0:
+        raise MoeError("moe_auto_path", -p)
+    return p
 
 
 def moe_route_bucket(topk_ids, T: int, k: int, E: int, expert_base: int, offsets, pair_ids,

@@ -27,6 +27,17 @@ int check_common(int32_t T, int32_t k, int32_t E) {
     return MOE_OK;
 }
 
+// MOE_PATH_AUTO: the decode path where it measured faster than the GEMM path -- up to 128
+// tokens, or up to MOE_AUTO_PAIRS_PER_EXPERT routed pairs per local expert (the decode kernels
+// stream an expert's weights once per run of 16 pairs, so their cost grows with the pairs per
+// expert, the GEMMs' with the 128-pair M tiles) -- and where its kernels can launch; else the
+// GEMM path.
+int32_t auto_path(const FfnArgs &a) {
+    const int64_t P = (int64_t)a.T * a.k;
+    const bool few = a.T <= 128 || P <= (int64_t)MOE_AUTO_PAIRS_PER_EXPERT * a.E;
+    return few && decode_supported(a) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+}
+
 }  // namespace
 
 extern "C" {
@@ -47,6 +58,16 @@ int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, i
     if (ws_bytes < need || (need && !ws)) return MOE_EWS;
     return launch_bucket(topk_ids, T, k, E, expert_base, offsets, pair_ids, active, counts, ws,
                          reinterpret_cast<hipStream_t>(stream));
+}
+
+int32_t moe_auto_path(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
+    const int st = check_common(T, k, E);
+    if (st != MOE_OK) return -st;
+    if (H < 64 || F < 64 || H % 64 || F % 64) return -MOE_EINVAL;
+    if (H > MOE_MAX_HIDDEN || F > MOE_MAX_FF) return -MOE_ESHAPE;
+    const FfnArgs a{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, {}, {}, {},
+                    T, k, E, H, F, nullptr, nullptr, 0};
+    return auto_path(a);
 }
 
 size_t moe_ffn_nvfp4_ws(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
@@ -73,9 +94,7 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
     FfnArgs a{x, topk_w, offsets, pair_ids, active, counts, gate, up, down, T, k, E, H, F, y,
               ws, ws_bytes};
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    // AUTO: the decode path for up to 128 tokens where its slices fit, else the GEMM path
-    if (path == MOE_PATH_AUTO)
-        path = (T <= 128 && decode_supported(a)) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    if (path == MOE_PATH_AUTO) path = auto_path(a);
     return path == MOE_PATH_DECODE ? launch_decode(a, s) : launch_prefill(a, s);
 }
 
@@ -121,8 +140,7 @@ int moe_layer_nvfp4(const int32_t *topk_ids, int32_t expert_base, const uint16_t
     void *bws = reinterpret_cast<uint8_t *>(counts) + 256;
     FfnArgs a{x, topk_w, offsets, pair_ids, active, counts, gate, up, down, T, k, E, H, F, y,
               b + csr, ws_bytes - csr};
-    if (path == MOE_PATH_AUTO)
-        path = (T <= 128 && decode_supported(a)) ? MOE_PATH_DECODE : MOE_PATH_PREFILL;
+    if (path == MOE_PATH_AUTO) path = auto_path(a);
     if (path == MOE_PATH_DECODE) {
         // bucketed inside the decode kernels when the routed pairs fit their LDS plan
         FfnArgs f = a;

@@ -197,3 +197,30 @@ def test_layer_workspace_covers_the_two_calls():
         ws = moe.moe_layer_nvfp4_ws(T, k, E, H, F)
         assert ws >= moe.moe_ffn_nvfp4_ws(T, k, E, H, F) + moe.moe_route_bucket_ws(T, k, E)
         assert ws >= 4 * (E + 1 + T * k + E + 2)
+
+
+@pytest.mark.parametrize("T,k,E,H,F,path", [
+    (1, 10, 64, 2560, 640, moe.MOE_PATH_DECODE),       # tiny decode
+    (6, 10, 512, 2560, 640, moe.MOE_PATH_DECODE),      # verify chunk
+    (128, 10, 256, 2560, 640, moe.MOE_PATH_DECODE),    # E256 plateau, 5 pairs per expert
+    (128, 1, 1, 2560, 320, moe.MOE_PATH_DECODE),       # shared expert: 128 tokens, one expert
+    (512, 8, 288, 4096, 640, moe.MOE_PATH_DECODE),     # skewed prefill T=512: 14.2 pairs/expert
+    (864, 8, 288, 4096, 640, moe.MOE_PATH_DECODE),     # 24 pairs per expert: the limit
+    (865, 8, 288, 4096, 640, moe.MOE_PATH_PREFILL),    # one token past it
+    (2048, 8, 288, 4096, 640, moe.MOE_PATH_PREFILL),
+    (4096, 8, 288, 4096, 1280, moe.MOE_PATH_PREFILL),  # full-width prefill
+    (129, 1, 1, 2560, 320, moe.MOE_PATH_PREFILL),      # past 128 tokens, 129 pairs per expert
+    (6, 10, 512, 16384, 640, moe.MOE_PATH_PREFILL),    # hidden beyond the decode slices
+])
+def test_auto_path(T, k, E, H, F, path):
+    """AUTO's rule on the host: decode for T <= 128 or at most MOE_AUTO_PAIRS_PER_EXPERT routed
+    pairs per local expert, where the decode kernels can launch."""
+    assert moe.moe_auto_path(T, k, E, H, F) == path
+
+
+def test_auto_path_refuses_what_the_ffn_refuses():
+    for args, status in [((1, 0, 8, 64, 64), moe.MOE_EINVAL), ((1, 1, 8, 96, 64), moe.MOE_EINVAL),
+                         ((1, 1, 4096, 64, 64), moe.MOE_ESHAPE)]:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_auto_path(*args)
+        assert ei.value.status == status

@@ -197,16 +197,27 @@ def test_prefill_small(seed, T, k, E, H, F, scales, frac, base, fused):
 @pytest.mark.parametrize("name,T", [("skewed_prefill", 512), ("skewed_prefill", 2048),
                                     ("skewed_prefill", 4096), ("full_prefill", 4096)])
 def test_prefill_workloads(name, T):
-    """Full-size prefill workloads through AUTO (the GEMM path), compared on the tokens that
-    cover every M tile: each tile's first and last pair and both ends of its halves."""
+    """Full-size prefill workloads. The GEMM path (forced) on the tokens that cover every M tile:
+    each tile's first and last pair and both ends of its halves. AUTO must give what the path
+    moe_auto_path names gives, bit for bit; where that is the decode path (skewed T=512: 14 pairs
+    per expert), it is compared on every token."""
     _print_case("prefill_workload", name=name, T=T)
     case = _workload(name, T)
     dc = DeviceCase(case)
-    y = dc.run(moe.MOE_PATH_AUTO)
+    y = dc.run(moe.MOE_PATH_PREFILL)
     _check_bucket(dc)
     tok = tile_tokens(case["ids"], dc.E)
-    print(f"[case] comparing {tok.size} tokens", flush=True)
-    assert_parity(y[tok], oracle.ffn_union(case, tokens=tok), name)
+    auto = moe.moe_auto_path(T, dc.k, dc.E, dc.H, dc.F)
+    if auto == moe.MOE_PATH_DECODE:
+        ref = oracle.ffn_union(case)
+        assert_parity(y[tok], ref[tok], name + " gemm path")
+        yd = dc.run(moe.MOE_PATH_DECODE)
+        assert_parity(yd, ref, name + " decode path")
+        assert np.array_equal(dc.run(moe.MOE_PATH_AUTO), yd), "AUTO differs from the decode path"
+    else:
+        print(f"[case] comparing {tok.size} tokens", flush=True)
+        assert_parity(y[tok], oracle.ffn_union(case, tokens=tok), name)
+        assert np.array_equal(dc.run(moe.MOE_PATH_AUTO), y), "AUTO differs from the GEMM path"
 
 
 def test_e256_forced_through_gemm_path():
