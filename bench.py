@@ -48,8 +48,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "aa57533171065ba870ad466847760c80132472999863ba926f33bc4534bfc03c",
-        "fetch_kib": 54383.3, "write_kib": 168.7,
+        "sha256": "6ebf0b0c40fc691ab36469f24d6b7f8a7656cc991b23129f646a03aa0ff8d6d4",
+        "fetch_kib": 54367.0, "write_kib": 168.3,
     },
 }
 
