@@ -10,7 +10,9 @@ every step streams its experts' weights from HBM, not from the 256 MB Infinity C
 
 Every timed region is queued behind a bounded sleep kernel, so all of its launches are enqueued
 before the GPU reaches the first one: the HIP events then time the GPU alone, not the host's
-launch rate.
+launch rate. The layer time is the mean over K back-to-back layers between two events; a second
+pass with an event between every two layers gives the per-step distribution (those events are
+queue packets of their own and add about 3 us per decode layer).
 
 Prints one JSON line: value = unique-expert weight bytes per second (decode workloads) or useful
 TFLOP/s (prefill workloads), the dominant kernel's roofline from HIP events recorded around its
@@ -167,7 +169,11 @@ class Queue:
 
 
 def time_steps(q, step, K, first):
-    """Per-step GPU ms of K steps (step(first + i)), queued behind a sleep."""
+    """GPU time of K steps (step(first + i)), queued behind a sleep, twice: once with an event
+    between every two steps (the per-step distribution), once with events only around the K
+    steps (the mean per step: each event is a packet of its own in the queue, and one between
+    every two steps measured about 3 us more per decode layer). Returns (per-step ms, mean ms
+    per step over the span, queue info)."""
     torch = q.torch
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     t0 = time.perf_counter()
@@ -183,7 +189,17 @@ def time_steps(q, step, K, first):
 
     host_ms, sleep_ms, ahead = q.run(enqueue, hint)
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(K)]
-    return per, {"host_enqueue_ms": host_ms, "sleep_ms": sleep_ms, "queued_ahead": ahead}
+
+    def enqueue_span():
+        evs[0].record(q.stream)
+        for i in range(K):
+            step(first + i)
+        evs[K].record(q.stream)
+
+    host2, sleep2, ahead2 = q.run(enqueue_span, hint)
+    span = evs[0].elapsed_time(evs[K]) / K
+    return per, span, {"host_enqueue_ms": host_ms, "sleep_ms": sleep_ms, "queued_ahead": ahead,
+                       "span_queued_ahead": ahead2}
 
 
 def kernel_avg_ms(q, moe, kid, step, K, first):
@@ -373,29 +389,29 @@ def measure(D, path_flag, K, W, q, torch, moe, kernels=True, two_calls=True):
         for i in range(W):
             two.step(i)
         torch.cuda.synchronize()
-        per2, _ = time_steps(q, two.step, K, W)
+        per2, span2, _ = time_steps(q, two.step, K, W)
         del two
     lay = Layer(D, path_flag, torch, moe)
     for i in range(W):
         lay.step(i)
     torch.cuda.synchronize()
-    per, qinfo = time_steps(q, lay.step, K, W)
+    per, span, qinfo = time_steps(q, lay.step, K, W)
     H, F, k = D["H"], D["F"], D["k"]
     decode = path_flag == moe.MOE_PATH_DECODE or (
         path_flag == moe.MOE_PATH_AUTO and moe.moe_auto_path(T, k, D["E"], H, F) == moe.MOE_PATH_DECODE)
     rbh, rbf = H // 64 * 36, F // 64 * 36
     per_expert = 2 * F * rbh + H * rbf
     uniq = statistics.mean(D["uniq"])
-    mean_ms = sum(per) / len(per)
     med = statistics.median(per)
-    s = mean_ms * 1e-3
+    s = span * 1e-3
     res = {
-        "layer_us": {"mean": mean_ms * 1e3, "min": min(per) * 1e3, "median": med * 1e3,
-                     "spread": (max(per) - min(per)) / med if med > 0 else None},
-        "ms_per_step": mean_ms, "decode": decode, "queue": qinfo,
+        # mean: K back-to-back layers between two events; the rest: an event between every two
+        "layer_us": {"mean": span * 1e3, "per_step_median": med * 1e3,
+                     "per_step_min": min(per) * 1e3,
+                     "per_step_spread": (max(per) - min(per)) / med if med > 0 else None},
+        "ms_per_step": span, "decode": decode, "queue": qinfo,
         "two_call_layer_us": None if per2 is None else {
-            "mean": sum(per2) / len(per2) * 1e3, "median": statistics.median(per2) * 1e3,
-            "min": min(per2) * 1e3},
+            "mean": span2 * 1e3, "per_step_median": statistics.median(per2) * 1e3},
         "unique_expert_bytes": uniq * per_expert,
         "unique_gbs": uniq * per_expert / s / 1e9,
         "hbm_frac_unique": uniq * per_expert / s / 1e9 / HBM_PEAK_GBS,
@@ -498,7 +514,7 @@ def main():
                      hbm=hbm_note(Dr, args.warm))
             del r["decode"]
             rows.append(r)
-            print(f"[row] {r['workload']}: {r['layer_us']['median']:.1f} us median, "
+            print(f"[row] {r['workload']}: {r['layer_us']['mean']:.1f} us per layer, "
                   f"{r['unique_gbs']:.0f} GB/s unique, {r['useful_tflops']:.1f} TFLOP/s",
                   file=sys.stderr, flush=True)
             del Dr
