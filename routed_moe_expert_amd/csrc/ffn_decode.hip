@@ -1137,15 +1137,22 @@ int64_t max_experts(int64_t n_items, int64_t tiles, int grid) {
 
 // Two workgroups per CU with two tile buffers each when the LDS holds them (both in flight while
 // a tile is computed from registers: measured as fast as three, the streaming rate being set
-// elsewhere), else one with as many as fit (at most kMaxBuf). The ring region also holds the
-// start-up scratch, so it is at least that large; `extra` bytes (the fused layer's pair list and
-// late plan scratch) follow the partials. Returns the dynamic LDS bytes (0: does not fit).
+// elsewhere), else two with one buffer each, else one with as many as fit (at most kMaxBuf).
+// The ring region also holds the start-up scratch, so it is at least that large; `extra` bytes
+// (the fused layer's pair list and late plan scratch) follow the partials. Returns the dynamic
+// LDS bytes (0: does not fit).
 size_t ring_plan(size_t tile, size_t scratch, size_t extra, int &nbuf, int &ring_bytes,
                  int &wgs) {
     const size_t fixed = kRedBytes + sizeof(Meta) + extra;
     const size_t scr = (scratch + 15) & ~size_t(15);
     if (2 * (std::max(2 * tile, scr) + fixed) <= kLds) {
         nbuf = 2;
+        wgs = 2;
+    } else if (2 * (std::max(tile, scr) + fixed) <= kLds) {
+        // wide tiles (hidden 4096: 37 KB): two workgroups of one buffer each, the tile in flight
+        // while the last one is computed from registers, measured 25% faster than one
+        // workgroup per CU with four (skewed prefill T=512, gate/up 406 -> 307 us)
+        nbuf = 1;
         wgs = 2;
     } else {
         if (kLds < fixed + 2 * tile) return 0;

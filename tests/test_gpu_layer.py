@@ -46,6 +46,8 @@ CASES = [
     (412, 128, 8, 3, 256, 64, 0.0, 0, False),        # hot experts: ~340 pairs, 22 runs each
     (413, 100, 5, 2, 512, 192, 0.25, 1, True),       # hot experts beside non-local pairs
     (414, 128, 40, 8, 256, 64, 0.0, 0, False),       # 320 runs: ranges cut inside an expert
+    (415, 64, 8, 32, 4096, 640, 0.1, 0, False),      # hidden 4096: one tile buffer per workgroup
+    (416, 100, 12, 16, 4096, 128, 0.0, 2, True),     # the same through the bucketing kernel
 ]
 
 
