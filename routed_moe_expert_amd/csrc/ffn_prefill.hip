@@ -456,23 +456,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
         // count as 0), then one power-of-two scale per (pair, this tile's 256 features): the
         // largest |h| over the tile into [2^14, 2^15), so h = 2^s (hi + lo) with hi and lo f16
         // (about 22 significant bits)
-        // (h is formed twice, for the maxima and for the stores, rather than held in registers
-        // over the workgroup's exchange of maxima)
+        // (h is formed once, into the gate accumulators, whose sums it no longer needs)
         auto hval = [&](int t, int c, int v, int sc) {
             const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q + v;
             const float g = ldexpf(acc[t][c][v], sc) * sc0, u = ldexpf(acc[2 + t][c][v], sc) * sc1;
             return o < F ? silu(g) * u : 0.f;
         };
         float *cmax = reinterpret_cast<float *>(smem);   // [kWaves][kBM]: stages are done
-        lds_barrier();   // every wave is past its last read of the stages
 #pragma unroll
         for (int c = 0; c < kCols; c++) {
             const int sc = xs[rowid[16 * c + n]];   // the token row's f16 scale exponent
+#pragma unroll
+            for (int t = 0; t < 2; t++)
+#pragma unroll
+                for (int v = 0; v < 4; v++) acc[t][c][v] = hval(t, c, v, sc);
+        }
+        lds_barrier();   // every wave is past its last read of the stages
+#pragma unroll
+        for (int c = 0; c < kCols; c++) {
             float m = 0.f;
 #pragma unroll
             for (int t = 0; t < 2; t++)
 #pragma unroll
-                for (int v = 0; v < 4; v++) m = fmaxf(m, fabsf(hval(t, c, v, sc)));
+                for (int v = 0; v < 4; v++) m = fmaxf(m, fabsf(acc[t][c][v]));
             m = fmaxf(m, __shfl_xor(m, 16, 64));
             m = fmaxf(m, __shfl_xor(m, 32, 64));
             if (q == 0) cmax[wave * kBM + 16 * c + n] = m;
@@ -489,7 +495,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
             const int sh = m > 0.f ? e - 15 : 0;
             if (col >= mt) continue;
             if (wave == 0 && q == 0) hs[(int64_t)(q0 + col) * nseg + nt] = sh;
-            const int sc = xs[rowid[col]];
 #pragma unroll
             for (int t = 0; t < 2; t++) {
                 const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q;
@@ -497,8 +502,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(
                 uint32_t hi2[2], lo2[2];
 #pragma unroll
                 for (int v = 0; v < 4; v += 2) {
-                    const float h0 = ldexpf(hval(t, c, v, sc), -sh);
-                    const float h1 = ldexpf(hval(t, c, v + 1, sc), -sh);
+                    const float h0 = ldexpf(acc[t][c][v], -sh);
+                    const float h1 = ldexpf(acc[t][c][v + 1], -sh);
                     const _Float16 a0 = (_Float16)h0, a1 = (_Float16)h1;
                     hi2[v / 2] = __builtin_bit_cast(uint32_t, f16x2_t{a0, a1});
                     lo2[v / 2] = __builtin_bit_cast(
