@@ -50,8 +50,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "6ebf0b0c40fc691ab36469f24d6b7f8a7656cc991b23129f646a03aa0ff8d6d4",
-        "fetch_kib": 54367.0, "write_kib": 168.3,
+        "sha256": "c028d242ecb6d0b9c505cc63afa94e3ec17a74ead381e22ba4b4d90bda7c37dd",
+        "fetch_kib": 54366.9, "write_kib": 168.5,
     },
 }
 
