@@ -58,6 +58,7 @@ constexpr int kGuO = 8;                // output features per gu item: 8 gate ro
 constexpr int kCUs = 256;
 constexpr int kMaxGuBlocks = 16;       // NVFP4 blocks per wave slice: hidden <= 4 * 16 * 64
 constexpr int kMaxDnBlocks = 10;       // ... ff <= 4 * 10 * 64
+constexpr int64_t kDnSpreadItems = 2048;   // down items (4 per workgroup) below which K splits
 constexpr int kRedFloats = kWaves * kCols * 16;      // one set of per-wave 16x16 fp32 partials
 constexpr int kRedBytes = 2 * kRedFloats * 4;        // two sets (double-buffered)
 
@@ -1177,15 +1178,24 @@ struct DecodeCfg {
 // Down: the smallest K split KS in {1, 2, 4} with at most kMaxDnBlocks blocks per slice, and
 // RT = 4 / KS row tiles per item; H must hold whole items, and two tiles plus the start-up
 // scratch must fit in LDS. fused: the plan is built from the routed ids (a.ids).
+// With few down items (a union of a few experts) KS is raised further, while the slices
+// average two blocks or more and the items at RT = 4 times KS stay under kDnSpreadItems:
+// smaller items spread over more workgroups, and each wave then loads only its slice of the h
+// rows. Measured down kernel, KS 1 / 2 / 4: 10 experts (tiny decode) 17.1 / 15.5 / 14.7 us,
+// 30 experts 21.1 / 20.9 / 25.1 us with the layer 45.0 / 43.5 / 48.9 us, 60 experts 25.7 /
+// 28.2 / 38.6 us.
 int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     const int bh = a.H / kBlockWeights, bf = a.F / kBlockWeights;
+    const int32_t P = a.T * a.k;
+    const int max_v = max_virtual(a.E, P);   // items: virtual experts x row tiles
     c.nb_gu = (bh + kWaves - 1) / kWaves;
     int ks = 1;
     while (ks < kWaves && (bf + ks - 1) / ks > kMaxDnBlocks) ks *= 2;
+    const int64_t items4 = (int64_t)max_v * (a.H / (16 * kWaves));   // items at RT = 4
+    while (ks < kWaves && 2 * (2 * ks) <= bf && items4 * ks < kDnSpreadItems) ks *= 2;
     c.nb_dn = (bf + ks - 1) / ks;
     c.rt = kWaves / ks;
     if (c.nb_gu > kMaxGuBlocks || c.nb_dn > kMaxDnBlocks || a.H % (16 * c.rt)) return MOE_ESHAPE;
-    const int32_t P = a.T * a.k;
     if (fused && (P > kIdsMaxPairs || a.E > kIdsMaxExperts)) return MOE_ESHAPE;
     c.fused = fused;
     // token columns when most tokens hit each active expert (dense routing, e.g. a shared
@@ -1194,7 +1204,6 @@ int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     c.tokcols = a.T <= kCols && 2 * (int64_t)P >= (int64_t)a.T * std::min<int64_t>(a.E, P);
     const size_t scratch = fused ? ids_early_bytes(a.E, P) : plan_scratch_bytes(a.E, P);
     const size_t extra = fused ? sizeof(int32_t) * (size_t)P + ids_late_bytes(a.E, P) : 0;
-    const int max_v = max_virtual(a.E, P);   // items: virtual experts x row tiles
     int wgs;
     c.gu_lds = ring_plan(2 * kGuO * (size_t)gu_pitch((int)row_bytes(a.H)), scratch, extra,
                          c.gu_nbuf, c.gu_ring, wgs);

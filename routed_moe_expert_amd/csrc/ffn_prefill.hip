@@ -60,7 +60,8 @@ constexpr int kRowsW = 64;            // A rows per wave
 // workgroup of the CU computes)
 template <bool DOWN> constexpr int gemm_threads() { return DOWN ? 256 : 512; }
 template <bool DOWN> constexpr int gemm_stages() { return DOWN ? 2 : 3; }
-constexpr int kSegF = kRowsW / 2 * (gemm_threads<false>() / 64);   // features per gate/up N tile (256)
+// h features per gate/up N tile (256): one h scale segment
+constexpr int kSegF = kRowsW / 2 * (gemm_threads<false>() / 64);
 constexpr int kMaxSeg = 32;           // h scale segments per pair: ff <= 32 * 256
 
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2_t;
@@ -566,7 +567,8 @@ template <bool DOWN>
 int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
     constexpr int kThreads = gemm_threads<DOWN>();
     constexpr int kRows = kRowsW * (kThreads / 64);
-    constexpr size_t lds = gemm_stages<DOWN>() * (kRows * 48 + kBBytes);   // B: 128 x1 or 64 x2 rows
+    // B: 128 rows x 1 operand or 64 x 2
+    constexpr size_t lds = gemm_stages<DOWN>() * (kRows * 48 + kBBytes);
     static bool attr = false;
     if (!attr) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_kernel<DOWN>),
