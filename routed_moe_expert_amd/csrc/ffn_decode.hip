@@ -350,6 +350,30 @@ __host__ __device__ inline int max_virtual(int E, int P) {
     return v < P ? v : P;
 }
 
+// The down kernel's K split, chosen once the number of virtual experts is known (the same rule on
+// both plan forms, so they scale h alike and give the same y): from the smallest split the slice
+// width allows (ks_min), doubled while the slices average two NVFP4 blocks or more and the items
+// (virtual experts x H / (16 RT), RT = 4 / KS row tiles per item) stay under kDnSpreadItems. With
+// a union of a few experts the smaller items then spread over every workgroup, and each wave
+// loads only its slice of the h rows (with one slice every wave loads all of them). Measured
+// down kernel, KS 1 / 2 / 4: 10 experts (tiny decode) 17.1 / 15.5 / 14.7 us; 30 experts 21.1 /
+// 20.9 / 25.1 us (layer 45.0 / 43.5 / 48.9 us); 60 experts 25.7 / 28.2 / 38.6 us; E256 T=16
+// 46.6 / 55.6 / 83.3 us.
+struct DnSplit {
+    int ks_min, bf, H;   // ks_min 0: not the down kernel (tiles fixed)
+};
+__host__ __device__ inline int dn_ks(const DnSplit &d, int n_active) {
+    int ks = d.ks_min;
+    while (ks < kWaves && 4 * ks <= d.bf &&
+           (int64_t)n_active * (d.H / (16 * kWaves)) * ks < kDnSpreadItems)
+        ks *= 2;
+    return ks;
+}
+// Row tiles per virtual expert: fixed, or the down kernel's for its split.
+__device__ __forceinline__ int plan_tiles(const DnSplit &d, int n_active, int tiles) {
+    return d.ks_min ? d.H / (16 * (kWaves / dn_ks(d, n_active))) : tiles;
+}
+
 // Expert e's first weight row in a bank: from the bank's per-expert pointer table when it has one,
 // else at base + e * stride.
 __device__ __forceinline__ const uint8_t *expert_rows(const uint8_t *base, int64_t stride,
@@ -399,8 +423,8 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
                           const int32_t *__restrict__ pair_ids, const uint8_t *wa, int64_t sa,
                           const uint8_t *const *ta, const float *__restrict__ s2a,
                           const uint8_t *wb, int64_t sb, const uint8_t *const *tb,
-                          const float *__restrict__ s2b, int E, int P, int tiles, int &i0,
-                          int &i1, int &a_first) {
+                          const float *__restrict__ s2b, int E, int P, const DnSplit &sp,
+                          int &tiles, int &i0, int &i1, int &a_first) {
     const int tid = threadIdx.x;
     const bool pairs_in_lds = P <= kPairCap;
     int32_t *s_act = scratch, *s_off = scratch + E, *s_pair = scratch + 2 * E + 1;
@@ -440,6 +464,7 @@ __device__ void load_plan(Meta &meta, int32_t *scratch, const int32_t *__restric
     }
     int nv;
     int v = wg_exclusive_scan(mine, s_wsum, &nv);
+    tiles = plan_tiles(sp, nv, tiles);
     item_range(nv, tiles, i0, i1);
     a_first = i0 / tiles;
     const int na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
@@ -533,8 +558,8 @@ __device__ void plan_ids_a(Meta &meta, const IdsLds &l, const int32_t *__restric
                            int expert_base, const uint8_t *wa, int64_t sa,
                            const uint8_t *const *ta, const float *__restrict__ s2a,
                            const uint8_t *wb, int64_t sb, const uint8_t *const *tb,
-                           const float *__restrict__ s2b, int E, int P, int tiles, int &i0,
-                           int &i1, int &a_first, int &na) {
+                           const float *__restrict__ s2b, int E, int P, const DnSplit &sp,
+                           int &tiles, int &i0, int &i1, int &a_first, int &na) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int key[kIdsPer];
@@ -579,6 +604,7 @@ __device__ void plan_ids_a(Meta &meta, const IdsLds &l, const int32_t *__restric
         meta.n_local = tot & 0xffff;
     }
     lds_barrier();
+    tiles = plan_tiles(sp, tot >> 16, tiles);
     item_range(meta.n_active, tiles, i0, i1);
     a_first = i0 / tiles;
     na = i0 < i1 ? min((i1 - 1) / tiles - a_first + 1, kMaxMeta) : 0;
@@ -715,7 +741,7 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     const int n = lane & 15, q = lane >> 4;   // A row / B column, and K group
     // K slices of NB blocks; a last slice may run past the row (reads clamp, operands zero)
     const int nblk = H / kBlockWeights, blk0 = wave * NB;
-    const int tiles = F / kGuO;
+    int tiles = F / kGuO;
     // fused layer: the pair list and the plan's late scratch live in LDS behind the partials;
     // else the pair list is the CSR's
     const bool fused = ids != nullptr;
@@ -731,11 +757,11 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
     int i0, i1, a_first, na = 0;
     if (fused)
         plan_ids_a(meta, il, ids, expert_base, gate, gate_stride, gate_tab, gate_s2, up,
-                   up_stride, up_tab, up_s2, E, P, tiles, i0, i1, a_first, na);
+                   up_stride, up_tab, up_s2, E, P, DnSplit{0, 0, 0}, tiles, i0, i1, a_first, na);
     else
         load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, gate,
-                  gate_stride, gate_tab, gate_s2, up, up_stride, up_tab, up_s2, E, P, tiles, i0,
-                  i1, a_first);
+                  gate_stride, gate_tab, gate_s2, up, up_stride, up_tab, up_s2, E, P,
+                  DnSplit{0, 0, 0}, tiles, i0, i1, a_first);
     // load k of this wave moves LDS chunk p = 64 wave + 256 k + lane of the tile; its source
     // offset within the gate or up rows of the tile (sign bit: up) is the same for every tile.
     // Padded pitch: chunk p is chunk p % cpr of row p / cpr (the last one a copy of chunk 0).
@@ -887,44 +913,23 @@ __global__ __launch_bounds__(kThreads, 2) void gu_decode_kernel(
 // ff up to 640) every wave owns whole rows and stores them from registers; otherwise the slices
 // are summed through LDS like gate/up, a quarter of the outputs per wave. Either way every wave
 // issues at least one store per item, which the ring waits count.
+// dn_items is the item loop for K slices of NB blocks (NB = ceil(blocks / KS), one instantiation
+// per split the kernel can choose), once the plan has given the workgroup its items [i0, i1) and
+// the row tiles per virtual expert.
 template <int NB>
-__global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
-    const int32_t *__restrict__ active, const int32_t *__restrict__ counts,
-    const uint8_t *__restrict__ down, int64_t down_stride,
-    const uint8_t *const *__restrict__ down_tab, const float *__restrict__ down_s2,
-    int32_t P, int32_t E, int32_t H, int32_t F, int32_t RT, int32_t nbuf, int32_t ring_bytes,
-    const float *__restrict__ h, float *__restrict__ ypair, const int32_t *__restrict__ ids,
-    int32_t expert_base) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+__device__ __forceinline__ void dn_items(
+    Meta &meta, int (&s_pid)[2][kCols], uint8_t *smem, const IdsLds &il, int32_t *lds_list,
+    bool fused, int P, int H, int F, int tiles, int i0, int i1, int a_first, int na, int nbuf,
+    int ring_bytes, const float *__restrict__ h, float *__restrict__ ypair) {
     const int rb = F / kBlockWeights * kBlockBytes;
-    const int rows = 16 * RT, tile_bytes = rows * rb;
+    const int rows = H / tiles, tile_bytes = rows * rb, RT = rows / 16;
     uint8_t *wb = smem;                                                // [nbuf][rows]
     float *red = reinterpret_cast<float *>(smem + ring_bytes);         // [2][wave][col][16 rows]
-    __shared__ Meta meta;
-    __shared__ int s_pid[2][kCols];   // pair ids of the token columns of the last two items
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 15, q = lane >> 4;
     const int rt = wave % RT, ks = wave / RT, KS = kWaves / RT;
     const int nblk = F / kBlockWeights, blk0 = ks * NB;
-    const int tiles = H / rows;
-
-    // fused layer: the plan from the routed ids, the pair list and the plan's late scratch in
-    // LDS behind the partials
-    const bool fused = ids != nullptr;
-    int32_t *lds_list = reinterpret_cast<int32_t *>(smem + ring_bytes + kRedBytes);
-    const IdsLds il = ids_lds(smem, lds_list + P, E, P);
-
-    int i0, i1, a_first, na = 0;
-    if (fused)
-        plan_ids_a(meta, il, ids, expert_base, down, down_stride, down_tab, down_s2, nullptr, 0,
-                   nullptr, nullptr, E, P, tiles, i0, i1, a_first, na);
-    else
-        load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, down,
-                  down_stride, down_tab, down_s2, nullptr, 0, nullptr, nullptr, E, P, tiles, i0,
-                  i1, a_first);
-    if (i0 >= i1) return;
     const int n_inst = stage_async_count<kThreads>(tile_bytes);
     int ia = 0, it = i0 - a_first * tiles, is = 0;   // stream cursor
     auto issue_next = [&]() {
@@ -1030,6 +1035,58 @@ __global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
         lds_barrier();
         reduce(red + ((u - 1) & 1) * kRedFloats, s_pid[(u - 1) & 1], p_t, p_mt, p_sd);
     }
+}
+
+template <int NB>
+__global__ __launch_bounds__(kThreads, 2) void dn_decode_kernel(
+    const int32_t *__restrict__ offsets, const int32_t *__restrict__ pair_ids,
+    const int32_t *__restrict__ active, const int32_t *__restrict__ counts,
+    const uint8_t *__restrict__ down, int64_t down_stride,
+    const uint8_t *const *__restrict__ down_tab, const float *__restrict__ down_s2,
+    int32_t P, int32_t E, int32_t H, int32_t F, int32_t ks_min, int32_t nbuf,
+    int32_t ring_bytes,
+    const float *__restrict__ h, float *__restrict__ ypair, const int32_t *__restrict__ ids,
+    int32_t expert_base) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    __shared__ Meta meta;
+    __shared__ int s_pid[2][kCols];   // pair ids of the token columns of the last two items
+    const int nblk = F / kBlockWeights;
+
+    // fused layer: the plan from the routed ids, the pair list and the plan's late scratch in
+    // LDS behind the partials
+    const bool fused = ids != nullptr;
+    int32_t *lds_list = reinterpret_cast<int32_t *>(smem + ring_bytes + kRedBytes);
+    const IdsLds il = ids_lds(smem, lds_list + P, E, P);
+
+    // the K split (and with it the row tiles per virtual expert) is the plan's
+    const DnSplit sp{ks_min, nblk, H};
+    int tiles = 0, i0, i1, a_first, na = 0;
+    if (fused)
+        plan_ids_a(meta, il, ids, expert_base, down, down_stride, down_tab, down_s2, nullptr, 0,
+                   nullptr, nullptr, E, P, sp, tiles, i0, i1, a_first, na);
+    else
+        load_plan(meta, reinterpret_cast<int32_t *>(smem), counts, active, offsets, pair_ids, down,
+                  down_stride, down_tab, down_s2, nullptr, 0, nullptr, nullptr, E, P, sp, tiles,
+                  i0, i1, a_first);
+    // workgroup-uniform: kept in scalar registers
+    tiles = __builtin_amdgcn_readfirstlane(tiles);
+    i0 = __builtin_amdgcn_readfirstlane(i0);
+    i1 = __builtin_amdgcn_readfirstlane(i1);
+    a_first = __builtin_amdgcn_readfirstlane(a_first);
+    na = __builtin_amdgcn_readfirstlane(na);
+    if (i0 >= i1) return;
+    // slice width for the chosen split: NB at ks_min, halved (rounded up) per doubling
+    const int KS = kWaves * 16 * tiles / H, nbs = (nblk + KS - 1) / KS;
+    constexpr int NB2 = (NB + 1) / 2, NB4 = (NB + 3) / 4;
+    if (nbs == NB)
+        dn_items<NB>(meta, s_pid, smem, il, lds_list, fused, P, H, F, tiles, i0, i1, a_first, na,
+                     nbuf, ring_bytes, h, ypair);
+    else if (nbs == NB2)
+        dn_items<NB2>(meta, s_pid, smem, il, lds_list, fused, P, H, F, tiles, i0, i1, a_first, na,
+                      nbuf, ring_bytes, h, ypair);
+    else if (nbs == NB4)
+        dn_items<NB4>(meta, s_pid, smem, il, lds_list, fused, P, H, F, tiles, i0, i1, a_first, na,
+                      nbuf, ring_bytes, h, ypair);
 }
 
 // One thread per 4 consecutive outputs of a token row; the grid's y dimension steps over the
@@ -1168,7 +1225,7 @@ size_t ring_plan(size_t tile, size_t scratch, size_t extra, int &nbuf, int &ring
 
 // Everything the two decode launches need, settled on the host before either is enqueued.
 struct DecodeCfg {
-    int nb_gu, nb_dn, rt;
+    int nb_gu, nb_dn, rt, ks_min;
     bool fused, tokcols;
     int gu_nbuf, gu_ring, gu_grid, dn_nbuf, dn_ring, dn_grid;
     size_t gu_lds, dn_lds;
@@ -1178,12 +1235,8 @@ struct DecodeCfg {
 // Down: the smallest K split KS in {1, 2, 4} with at most kMaxDnBlocks blocks per slice, and
 // RT = 4 / KS row tiles per item; H must hold whole items, and two tiles plus the start-up
 // scratch must fit in LDS. fused: the plan is built from the routed ids (a.ids).
-// With few down items (a union of a few experts) KS is raised further, while the slices
-// average two blocks or more and the items at RT = 4 times KS stay under kDnSpreadItems:
-// smaller items spread over more workgroups, and each wave then loads only its slice of the h
-// rows. Measured down kernel, KS 1 / 2 / 4: 10 experts (tiny decode) 17.1 / 15.5 / 14.7 us,
-// 30 experts 21.1 / 20.9 / 25.1 us with the layer 45.0 / 43.5 / 48.9 us, 60 experts 25.7 /
-// 28.2 / 38.6 us.
+// That KS is the smallest the down kernel takes; it raises it on the device for a union of few
+// experts (dn_ks).
 int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     const int bh = a.H / kBlockWeights, bf = a.F / kBlockWeights;
     const int32_t P = a.T * a.k;
@@ -1191,10 +1244,9 @@ int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     c.nb_gu = (bh + kWaves - 1) / kWaves;
     int ks = 1;
     while (ks < kWaves && (bf + ks - 1) / ks > kMaxDnBlocks) ks *= 2;
-    const int64_t items4 = (int64_t)max_v * (a.H / (16 * kWaves));   // items at RT = 4
-    while (ks < kWaves && 2 * (2 * ks) <= bf && items4 * ks < kDnSpreadItems) ks *= 2;
+    c.ks_min = ks;
     c.nb_dn = (bf + ks - 1) / ks;
-    c.rt = kWaves / ks;
+    c.rt = kWaves / ks;   // the most row tiles per item: the LDS tile size
     if (c.nb_gu > kMaxGuBlocks || c.nb_dn > kMaxDnBlocks || a.H % (16 * c.rt)) return MOE_ESHAPE;
     if (fused && (P > kIdsMaxPairs || a.E > kIdsMaxExperts)) return MOE_ESHAPE;
     c.fused = fused;
@@ -1215,10 +1267,16 @@ int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     const int rows = 16 * c.rt;
     c.dn_lds = ring_plan(rows * (size_t)row_bytes(a.F), scratch, extra, c.dn_nbuf, c.dn_ring, wgs);
     if (!c.dn_lds) return MOE_ESHAPE;
-    const int dn_tiles = a.H / rows;
-    c.dn_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_v * dn_tiles);
-    if (max_experts((int64_t)max_v * dn_tiles, dn_tiles, c.dn_grid) > kMaxMeta)
-        return MOE_ESHAPE;
+    // the kernel splits K from ks_min up to ks_max (one virtual expert): the grid is sized for
+    // the finest items, and every split keeps a workgroup's experts within kMaxMeta
+    const DnSplit sp{c.ks_min, bf, a.H};
+    const int ks_max = dn_ks(sp, 1);
+    c.dn_grid = (int)std::min<int64_t>(wgs * kCUs, (int64_t)max_v * (a.H * ks_max / 64));
+    for (int kk = c.ks_min; kk <= ks_max; kk *= 2) {
+        const int dn_tiles = a.H * kk / 64;
+        if (max_experts((int64_t)max_v * dn_tiles, dn_tiles, c.dn_grid) > kMaxMeta)
+            return MOE_ESHAPE;
+    }
     return MOE_OK;
 }
 
@@ -1251,7 +1309,7 @@ int launch_dn(const FfnArgs &a, const DecodeWs &d, const DecodeCfg &c, hipStream
     prof_start(MOE_KERNEL_DN_DECODE, s);
     hipLaunchKernelGGL(kern, dim3(c.dn_grid), dim3(kThreads), c.dn_lds, s, a.offsets, a.pair_ids,
                        a.active, a.counts, a.down.base, a.down.expert_stride, a.down.experts,
-                       a.down.scale2, a.T * a.k, a.E, a.H, a.F, c.rt, c.dn_nbuf, c.dn_ring, d.h,
+                       a.down.scale2, a.T * a.k, a.E, a.H, a.F, c.ks_min, c.dn_nbuf, c.dn_ring, d.h,
                        d.ypair, a.ids, a.expert_base);
     prof_stop(MOE_KERNEL_DN_DECODE, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
