@@ -1244,6 +1244,9 @@ int decode_plan(const FfnArgs &a, bool fused, DecodeCfg &c) {
     c.nb_gu = (bh + kWaves - 1) / kWaves;
     int ks = 1;
     while (ks < kWaves && (bf + ks - 1) / ks > kMaxDnBlocks) ks *= 2;
+    // the split the kernel would take for the most virtual experts the routing can make is the
+    // least it can take (dn_ks falls with the count): start there, in the narrowest kernel
+    ks = dn_ks(DnSplit{ks, bf, a.H}, max_v);
     c.ks_min = ks;
     c.nb_dn = (bf + ks - 1) / ks;
     c.rt = kWaves / ks;   // the most row tiles per item: the LDS tile size
