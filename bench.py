@@ -50,8 +50,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "c028d242ecb6d0b9c505cc63afa94e3ec17a74ead381e22ba4b4d90bda7c37dd",
-        "fetch_kib": 54366.9, "write_kib": 168.5,
+        "sha256": "654435f61108806698e790f3cc1b3b4375bcd8466777263c14c7e4b5477e3fcd",
+        "fetch_kib": 54366.9, "write_kib": 168.6,
     },
 }
 
