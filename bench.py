@@ -50,7 +50,7 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "654435f61108806698e790f3cc1b3b4375bcd8466777263c14c7e4b5477e3fcd",
+        "sha256": "36e2c02014666ade25c8ae6684a9234c88bd23602e24421723e829b4010e9bfb",
         "fetch_kib": 54366.9, "write_kib": 168.6,
     },
 }

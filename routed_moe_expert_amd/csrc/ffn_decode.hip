@@ -22,9 +22,12 @@
 //              slices are unscaled, summed across the waves through LDS, and the epilogue
 //              writes h = SiLU(g) * u (fp32) in CSR pair order.
 //   dn_decode: items of 16*RT down rows; RT row tiles x (4/RT) K slices of ff over the four
-//              waves. B is the expert's h rows, scaled per (pair, K slice) and split into
-//              f16 hi + lo (about 22 significant bits), two MFMAs per step. Slices are summed
-//              through LDS into the per-pair rows ypair (row = pair id).
+//              waves, the split KS = 4/RT chosen by the kernel once its plan has counted the
+//              virtual experts (more slices for a union of a few experts, so that the smaller
+//              items reach every workgroup). B is the expert's h rows, scaled per (pair, K
+//              slice) and split into f16 hi + lo (about 22 significant bits), two MFMAs per
+//              step. Slices are summed through LDS into the per-pair rows ypair (row = pair
+//              id).
 //   combine:   y[t] = sum over t's local slots in ascending j of w[t,j] * ypair[t*k + j]; the
 //              pair -> CSR slot map only says which slots are local.
 //

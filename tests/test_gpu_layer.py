@@ -65,7 +65,11 @@ def test_layer_matches_two_calls(seed, T, k, E, H, F, frac, base, fused):
         assert_parity(y1, ref, f"layer path {path}")
 
 
-@pytest.mark.parametrize("name,T,U", [("tiny_decode", 1, None), ("verify_chunk", 6, 60),
+# the down kernel's K split is chosen on the device from the counted experts: 4 for tiny decode
+# and the 10-expert union, 2 for the 30-expert union and the shared expert, 1 for the rest
+@pytest.mark.parametrize("name,T,U", [("tiny_decode", 1, None), ("verify_chunk", 6, 10),
+                                      ("verify_chunk", 6, 30), ("verify_chunk", 6, 60),
+                                      ("shared_expert", 128, None),
                                       ("e256_plateau", 16, None), ("e256_plateau", 128, None)])
 def test_layer_workloads(name, T, U):
     print(f"[case] layer workload {name} T={T} U={U}", flush=True)
