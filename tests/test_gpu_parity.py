@@ -83,6 +83,12 @@ SMALL = [
     (4, 40, 2, 2, 256, 64, "pow2", 0.0, 0, False),     # > 8 tokens per expert: token chunks
     (5, 3, 6, 4, 768, 128, "all", 0.5, 0, True),       # duplicates within tokens
     (6, 12, 3, 16, 256, 320, "all", 0.0, 0, False),
+    # the down kernel's K split taken on the device, from its smallest to a wider one: ff 576
+    # (9 blocks: slices of 9 or 5), ff 1280 (20 blocks: from 2 slices of 10 to 4 of 5), ff 2560
+    # (40 blocks: 4 slices of 10, no wider), each with a union of a few experts
+    (7, 2, 3, 64, 512, 576, "all", 0.0, 0, False),
+    (8, 3, 2, 32, 1024, 1280, "all", 0.1, 0, True),
+    (9, 2, 2, 8, 256, 2560, "all", 0.0, 0, False),
 ]
 
 
@@ -123,6 +129,21 @@ def test_decode_workloads(name, T, U):
     y = dc.run(moe.MOE_PATH_AUTO)
     _check_bucket(dc)
     assert_parity(y, oracle.ffn_union(case), name)
+
+
+@pytest.mark.parametrize("F,U", [(640, 10), (640, 30), (1280, 10)])
+def test_decode_union_split(F, U):
+    """A union of a few experts in a routing that could hold many (60 pairs over 64 experts): the
+    host sizes the down kernel for the widest union (one K slice at ff 640, two at ff 1280) and
+    the kernel widens its K split once its plan has counted the experts (4 slices for 10 experts,
+    2 for 30). Every token against the oracle."""
+    _print_case("decode_union_split", F=F, U=U)
+    case = gen.make_random_case(500 + U + F, 6, 10, 64, 2560, F, fused=(F == 640))
+    case["ids"] = gen.route_union(500 + U, 6, 10, 64, U).astype(np.int32)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_DECODE)
+    _check_bucket(dc)
+    assert_parity(y, oracle.ffn_union(case), "decode_union_split")
 
 
 def test_decode_beyond_slice_width_uses_gemm_path():
