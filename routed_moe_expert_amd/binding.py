@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 MOE_OK, MOE_EINVAL, MOE_EWS, MOE_ESHAPE, MOE_ELAUNCH = 0, 1, 2, 3, 4
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
 MOE_AUTO_PAIRS_PER_EXPERT = 32
+MOE_KPACK_ROWS = 256
 (MOE_KERNEL_NONE, MOE_KERNEL_BUCKET, MOE_KERNEL_GU_DECODE, MOE_KERNEL_DN_DECODE, MOE_KERNEL_COMBINE,
  MOE_KERNEL_SCHEDULE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_DN_PREFILL, MOE_KERNEL_ROUTER) = range(9)
 
@@ -28,7 +29,8 @@ class MoeError(RuntimeError):
 
 class moe_bank(ctypes.Structure):
     _fields_ = [("base", ctypes.c_void_p), ("expert_stride", ctypes.c_int64),
-                ("scale2", ctypes.c_void_p), ("experts", ctypes.c_void_p)]
+                ("scale2", ctypes.c_void_p), ("experts", ctypes.c_void_p),
+                ("kpack", ctypes.c_void_p)]
 
 
 def _load():
@@ -61,6 +63,10 @@ def _load():
     l.moe_ffn_nvfp4_static.restype = ctypes.c_int
     l.moe_ffn_nvfp4_static.argtypes = [vp, vp, vp, vp, vp, vp, moe_bank, moe_bank, moe_bank,
                                        i32, i32, i32, i32, i32, vp, i32, vp]
+    l.moe_kpack_bytes.restype = sz
+    l.moe_kpack_bytes.argtypes = [i32, i32, i32]
+    l.moe_kpack.restype = ctypes.c_int
+    l.moe_kpack.argtypes = [moe_bank, i32, i32, i32, vp, vp]
     l.moe_router_topk.restype = ctypes.c_int
     l.moe_router_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp]
     l.moe_profile_kernel.restype = ctypes.c_int
@@ -127,17 +133,42 @@ def moe_route_bucket(topk_ids, T: int, k: int, E: int, expert_base: int, offsets
     return _check("moe_route_bucket", st, raise_on_error)
 
 
-def bank(base, expert_stride: int, byte_offset: int = 0, scale2=None, experts=None) -> moe_bank:
+def bank(base, expert_stride: int, byte_offset: int = 0, scale2=None, experts=None,
+         kpack=None) -> moe_bank:
     """A moe_bank for a device tensor (or address) plus an optional byte offset, and optionally
-    the bank's per-expert fp32 second-level scales (a device tensor of E floats) and a per-expert
-    pointer table (a device int64 tensor of E addresses; base and expert_stride are then unused).
+    the bank's per-expert fp32 second-level scales (a device tensor of E floats), a per-expert
+    pointer table (a device int64 tensor of E addresses; base and expert_stride are then unused)
+    and a K-step-packed copy of the same weights for the GEMM path (a device uint8 tensor that
+    moe_kpack wrote).
 
     The bank holds raw addresses, so it also keeps a reference to every tensor it was given
     (`_keep`): their memory cannot be freed and reused while the bank object is alive. Addresses
     passed as ints are the caller's to keep valid."""
     b = moe_bank(_ptr(base) + byte_offset if base is not None else None, int(expert_stride),
-                 _ptr(scale2) or None, _ptr(experts) or None)
-    b._keep = tuple(t for t in (base, scale2, experts) if t is not None and not isinstance(t, int))
+                 _ptr(scale2) or None, _ptr(experts) or None, _ptr(kpack) or None)
+    b._keep = tuple(t for t in (base, scale2, experts, kpack)
+                    if t is not None and not isinstance(t, int))
+    return b
+
+
+def moe_kpack_bytes(E: int, out_f: int, in_f: int) -> int:
+    return int(lib.moe_kpack_bytes(E, out_f, in_f))
+
+
+def moe_kpack(src: moe_bank, E: int, out_f: int, in_f: int, dst, stream=None,
+              raise_on_error: bool = True) -> int:
+    st = lib.moe_kpack(src, E, out_f, in_f, _ptr(dst), _stream(stream))
+    return _check("moe_kpack", st, raise_on_error)
+
+
+def with_kpack(src: moe_bank, E: int, out_f: int, in_f: int, stream=None) -> moe_bank:
+    """A copy of bank src that also carries its K-step-packed copy (allocated here as a device
+    uint8 tensor and written by moe_kpack on the stream)."""
+    import torch
+    dst = torch.empty(moe_kpack_bytes(E, out_f, in_f), dtype=torch.uint8, device="cuda")
+    moe_kpack(src, E, out_f, in_f, dst, stream)
+    b = moe_bank(src.base, src.expert_stride, src.scale2, src.experts, dst.data_ptr())
+    b._keep = getattr(src, "_keep", ()) + (dst,)
     return b
 
 

@@ -15,10 +15,17 @@ namespace {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool bank_ok(const moe_bank &b) {
-    if (!aligned(b.scale2, 4)) return false;
+    if (!aligned(b.scale2, 4) || !aligned(b.kpack, 16)) return false;
     if (b.experts != nullptr) return aligned(b.experts, 8);   // base and stride unused
     return b.base != nullptr && aligned(b.base, 16) && b.expert_stride >= 0 &&
            b.expert_stride % 16 == 0;
+}
+
+// The three banks of an FFN call: each valid, and gate and up either both with a K-step-packed
+// copy or both without (the gate/up GEMM reads both from one form).
+bool banks_ok(const moe_bank &gate, const moe_bank &up, const moe_bank &down) {
+    return bank_ok(gate) && bank_ok(up) && bank_ok(down) &&
+           (gate.kpack == nullptr) == (up.kpack == nullptr);
 }
 
 int check_common(int32_t T, int32_t k, int32_t E) {
@@ -89,7 +96,7 @@ int moe_ffn_nvfp4(const uint16_t *x, const float *topk_w, const int32_t *offsets
     if (!x || !topk_w || !offsets || !pair_ids || !active || !counts || !y || !ws)
         return MOE_EINVAL;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return MOE_EINVAL;
-    if (!bank_ok(gate) || !bank_ok(up) || !bank_ok(down)) return MOE_EINVAL;
+    if (!banks_ok(gate, up, down)) return MOE_EINVAL;
     if (ws_bytes < moe_ffn_nvfp4_ws(T, k, E, H, F)) return MOE_EWS;
     FfnArgs a{x, topk_w, offsets, pair_ids, active, counts, gate, up, down, T, k, E, H, F, y,
               ws, ws_bytes};
@@ -126,7 +133,7 @@ int moe_layer_nvfp4(const int32_t *topk_ids, int32_t expert_base, const uint16_t
     if (T == 0) return MOE_OK;
     if (!topk_ids || !x || !topk_w || !y || !ws) return MOE_EINVAL;
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(ws, 256)) return MOE_EINVAL;
-    if (!bank_ok(gate) || !bank_ok(up) || !bank_ok(down)) return MOE_EINVAL;
+    if (!banks_ok(gate, up, down)) return MOE_EINVAL;
     if (ws_bytes < moe_layer_nvfp4_ws(T, k, E, H, F)) return MOE_EWS;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const size_t csr = layer_csr_bytes(T, k, E);
@@ -165,6 +172,19 @@ int moe_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_
     if (!logits || !topk_ids || !topk_w) return MOE_EINVAL;
     return launch_router_topk(logits, T, E, k, topk_ids, topk_w,
                               reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t moe_kpack_bytes(int32_t E, int32_t out_f, int32_t in_f) {
+    if (E < 1 || out_f < 1 || in_f < kBlockWeights || in_f % kBlockWeights) return 0;
+    return (size_t)E * (size_t)kpack_expert_bytes(out_f, in_f);
+}
+
+int moe_kpack(moe_bank src, int32_t E, int32_t out_f, int32_t in_f, uint8_t *dst,
+              moe_stream_t stream) {
+    if (E < 1 || out_f < 1 || in_f < kBlockWeights || in_f % kBlockWeights) return MOE_EINVAL;
+    if (!dst || !aligned(dst, 16) || !bank_ok(src)) return MOE_EINVAL;
+    if (out_f > MOE_MAX_HIDDEN || in_f > MOE_MAX_HIDDEN || E > MOE_MAX_EXPERTS) return MOE_ESHAPE;
+    return launch_kpack(src, E, out_f, in_f, dst, reinterpret_cast<hipStream_t>(stream));
 }
 
 int moe_profile_kernel(int32_t kernel_id, void *const *start_events, void *const *stop_events,

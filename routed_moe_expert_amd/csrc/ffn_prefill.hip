@@ -235,6 +235,7 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     const int32_t *__restrict__ n_tiles, int32_t max_tiles, int32_t n_ntiles,
     const uint8_t *__restrict__ w0, int64_t s0, const uint8_t *const *__restrict__ t0,
     const uint8_t *__restrict__ w1, int64_t s1, const uint8_t *const *__restrict__ t1,
+    const uint8_t *__restrict__ kp0, const uint8_t *__restrict__ kp1,
     const float *__restrict__ w0_s2, const float *__restrict__ w1_s2,
     int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
     uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int32_t *__restrict__ hs,
@@ -297,20 +298,28 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     lds_barrier();
 
     // A: load i of a wave covers units (i*kWaves + wave)*64 + lane (unit j = u % 3 of row
-    // u / 3); loads whose units all lie past kAUnits are skipped by the whole wave
+    // u / 3); loads whose units all lie past kAUnits are skipped by the whole wave. From a
+    // K-step-packed copy (kp0, kp1) a bank's N tile is one row group, whose K step b is one run
+    // of kKpackRows 36-byte blocks (rows past the matrix are zero there); from the row-major bank
+    // each row's block sits at the row's start plus 36 b (rows past the matrix read the last).
+    static_assert((DOWN ? kRows : kRows / 2) == kKpackRows, "an N tile is one packed row group");
+    const bool packed = kp0 != nullptr;
+    const int64_t astep = packed ? (int64_t)kKpackRows * kBlockBytes : kBlockBytes;
+    const int64_t epack = kpack_expert_bytes(n_out, K);
     const uint8_t *asrc[kALoadsMax];
 #pragma unroll
     for (int i = 0; i < kALoadsMax; i++) {
         const int u = min((i * kWaves + wave) * 64 + lane, kAUnits - 1);
         const int row = u / 3;
+        const int half = DOWN ? kRows : kRows / 2;   // gate/up: gate rows, then the up rows
+        const bool second = !DOWN && row >= half;
+        const int r = second ? row - half : row;     // row within the bank's N tile
         const uint8_t *base;
-        if (DOWN) {
-            base = e0 + (int64_t)min(nt * kRows + row, n_out - 1) * rb;
-        } else {
-            const int half = kRows / 2;   // gate rows, then the matching up rows
-            const int f = min(nt * half + (row < half ? row : row - half), n_out - 1);
-            base = (row < half ? e0 : e1) + (int64_t)f * rb;
-        }
+        if (packed)
+            base = (second ? kp1 : kp0) + e * epack + (int64_t)nt * nblk * astep +
+                   (int64_t)r * kBlockBytes;
+        else
+            base = (second ? e1 : e0) + (int64_t)min(nt * half + r, n_out - 1) * rb;
         asrc[i] = base + 12 * (u % 3);
     }
     static_assert(kAUnits == kALoadsMax * kThreads, "every lane issues kALoadsMax A loads");
@@ -337,7 +346,7 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     auto issue_one = [&](int kb, int li) {
         uint8_t *st = smem + (kb % kStages) * kStageBytes;
         if (li < kALoadsMax) {
-            dma12(asrc[li] + kb * kBlockBytes, st + (li * kWaves + wave) * 1024);
+            dma12(asrc[li] + kb * astep, st + (li * kWaves + wave) * 1024);
         } else {
             const int o = (li - kALoadsMax) / kBUnits, i = (li - kALoadsMax) % kBUnits;
             dma16(bsrc[o][i] + kb * 64, st + kABytes + o * kBBytesW + (i * kWaves + wave) * 1024);
@@ -586,14 +595,16 @@ int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
         hipLaunchKernelGGL((gemm_kernel<true>), dim3(grid), dim3(kThreads), lds, s, nullptr,
                            w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt, n_ntiles,
                            a.down.base, a.down.expert_stride, a.down.experts, nullptr, (int64_t)0,
-                           nullptr, a.down.scale2, nullptr, a.k, a.F, a.F, a.H, nullptr, nullptr,
+                           nullptr, a.down.kpack, nullptr, a.down.scale2, nullptr, a.k, a.F, a.F,
+                           a.H, nullptr, nullptr,
                            nullptr, w.hs, w.ypair);
     else
         hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kThreads), lds, s,
                            (const uint16_t *)w.x16, nullptr, nullptr, a.offsets, a.pair_ids,
                            w.tiles, w.n_tiles, mt, n_ntiles, a.gate.base, a.gate.expert_stride,
                            a.gate.experts, a.up.base, a.up.expert_stride, a.up.experts,
-                           a.gate.scale2, a.up.scale2, a.k, a.H,
+                           a.gate.kpack, a.gate.kpack ? a.up.kpack : nullptr, a.gate.scale2,
+                           a.up.scale2, a.k, a.H,
                            a.F, a.H,
                            (const int32_t *)w.xs, w.h_hi, w.h_lo, w.hs, nullptr);
     prof_stop(id, s);

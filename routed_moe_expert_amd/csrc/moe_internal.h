@@ -15,6 +15,12 @@ constexpr int kBlockWeights = 64;  // NVFP4: weights per block
 constexpr int kBlockBytes = 36;    // NVFP4: 4 UE4M3 scale bytes + 32 code bytes
 
 inline int64_t row_bytes(int64_t in_f) { return in_f / kBlockWeights * kBlockBytes; }
+// K-step-packed banks (moe_kpack): rows per group, and bytes per expert of the packed copy
+constexpr int kKpackRows = MOE_KPACK_ROWS;
+__host__ __device__ inline int64_t kpack_expert_bytes(int64_t out_f, int64_t in_f) {
+    return (out_f + kKpackRows - 1) / kKpackRows * (in_f / kBlockWeights) * kKpackRows *
+           kBlockBytes;
+}
 
 // SiLU(z) = z * sigmoid(z), with the hardware reciprocal (about 1 ulp) in place of a division.
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
@@ -126,6 +132,9 @@ bool decode_supported(const FfnArgs &a);         // shape within the decode kern
 bool decode_fused_supported(const FfnArgs &a);   // ... and the in-kernel bucketing's
 int launch_decode(const FfnArgs &a, hipStream_t s);
 int launch_prefill(const FfnArgs &a, hipStream_t s);
+
+int launch_kpack(const moe_bank &src, int32_t E, int32_t out_f, int32_t in_f, uint8_t *dst,
+                 hipStream_t s);
 
 int launch_router_topk(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *ids,
                        float *w, hipStream_t s);

@@ -57,6 +57,17 @@ class DeviceCase:
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=dev)
         self.y = torch.empty(max(self.T, 1), H, dtype=torch.float32, device=dev)
 
+    def use_kpack(self, on: bool = True):
+        """Give the three banks their K-step-packed copies (moe_kpack, made once and kept), so that
+        the GEMM path reads those, or go back to the row-major banks alone."""
+        if not hasattr(self, "_plain"):
+            g, u, d = self._plain = (self.gate, self.up, self.down)
+            self._packed = (moe.with_kpack(g, self.E, self.F, self.H),
+                            moe.with_kpack(u, self.E, self.F, self.H),
+                            moe.with_kpack(d, self.E, self.H, self.F))
+            torch.cuda.synchronize()
+        self.gate, self.up, self.down = self._packed if on else self._plain
+
     def bucket(self, stream=None):
         moe.moe_route_bucket(self.ids, self.T, self.k, self.E, self.base, self.offsets,
                              self.pair_ids, self.active, self.counts, self.bucket_ws, self.bws,

@@ -70,6 +70,9 @@ def _ffn(**over):
     (dict(gate=moe_bank(0, 0, None, FAKE + 4)), moe.MOE_EINVAL),      # pointer table misaligned
     (dict(down=moe_bank(FAKE, 4096, FAKE + 2)), moe.MOE_EINVAL),      # scale2 misaligned
     (dict(ws=FAKE + 16), moe.MOE_EINVAL),
+    (dict(gate=moe_bank(FAKE, 4096, None, None, FAKE + 8)), moe.MOE_EINVAL),  # kpack misaligned
+    (dict(gate=moe_bank(FAKE, 4096, None, None, FAKE)), moe.MOE_EINVAL),  # gate packed, up not
+    (dict(up=moe_bank(FAKE, 4096, None, None, FAKE)), moe.MOE_EINVAL),    # up packed, gate not
     (dict(E=4096), moe.MOE_ESHAPE), (dict(H=1 << 15), moe.MOE_ESHAPE),
     (dict(ws_bytes=16), moe.MOE_EWS),
     (dict(T=0), moe.MOE_OK), (dict(T=0, x=0, y=0), moe.MOE_OK),
@@ -150,6 +153,32 @@ def test_router_host_checks(over, status):
     assert _router(**over) == status
 
 
+def test_kpack_sizes():
+    """The packed copy: E x row groups of MOE_KPACK_ROWS x K steps x a 36-byte block per row."""
+    R = moe.MOE_KPACK_ROWS
+    assert R == 256
+    assert moe.moe_kpack_bytes(288, 1280, 4096) == 288 * 5 * 64 * R * 36    # exact row groups
+    assert moe.moe_kpack_bytes(288, 640, 4096) == 288 * 3 * 64 * R * 36     # 640 rows: 3 groups
+    assert moe.moe_kpack_bytes(288, 4096, 640) == 288 * 16 * 10 * R * 36
+    assert moe.moe_kpack_bytes(1, 1, 64) == R * 36
+    for bad in ((0, 64, 64), (1, 0, 64), (1, 64, 0), (1, 64, 96), (-1, 64, 64)):
+        assert moe.moe_kpack_bytes(*bad) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(dst=0), moe.MOE_EINVAL), (dict(dst=FAKE + 4), moe.MOE_EINVAL),
+    (dict(E=0), moe.MOE_EINVAL), (dict(out_f=0), moe.MOE_EINVAL), (dict(in_f=96), moe.MOE_EINVAL),
+    (dict(src=_bank(FAKE + 4)), moe.MOE_EINVAL), (dict(src=_bank(0)), moe.MOE_EINVAL),
+    (dict(E=4096), moe.MOE_ESHAPE), (dict(out_f=1 << 15), moe.MOE_ESHAPE),
+    (dict(in_f=1 << 15), moe.MOE_ESHAPE),
+])
+def test_kpack_host_checks(over, status):
+    a = dict(src=_bank(), E=8, out_f=256, in_f=256, dst=FAKE)
+    a.update(over)
+    assert moe.moe_kpack(a["src"], a["E"], a["out_f"], a["in_f"], a["dst"], stream=0,
+                         raise_on_error=False) == status
+
+
 def test_bank_keeps_its_tensors_alive():
     """A moe_bank stores raw addresses; bank() must hold the tensors behind them, so that a
     table or weight tensor cannot be freed (and its memory reused) while the bank is in use."""
@@ -160,10 +189,12 @@ def test_bank_keeps_its_tensors_alive():
     base = torch.zeros(4096, dtype=torch.uint8)
     s2 = torch.ones(4, dtype=torch.float32)
     tab = torch.tensor([base.data_ptr()] * 4, dtype=torch.int64)
-    refs = [weakref.ref(t) for t in (base, s2, tab)]
-    b = moe.bank(base, 1024, 16, scale2=s2, experts=tab)
+    kp = torch.zeros(1024, dtype=torch.uint8)
+    refs = [weakref.ref(t) for t in (base, s2, tab, kp)]
+    b = moe.bank(base, 1024, 16, scale2=s2, experts=tab, kpack=kp)
     assert b.base == base.data_ptr() + 16 and b.experts == tab.data_ptr()
-    del base, s2, tab
+    assert b.kpack == kp.data_ptr()
+    del base, s2, tab, kp
     gc.collect()
     assert all(r() is not None for r in refs)
     del b
