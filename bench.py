@@ -14,6 +14,10 @@ launch rate. The layer time is the mean over K back-to-back layers between two e
 pass with an event between every two layers gives the per-step distribution (those events are
 queue packets of their own and add about 3 us per decode layer).
 
+Where a layer runs the grouped-GEMM path, its banks also carry their K-step-packed copies
+(moe_kpack, written once before any timing, as a model would at load time), which the GEMMs read;
+`--no-kpack` times the GEMMs on the row-major banks. The decode path reads the row-major banks.
+
 Prints one JSON line: value = unique-expert weight bytes per second (decode workloads) or useful
 TFLOP/s (prefill workloads), the dominant kernel's roofline from HIP events recorded around its
 launches, the fp64 oracle timed on a bounded sample on the host cores, and `rows`: the same
@@ -110,6 +114,8 @@ def parse():
                     help="shared_expert: route it as G caller-side virtual experts over its one "
                          "weight copy (0: the one expert, E=1)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "prefill"])
+    ap.add_argument("--no-kpack", action="store_true",
+                    help="GEMM path from the row-major banks (default: from K-step-packed copies)")
     ap.add_argument("--warm", action="store_true", help="reuse one routing (cache-warm numbers)")
     ap.add_argument("--layer-only", action="store_true",
                     help="time only the one-call layer (not also the two calls), e.g. under a profiler")
@@ -244,8 +250,20 @@ def make_banks_host(gen, name):
     return gen.make_banks(w["E"], w["H"], w["F"], w["fused"], w["seed"])
 
 
-def build_inputs(name, T, U, warm, virtual, torch, gen, moe, host_banks=None):
-    """Host generation + upload of one workload at T tokens."""
+def uses_gemm(gen, moe, name, T, path, args):
+    """Whether the layer runs the GEMM path (and so reads K-step-packed copies unless --no-kpack);
+    the packed copies are made only then."""
+    if args.no_kpack or name == "shared_expert":
+        return False
+    w = gen.WORKLOADS[name]
+    p = path if path != moe.MOE_PATH_AUTO else moe.moe_auto_path(T, w["k"], w["E"], w["H"],
+                                                                 w["F"])
+    return p == moe.MOE_PATH_PREFILL
+
+
+def build_inputs(name, T, U, warm, virtual, torch, gen, moe, host_banks=None, kpack=False):
+    """Host generation + upload of one workload at T tokens. kpack: the banks also carry their
+    K-step-packed copies (moe_kpack, written here, before any timing), which the GEMM path reads."""
     import numpy as np
 
     w = gen.WORKLOADS[name]
@@ -292,12 +310,17 @@ def build_inputs(name, T, U, warm, virtual, torch, gen, moe, host_banks=None):
                     for b in strided]
             gate, up, down = (moe.bank(None, 0, experts=tb) for tb in tabs)
             gate._keep += (strided,)   # the tables point into these banks' tensors
+        if kpack:
+            gate, up, down = (moe.with_kpack(gate, E, F, H), moe.with_kpack(up, E, F, H),
+                              moe.with_kpack(down, E, H, F))
+            torch.cuda.synchronize()
         bank_sets.append((gate, up, down))
     ids_dev = [t(v.reshape(-1).astype(np.int32)) for v in variants]
     uniq = [1] if virtual else [int(np.unique(v).size) for v in variants]
     out = dict(name=name, E=virtual or E, H=H, F=F, k=k, T=T, U=U, copies=copies,
                variants=variants, ids=ids_dev, uniq=uniq, x=t(x), w=t(wts.reshape(-1)),
-               bank_sets=bank_sets, host=dict(x=x, w=wts, banks=banks), virtual=virtual)
+               bank_sets=bank_sets, host=dict(x=x, w=wts, banks=banks), virtual=virtual,
+               kpack=kpack)
     if virtual:   # the oracle takes the plain one-expert form
         out.update(oracle_E=E, oracle_ids=np.zeros((T, 1), dtype=np.int32))
     return out
@@ -475,7 +498,7 @@ def main():
     T = args.T or DEFAULT_T[name]
     t_wall = time.perf_counter()
     D = build_inputs(name, T, args.U if name == "verify_chunk" else None, args.warm, args.virtual,
-                     torch, gen, moe)
+                     torch, gen, moe, kpack=uses_gemm(gen, moe, name, T, path, args))
     res = measure(D, path, K, W, q, torch, moe, two_calls=not args.layer_only)
     decode = res["decode"]
     kname = "gu_decode_kernel" if decode else "gemm_kernel<false>"   # gate/up (+ SiLU)
@@ -495,6 +518,7 @@ def main():
         roof["traffic_detail"] = tr
 
     desc, note = describe(D), hbm_note(D, args.warm)
+    D_kpack = D["kpack"]
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(args, D, unit)
@@ -507,11 +531,13 @@ def main():
         for wl, Tr, Ur in ROWS:
             if wl not in host_banks:
                 host_banks = {wl: make_banks_host(gen, wl)}   # one workload's banks at a time
-            Dr = build_inputs(wl, Tr, Ur, args.warm, 0, torch, gen, moe, host_banks[wl])
+            Dr = build_inputs(wl, Tr, Ur, args.warm, 0, torch, gen, moe, host_banks[wl],
+                              kpack=uses_gemm(gen, moe, wl, Tr, moe.MOE_PATH_AUTO, args))
             r = measure(Dr, moe.MOE_PATH_AUTO, K, W, q, torch, moe, two_calls=not args.layer_only)
             r.update(workload=describe(Dr), name=wl, T=Tr, U=Dr["U"], E=Dr["E"], H=Dr["H"],
                      F=Dr["F"], top_k=Dr["k"], path="decode" if r["decode"] else "prefill",
-                     hbm=hbm_note(Dr, args.warm))
+                     hbm=hbm_note(Dr, args.warm),
+                     gemm_weights="kpack" if Dr["kpack"] else "row-major")
             del r["decode"]
             rows.append(r)
             print(f"[row] {r['workload']}: {r['layer_us']['mean']:.1f} us per layer, "
@@ -526,7 +552,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f16",
         "data": "synthetic",
         "config": {"workload": desc, "T": T, "path": "decode" if decode else "prefill",
-                   "hbm": note},
+                   "hbm": note,
+                   "gemm_weights": "kpack" if D_kpack else "row-major"},
         "layer": res["layer_us"],
         "two_call_layer_us": res["two_call_layer_us"],
         "unique_expert_bytes": res["unique_expert_bytes"],
