@@ -55,11 +55,13 @@ constexpr int kBRow = 64 * 2;          // bytes of one token row per K step (64 
 constexpr int kBBytes = kBM * kBRow;   // 16 KB per B operand per stage (128 tokens)
 constexpr int kRowsW = 64;            // A rows per wave
 
-// gate/up: 8 waves, one workgroup per CU, three LDS stages (two K steps in flight); down: 4
-// waves, two workgroups per CU, two stages (one step in flight per workgroup, while the other
-// workgroup of the CU computes)
+// gate/up: 8 waves, one workgroup per CU, three LDS stages (two K steps in flight), four from
+// K-step-packed copies (DENSE: rows staged at 36 bytes instead of 48); down: 4 waves, two
+// workgroups per CU, two stages (one step in flight per workgroup, while the other workgroup of
+// the CU computes)
 template <bool DOWN> constexpr int gemm_threads() { return DOWN ? 256 : 512; }
-template <bool DOWN> constexpr int gemm_stages() { return DOWN ? 2 : 3; }
+template <bool DOWN, bool DENSE> constexpr int gemm_stages() { return DOWN ? 2 : DENSE ? 4 : 3; }
+template <bool DOWN, bool DENSE> constexpr int gemm_a_pitch() { return DENSE ? 36 : 48; }
 // h features per gate/up N tile (256): one h scale segment
 constexpr int kSegF = kRowsW / 2 * (gemm_threads<false>() / 64);
 constexpr int kMaxSeg = 32;           // h scale segments per pair: ff <= 32 * 256
@@ -215,19 +217,22 @@ __host__ __device__ constexpr int blk_lds(int b) { return 16 * (b / 12) + b % 12
 __device__ __forceinline__ int b_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ b_swz(r)); }
 
-// One workgroup: N tile nt (512 weight rows) of M tile ti (gate/up: all of its up to 128 pairs;
-// down: the half hf of 64 pairs). DOWN = false: gate/up (A rows are 256 gate rows then the
-// matching up rows; K = H; B = x rows by token); DOWN = true: down (A rows are 512 rows of W_d;
-// K = F; B = h_hi and h_lo rows by CSR slot, with their scale exponents per 256-feature
-// segment). N tiles may run past the matrix: rows beyond it
-// read the last row and are not stored.
+// One workgroup: N tile nt of M tile ti (gate/up: 512 weight rows, all of the tile's up to 128
+// pairs; down: 256 rows, the half hf of 64 pairs). DOWN = false: gate/up (A rows are 256 gate
+// rows then the matching up rows; K = H; B = x rows by token); DOWN = true: down (A rows are 256
+// rows of W_d; K = F; B = h_hi and h_lo rows by CSR slot, with their scale exponents per
+// 256-feature segment). N tiles may run past the matrix: rows beyond it are zero (packed copies)
+// or read the last row (row-major banks), and are not stored.
 //
-// Each K step of 64 stages one NVFP4 block of every A row (three 12-byte direct-to-LDS loads per
-// row, lane i of a load landing at +16 i, so a row takes 48 bytes of LDS) and the B rows, in one
-// of kStages LDS stages: kStages - 1 steps are in flight while one is computed, which (at two
-// waves per SIMD and 64 MFMAs per wave per step) covers the latency of these scattered loads. Each wave issues a fixed number of loads per step,
-// so its count of outstanding loads is exact and the waits are partial.
-template <bool DOWN>
+// Each K step of 64 stages one NVFP4 block of every A row and the B rows in one of kStages LDS
+// stages: kStages - 1 steps are in flight while one is computed, which (at two waves per SIMD and
+// 64 MFMAs per wave per step) covers the latency of these loads. A row's block arrives by three
+// 12-byte direct-to-LDS loads (lane i of a load lands at +16 i, so a row takes 48 bytes of LDS),
+// or, with DENSE (gate/up from K-step-packed copies, whose K step is one contiguous run per bank),
+// by 16-byte loads of the run into rows 36 bytes apart, which frees the LDS for a fourth stage.
+// Each wave issues a fixed number of loads per step, so its count of outstanding loads is exact
+// and the waits are partial.
+template <bool DOWN, bool DENSE>
 __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ hin_hi,
     const uint16_t *__restrict__ hin_lo, const int32_t *__restrict__ offsets,
@@ -240,12 +245,15 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
     uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int32_t *__restrict__ hs,
     float *__restrict__ ypair) {
+    static_assert(!(DOWN && DENSE), "the down GEMM stages 48-byte rows");
     constexpr int kThreads = gemm_threads<DOWN>();
-    constexpr int kStages = gemm_stages<DOWN>();
+    constexpr int kStages = gemm_stages<DOWN, DENSE>();
     constexpr int kWaves = kThreads / 64;
     constexpr int kRows = kRowsW * kWaves;          // A rows per workgroup
-    constexpr int kAUnits = kRows * 3;              // 12-byte A loads per step (3 per row)
-    constexpr int kABytes = kAUnits * 16;           // 48 bytes per row
+    constexpr int kPitch = gemm_a_pitch<DOWN, DENSE>();   // LDS bytes per A row
+    // A load units per step: 12-byte pieces (3 per row), or 16-byte pieces of the two runs
+    constexpr int kAUnits = DENSE ? kRows * kBlockBytes / 16 : kRows * 3;
+    constexpr int kABytes = kRows * kPitch;
     constexpr int kNB = DOWN ? 2 : 1;               // B operands (h_hi, h_lo) or (x)
     constexpr int kBM2 = DOWN ? kBM / 2 : kBM;      // token columns per workgroup
     constexpr int kCols = kBM2 / 16;
@@ -307,8 +315,26 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     const int64_t astep = packed ? (int64_t)kKpackRows * kBlockBytes : kBlockBytes;
     const int64_t epack = kpack_expert_bytes(n_out, K);
     const uint8_t *asrc[kALoadsMax];
+    int adst[kALoadsMax];   // LDS offset of the wave's load i within a stage
+    if constexpr (DENSE) {
+        // units u < kAUnits / 2 are the gate run of the step, the rest the up run; a wave's
+        // last load past kAUnits repeats its first (same bytes to the same place), so that every
+        // wave issues kALoadsMax loads
+        // (a wave's 64 units never straddle the two runs: the source is a wave-uniform base
+        // plus 16 bytes per lane)
+        static_assert(kAUnits % 128 == 0 && kAUnits > (kALoadsMax - 1) * kThreads, "");
+#pragma unroll
+        for (int i = 0; i < kALoadsMax; i++) {
+            int u0 = (i * kWaves + wave) * 64;
+            if (u0 >= kAUnits) u0 = wave * 64;
+            adst[i] = u0 * 16;
+            const int64_t run = e * epack + (int64_t)nt * nblk * astep;
+            asrc[i] = u0 < kAUnits / 2 ? kp0 + run + 16 * u0 : kp1 + run + 16 * (u0 - kAUnits / 2);
+        }
+    } else
 #pragma unroll
     for (int i = 0; i < kALoadsMax; i++) {
+        adst[i] = (i * kWaves + wave) * 1024;
         const int u = min((i * kWaves + wave) * 64 + lane, kAUnits - 1);
         const int row = u / 3;
         const int half = DOWN ? kRows : kRows / 2;   // gate/up: gate rows, then the up rows
@@ -322,7 +348,7 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
             base = (second ? e1 : e0) + (int64_t)min(nt * half + r, n_out - 1) * rb;
         asrc[i] = base + 12 * (u % 3);
     }
-    static_assert(kAUnits == kALoadsMax * kThreads, "every lane issues kALoadsMax A loads");
+    static_assert(DENSE || kAUnits == kALoadsMax * kThreads, "every lane issues kALoadsMax A loads");
     // B: lane loads 16-byte units u = (i*kWaves + wave)*64 + lane of each operand, i.e. rows
     // 8 (i*kWaves + wave) .. +7 of the tile. Rows past the tile (r >= mt) load the row of the
     // tile's first pair (rowid clamps them; their columns are never stored), so every wave issues
@@ -342,11 +368,14 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     }
     // load li of step kb: the A loads, then the B loads of each operand
     constexpr int kLoads = kALoadsMax + kNB * kBUnits;
-    static_assert(kLoads <= 15, "waits below encode vmcnt in 4 bits");
+    static_assert((kStages - 2) * kLoads <= 15, "waits below encode vmcnt in 4 bits");
     auto issue_one = [&](int kb, int li) {
         uint8_t *st = smem + (kb % kStages) * kStageBytes;
         if (li < kALoadsMax) {
-            dma12(asrc[li] + kb * astep, st + (li * kWaves + wave) * 1024);
+            if constexpr (DENSE)
+                dma16(asrc[li] + (uint32_t)(16 * lane + kb * astep), st + adst[li]);
+            else
+                dma12(asrc[li] + kb * astep, st + adst[li]);
         } else {
             const int o = (li - kALoadsMax) / kBUnits, i = (li - kALoadsMax) % kBUnits;
             dma16(bsrc[o][i] + kb * 64, st + kABytes + o * kBBytesW + (i * kWaves + wave) * 1024);
@@ -373,8 +402,10 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     for (int f = 0; f < kAT; f++)
         arow[f] = DOWN ? kRowsW * wave + 16 * f
                        : (f >= 2 ? kRows / 2 : 0) + (kRowsW / 2) * wave + 16 * (f & 1);
-    // this lane's scale byte and code dwords within a staged block (12-byte loads, 16 apart)
-    const int c0_off = blk_lds(4 + 8 * q), c1_off = blk_lds(8 + 8 * q);
+    // this lane's scale byte and code dwords within a staged block (12-byte loads, 16 apart;
+    // with DENSE the block's 36 bytes in order)
+    const int c0_off = DENSE ? 4 + 8 * q : blk_lds(4 + 8 * q);
+    const int c1_off = DENSE ? 8 + 8 * q : blk_lds(8 + 8 * q);
 
     const int nsteps = nblk;
     for (int kb = 0; kb < min(kStages - 1, nsteps); kb++)
@@ -396,8 +427,11 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
                 }
             }
         }
-        // step kb landed: at most step kb + 1's loads still outstanding (s_waitcnt vmcnt(n))
-        if (kStages == 3 && kb + 1 < nsteps)
+        // step kb landed: at most the loads of the kStages - 2 steps after it still outstanding
+        // (s_waitcnt vmcnt(n))
+        if (kStages == 4 && kb + 2 < nsteps)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads));
+        else if (kStages >= 3 && kb + 1 < nsteps)
             __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);
         else
             __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -414,7 +448,7 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
             uint32_t sb[kAT], cw[kAT][2];
 #pragma unroll
             for (int f = 0; f < kAT; f++) {
-                const uint8_t *blk = st + (arow[f] + n) * 48;
+                const uint8_t *blk = st + (arow[f] + n) * kPitch;
                 sb[f] = blk[q];
                 cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
                 cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
@@ -572,15 +606,16 @@ PrefillWs carve(void *ws, int32_t T, int32_t P, int32_t E, int32_t H, int32_t F)
     return w;
 }
 
-template <bool DOWN>
-int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
+template <bool DOWN, bool DENSE>
+int launch_gemm_as(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
     constexpr int kThreads = gemm_threads<DOWN>();
     constexpr int kRows = kRowsW * (kThreads / 64);
-    // B: 128 rows x 1 operand or 64 x 2
-    constexpr size_t lds = gemm_stages<DOWN>() * (kRows * 48 + kBBytes);
+    // A rows at their pitch; B: 128 rows x 1 operand or 64 x 2
+    constexpr size_t lds =
+        gemm_stages<DOWN, DENSE>() * (kRows * gemm_a_pitch<DOWN, DENSE>() + kBBytes);
     static bool attr = false;
     if (!attr) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_kernel<DOWN>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_kernel<DOWN, DENSE>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return MOE_ELAUNCH;
         attr = true;
@@ -592,23 +627,30 @@ int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
     const int id = DOWN ? MOE_KERNEL_DN_PREFILL : MOE_KERNEL_GU_PREFILL;
     prof_start(id, s);
     if constexpr (DOWN)
-        hipLaunchKernelGGL((gemm_kernel<true>), dim3(grid), dim3(kThreads), lds, s, nullptr,
-                           w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt, n_ntiles,
-                           a.down.base, a.down.expert_stride, a.down.experts, nullptr, (int64_t)0,
-                           nullptr, a.down.kpack, nullptr, a.down.scale2, nullptr, a.k, a.F, a.F,
-                           a.H, nullptr, nullptr,
-                           nullptr, w.hs, w.ypair);
+        hipLaunchKernelGGL((gemm_kernel<true, false>), dim3(grid), dim3(kThreads), lds, s,
+                           nullptr, w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt,
+                           n_ntiles, a.down.base, a.down.expert_stride, a.down.experts, nullptr,
+                           (int64_t)0, nullptr, a.down.kpack, nullptr, a.down.scale2, nullptr,
+                           a.k, a.F, a.F, a.H, nullptr, nullptr, nullptr, w.hs, w.ypair);
     else
-        hipLaunchKernelGGL((gemm_kernel<false>), dim3(grid), dim3(kThreads), lds, s,
+        hipLaunchKernelGGL((gemm_kernel<false, DENSE>), dim3(grid), dim3(kThreads), lds, s,
                            (const uint16_t *)w.x16, nullptr, nullptr, a.offsets, a.pair_ids,
                            w.tiles, w.n_tiles, mt, n_ntiles, a.gate.base, a.gate.expert_stride,
                            a.gate.experts, a.up.base, a.up.expert_stride, a.up.experts,
                            a.gate.kpack, a.gate.kpack ? a.up.kpack : nullptr, a.gate.scale2,
-                           a.up.scale2, a.k, a.H,
-                           a.F, a.H,
-                           (const int32_t *)w.xs, w.h_hi, w.h_lo, w.hs, nullptr);
+                           a.up.scale2, a.k, a.H, a.F, a.H, (const int32_t *)w.xs, w.h_hi,
+                           w.h_lo, w.hs, nullptr);
     prof_stop(id, s);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
+}
+
+// gate/up from K-step-packed copies stages the dense rows (DENSE); everything else the 48-byte
+// rows
+template <bool DOWN>
+int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
+    if constexpr (!DOWN)
+        if (a.gate.kpack) return launch_gemm_as<false, true>(a, w, mt, s);
+    return launch_gemm_as<DOWN, false>(a, w, mt, s);
 }
 
 }  // namespace
