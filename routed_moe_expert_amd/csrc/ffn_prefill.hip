@@ -60,7 +60,9 @@ constexpr int kRowsW = 64;            // A rows per wave
 // workgroups per CU, two stages (one step in flight per workgroup, while the other workgroup of
 // the CU computes)
 template <bool DOWN> constexpr int gemm_threads() { return DOWN ? 256 : 512; }
-template <bool DOWN, bool DENSE> constexpr int gemm_stages() { return DOWN ? 2 : DENSE ? 4 : 3; }
+template <bool DOWN, bool DENSE> constexpr int gemm_stages() {
+    return DOWN ? (DENSE ? 3 : 2) : (DENSE ? 4 : 3);
+}
 template <bool DOWN, bool DENSE> constexpr int gemm_a_pitch() { return DENSE ? 36 : 48; }
 // h features per gate/up N tile (256): one h scale segment
 constexpr int kSegF = kRowsW / 2 * (gemm_threads<false>() / 64);
@@ -245,7 +247,6 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
     uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int32_t *__restrict__ hs,
     float *__restrict__ ypair) {
-    static_assert(!(DOWN && DENSE), "the down GEMM stages 48-byte rows");
     constexpr int kThreads = gemm_threads<DOWN>();
     constexpr int kStages = gemm_stages<DOWN, DENSE>();
     constexpr int kWaves = kThreads / 64;
@@ -263,7 +264,7 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     constexpr int kALoadsMax = (kAUnits + kThreads - 1) / kThreads;   // 3
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     __shared__ int rowid[kBM2];               // token (gate/up) or CSR slot (down) of each column
-    __shared__ int hsc[DOWN ? kBM2 : 1][DOWN ? kMaxSeg : 1];   // down: h scale exponents
+    __shared__ int16_t hsc[DOWN ? kBM2 : 1][DOWN ? kMaxSeg : 1];   // down: h scale exponents
 
     // M tile ti runs on XCD ti mod 8 (hardware workgroup b runs on XCD b mod 8), its N tiles (and
     // halves) in consecutive slots there: they share its token rows in that XCD's L2, and the
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     if constexpr (DOWN)
         for (int i = tid; i < kBM2 * nseg; i += kThreads) {
             const int r = i / nseg, g = i - r * nseg;
-            hsc[r][g] = hs[(int64_t)(q0 + (r < mt ? r : 0)) * nseg + g];
+            hsc[r][g] = (int16_t)hs[(int64_t)(q0 + (r < mt ? r : 0)) * nseg + g];
         }
     lds_barrier();
 
@@ -322,14 +323,16 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
         // wave issues kALoadsMax loads
         // (a wave's 64 units never straddle the two runs: the source is a wave-uniform base
         // plus 16 bytes per lane)
-        static_assert(kAUnits % 128 == 0 && kAUnits > (kALoadsMax - 1) * kThreads, "");
+        static_assert((DOWN ? kAUnits : kAUnits / 2) % 64 == 0 &&
+                      kAUnits > (kALoadsMax - 1) * kThreads, "");
 #pragma unroll
         for (int i = 0; i < kALoadsMax; i++) {
             int u0 = (i * kWaves + wave) * 64;
             if (u0 >= kAUnits) u0 = wave * 64;
             adst[i] = u0 * 16;
             const int64_t run = e * epack + (int64_t)nt * nblk * astep;
-            asrc[i] = u0 < kAUnits / 2 ? kp0 + run + 16 * u0 : kp1 + run + 16 * (u0 - kAUnits / 2);
+            asrc[i] = DOWN || u0 < kAUnits / 2 ? kp0 + run + 16 * u0
+                                               : kp1 + run + 16 * (u0 - kAUnits / 2);
         }
     } else
 #pragma unroll
@@ -348,7 +351,8 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
             base = (second ? e1 : e0) + (int64_t)min(nt * half + r, n_out - 1) * rb;
         asrc[i] = base + 12 * (u % 3);
     }
-    static_assert(DENSE || kAUnits == kALoadsMax * kThreads, "every lane issues kALoadsMax A loads");
+    static_assert(DENSE || kAUnits == kALoadsMax * kThreads,
+                  "every lane issues kALoadsMax A loads");
     // B: lane loads 16-byte units u = (i*kWaves + wave)*64 + lane of each operand, i.e. rows
     // 8 (i*kWaves + wave) .. +7 of the tile. Rows past the tile (r >= mt) load the row of the
     // tile's first pair (rowid clamps them; their columns are never stored), so every wave issues
@@ -627,7 +631,7 @@ int launch_gemm_as(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) 
     const int id = DOWN ? MOE_KERNEL_DN_PREFILL : MOE_KERNEL_GU_PREFILL;
     prof_start(id, s);
     if constexpr (DOWN)
-        hipLaunchKernelGGL((gemm_kernel<true, false>), dim3(grid), dim3(kThreads), lds, s,
+        hipLaunchKernelGGL((gemm_kernel<true, DENSE>), dim3(grid), dim3(kThreads), lds, s,
                            nullptr, w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt,
                            n_ntiles, a.down.base, a.down.expert_stride, a.down.experts, nullptr,
                            (int64_t)0, nullptr, a.down.kpack, nullptr, a.down.scale2, nullptr,
@@ -644,13 +648,13 @@ int launch_gemm_as(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) 
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-// gate/up from K-step-packed copies stages the dense rows (DENSE); everything else the 48-byte
+// from K-step-packed copies the GEMMs stage dense rows (DENSE), from row-major banks 48-byte
 // rows
 template <bool DOWN>
 int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
-    if constexpr (!DOWN)
-        if (a.gate.kpack) return launch_gemm_as<false, true>(a, w, mt, s);
-    return launch_gemm_as<DOWN, false>(a, w, mt, s);
+    const bool packed = (DOWN ? a.down.kpack : a.gate.kpack) != nullptr;
+    return packed ? launch_gemm_as<DOWN, true>(a, w, mt, s)
+                  : launch_gemm_as<DOWN, false>(a, w, mt, s);
 }
 
 }  // namespace
