@@ -55,18 +55,19 @@ constexpr int kBRow = 64 * 2;          // bytes of one token row per K step (64 
 constexpr int kBBytes = kBM * kBRow;   // 16 KB per B operand per stage (128 tokens)
 constexpr int kRowsW = 64;            // A rows per wave
 
-// gate/up: 8 waves, one workgroup per CU, three LDS stages (two K steps in flight), four from
-// K-step-packed copies (DENSE: rows staged at 36 bytes instead of 48); down: 4 waves, two
-// workgroups per CU, two stages (one step in flight per workgroup, while the other workgroup of
-// the CU computes)
-template <bool DOWN> constexpr int gemm_threads() { return DOWN ? 256 : 512; }
-template <bool DOWN, bool DENSE> constexpr int gemm_stages() {
-    return DOWN ? (DENSE ? 3 : 2) : (DENSE ? 4 : 3);
+// gate/up: 8 waves (256 features per N tile), one workgroup per CU, three LDS stages (two K
+// steps in flight), four from K-step-packed copies (DENSE: rows staged at 36 bytes instead of
+// 48); or, from packed copies when ff is not a multiple of 256, 4 waves (128 features) with two
+// workgroups per CU and three stages, so that no N tile is half empty (ff 640: 5 tiles of 128
+// instead of 3 of 256). Down: 4 waves, two workgroups per CU, two stages (one step in flight per
+// workgroup while the other workgroup of the CU computes), three from packed copies.
+template <bool DOWN, bool DENSE, int WAVES> constexpr int gemm_stages() {
+    return DOWN ? (DENSE ? 3 : 2) : (DENSE ? (WAVES == 8 ? 4 : 3) : 3);
 }
-template <bool DOWN, bool DENSE> constexpr int gemm_a_pitch() { return DENSE ? 36 : 48; }
-// h features per gate/up N tile (256): one h scale segment
-constexpr int kSegF = kRowsW / 2 * (gemm_threads<false>() / 64);
-constexpr int kMaxSeg = 32;           // h scale segments per pair: ff <= 32 * 256
+template <bool DENSE> constexpr int gemm_a_pitch() { return DENSE ? 36 : 48; }
+// h is scaled per (pair, segment): a segment is the features of one gate/up N tile
+template <int WAVES> constexpr int gate_up_segment() { return kRowsW / 2 * WAVES; }
+constexpr int kMaxSeg = 32;           // h scale segments per pair (ff <= 32 segments)
 
 typedef __attribute__((ext_vector_type(2))) int32_t i32x2_t;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
@@ -234,8 +235,8 @@ __device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ b_swz(
 // by 16-byte loads of the run into rows 36 bytes apart, which frees the LDS for a fourth stage.
 // Each wave issues a fixed number of loads per step, so its count of outstanding loads is exact
 // and the waits are partial.
-template <bool DOWN, bool DENSE>
-__global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kernel(
+template <bool DOWN, bool DENSE, int WAVES, int SEGF>
+__global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ hin_hi,
     const uint16_t *__restrict__ hin_lo, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ pair_ids, const i32x2_t *__restrict__ tiles,
@@ -247,11 +248,13 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     int32_t k, int32_t K, int32_t F, int32_t H, const int32_t *__restrict__ xs,
     uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int32_t *__restrict__ hs,
     float *__restrict__ ypair) {
-    constexpr int kThreads = gemm_threads<DOWN>();
-    constexpr int kStages = gemm_stages<DOWN, DENSE>();
+    constexpr int segf = SEGF;   // features per h scale segment
+    static_assert(!DOWN || WAVES == 4, "the down GEMM runs 4-wave workgroups");
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kStages = gemm_stages<DOWN, DENSE, WAVES>();
     constexpr int kWaves = kThreads / 64;
     constexpr int kRows = kRowsW * kWaves;          // A rows per workgroup
-    constexpr int kPitch = gemm_a_pitch<DOWN, DENSE>();   // LDS bytes per A row
+    constexpr int kPitch = gemm_a_pitch<DENSE>();   // LDS bytes per A row
     // A load units per step: 12-byte pieces (3 per row), or 16-byte pieces of the two runs
     constexpr int kAUnits = DENSE ? kRows * kBlockBytes / 16 : kRows * 3;
     constexpr int kABytes = kRows * kPitch;
@@ -298,7 +301,9 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
         const int c = r < mt ? r : 0;
         rowid[r] = DOWN ? q0 + c : pair_ids[q0 + c] / k;
     }
-    const int nseg = (F + kSegF - 1) / kSegF;   // h scale segments of a pair's row
+    // h scale segments of a pair's row (segf: features per segment, the gate/up N tile's width
+    // or half of it)
+    const int nseg = (F + segf - 1) / segf;
     if constexpr (DOWN)
         for (int i = tid; i < kBM2 * nseg; i += kThreads) {
             const int r = i / nseg, g = i - r * nseg;
@@ -308,31 +313,36 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
 
     // A: load i of a wave covers units (i*kWaves + wave)*64 + lane (unit j = u % 3 of row
     // u / 3); loads whose units all lie past kAUnits are skipped by the whole wave. From a
-    // K-step-packed copy (kp0, kp1) a bank's N tile is one row group, whose K step b is one run
-    // of kKpackRows 36-byte blocks (rows past the matrix are zero there); from the row-major bank
-    // each row's block sits at the row's start plus 36 b (rows past the matrix read the last).
-    static_assert((DOWN ? kRows : kRows / 2) == kKpackRows, "an N tile is one packed row group");
+    // K-step-packed copy (kp0, kp1) a bank's N tile lies in one row group, and its K step b is one
+    // run of 36-byte blocks (rows past the matrix are zero there); from the row-major bank each
+    // row's block sits at the row's start plus 36 b (rows past the matrix read the last).
+    constexpr int kTileRows = DOWN ? kRows : kRows / 2;   // rows of one bank in the N tile
+    static_assert(kKpackRows % kTileRows == 0 && (DENSE || kTileRows == kKpackRows),
+                  "an N tile lies in one packed row group");
+    constexpr int kRunUnits = kTileRows * kBlockBytes / 16;   // 16-byte units of one run
+    // the dense loads of a wave read one run (a wave-uniform base plus 16 bytes per lane) unless
+    // a wave's 64 units straddle the gate and up runs (4-wave gate/up: 288 units per run)
+    constexpr bool kUniform = DOWN || kRunUnits % 64 == 0;
     const bool packed = kp0 != nullptr;
     const int64_t astep = packed ? (int64_t)kKpackRows * kBlockBytes : kBlockBytes;
     const int64_t epack = kpack_expert_bytes(n_out, K);
     const uint8_t *asrc[kALoadsMax];
     int adst[kALoadsMax];   // LDS offset of the wave's load i within a stage
     if constexpr (DENSE) {
-        // units u < kAUnits / 2 are the gate run of the step, the rest the up run; a wave's
-        // last load past kAUnits repeats its first (same bytes to the same place), so that every
-        // wave issues kALoadsMax loads
-        // (a wave's 64 units never straddle the two runs: the source is a wave-uniform base
-        // plus 16 bytes per lane)
-        static_assert((DOWN ? kAUnits : kAUnits / 2) % 64 == 0 &&
-                      kAUnits > (kALoadsMax - 1) * kThreads, "");
+        // units u < kRunUnits are the gate run of the step (or down's one run), the rest the up
+        // run; a wave's last load past kAUnits repeats its first (same bytes to the same place),
+        // so that every wave issues kALoadsMax loads
+        static_assert(kAUnits > (kALoadsMax - 1) * kThreads, "");
+        const int64_t run = e * epack + (int64_t)(nt * kTileRows / kKpackRows) * nblk * astep +
+                            (int64_t)(nt * kTileRows % kKpackRows) * kBlockBytes;
 #pragma unroll
         for (int i = 0; i < kALoadsMax; i++) {
             int u0 = (i * kWaves + wave) * 64;
             if (u0 >= kAUnits) u0 = wave * 64;
             adst[i] = u0 * 16;
-            const int64_t run = e * epack + (int64_t)nt * nblk * astep;
-            asrc[i] = DOWN || u0 < kAUnits / 2 ? kp0 + run + 16 * u0
-                                               : kp1 + run + 16 * (u0 - kAUnits / 2);
+            const int u = kUniform ? u0 : u0 + lane;
+            asrc[i] = DOWN || u < kRunUnits ? kp0 + run + 16 * u
+                                            : kp1 + run + 16 * (u - kRunUnits);
         }
     } else
 #pragma unroll
@@ -376,8 +386,10 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
     auto issue_one = [&](int kb, int li) {
         uint8_t *st = smem + (kb % kStages) * kStageBytes;
         if (li < kALoadsMax) {
-            if constexpr (DENSE)
+            if constexpr (DENSE && kUniform)
                 dma16(asrc[li] + (uint32_t)(16 * lane + kb * astep), st + adst[li]);
+            else if constexpr (DENSE)
+                dma16(asrc[li] + kb * astep, st + adst[li]);
             else
                 dma12(asrc[li] + kb * astep, st + adst[li]);
         } else {
@@ -419,8 +431,9 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
         if constexpr (DOWN) {
             // a new h segment (its own scale exponent per column): rescale the running sums to
             // it, exactly (powers of two)
-            const int g = kb / (kSegF / kBlockWeights);
-            if (g > 0 && kb == g * (kSegF / kBlockWeights)) {
+            constexpr int seg_steps = segf / kBlockWeights;
+            const int g = kb / seg_steps;
+            if (g > 0 && kb == g * seg_steps) {
 #pragma unroll
                 for (int c = 0; c < kCols; c++) {
                     const int d = hsc[16 * c + n][g - 1] - hsc[16 * c + n][g];
@@ -540,17 +553,22 @@ __global__ __launch_bounds__(gemm_threads<DOWN>(), DOWN ? 2 : 1) void gemm_kerne
             if (q == 0) cmax[wave * kBM + 16 * c + n] = m;
         }
         lds_barrier();
+        // this wave's h segment: segf / 32 waves (32 features each) per segment, the tile's
+        // segments in order (segf is the tile's width, or half of it with the 8-wave kernel
+        // when ff is not a multiple of 256)
+        constexpr int wps = segf / (kRowsW / 2);
+        const int w0 = wave / wps * wps;
+        const int seg = nt * (kRows / 2 / segf) + wave / wps;
 #pragma unroll
         for (int c = 0; c < kCols; c++) {
             const int col = 16 * c + n;
             float m = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; w++) m = fmaxf(m, cmax[w * kBM + col]);
+            for (int w = w0; w < w0 + wps; w++) m = fmaxf(m, cmax[w * kBM + col]);
             int e = 0;
             if (m > 0.f) (void)frexpf(m, &e);   // m = f * 2^e, f in [0.5, 1)
             const int sh = m > 0.f ? e - 15 : 0;
-            if (col >= mt) continue;
-            if (wave == 0 && q == 0) hs[(int64_t)(q0 + col) * nseg + nt] = sh;
+            if (col >= mt || seg >= nseg) continue;   // (a half tile past ff: no segment)
+            if (wave == w0 && q == 0) hs[(int64_t)(q0 + col) * nseg + seg] = sh;
 #pragma unroll
             for (int t = 0; t < 2; t++) {
                 const int o = nt * (kRows / 2) + (kRowsW / 2) * wave + 16 * t + 4 * q;
@@ -587,7 +605,9 @@ struct PrefillWs {
 };
 
 int max_tiles(int32_t P, int32_t E) { return P / kBM + std::min(E, P) + 1; }
-int h_segments(int32_t F) { return (F + kSegF - 1) / kSegF; }
+int h_segments(int32_t F, int32_t segf) { return (F + segf - 1) / segf; }
+// the workspace holds the most segments any gate/up form can make
+constexpr int kMinSegF = gate_up_segment<4>();
 
 PrefillWs carve(void *ws, int32_t T, int32_t P, int32_t E, int32_t H, int32_t F) {
     uint8_t *b = static_cast<uint8_t *>(ws);
@@ -603,24 +623,25 @@ PrefillWs carve(void *ws, int32_t T, int32_t P, int32_t E, int32_t H, int32_t F)
     w.h_lo = reinterpret_cast<uint16_t *>(b);
     b += align256(2 * (size_t)P * F);
     w.hs = reinterpret_cast<int32_t *>(b);
-    b += align256(sizeof(int32_t) * (size_t)P * h_segments(F));
+    b += align256(sizeof(int32_t) * (size_t)P * h_segments(F, kMinSegF));
     w.ypair = reinterpret_cast<float *>(b);
     w.x16 = reinterpret_cast<uint16_t *>(b);   // 2 T H bytes <= 4 P H: P = T k >= T
     w.xs = reinterpret_cast<int32_t *>(b + align256(2 * (size_t)T * H));
     return w;
 }
 
-template <bool DOWN, bool DENSE>
+template <bool DOWN, bool DENSE, int WAVES, int SEGF>
 int launch_gemm_as(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
-    constexpr int kThreads = gemm_threads<DOWN>();
-    constexpr int kRows = kRowsW * (kThreads / 64);
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kRows = kRowsW * WAVES;
     // A rows at their pitch; B: 128 rows x 1 operand or 64 x 2
     constexpr size_t lds =
-        gemm_stages<DOWN, DENSE>() * (kRows * gemm_a_pitch<DOWN, DENSE>() + kBBytes);
+        gemm_stages<DOWN, DENSE, WAVES>() * (kRows * gemm_a_pitch<DENSE>() + kBBytes);
     static bool attr = false;
     if (!attr) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_kernel<DOWN, DENSE>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        const void *fn = reinterpret_cast<const void *>(gemm_kernel<DOWN, DENSE, WAVES, SEGF>);
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+            hipSuccess)
             return MOE_ELAUNCH;
         attr = true;
     }
@@ -631,13 +652,15 @@ int launch_gemm_as(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) 
     const int id = DOWN ? MOE_KERNEL_DN_PREFILL : MOE_KERNEL_GU_PREFILL;
     prof_start(id, s);
     if constexpr (DOWN)
-        hipLaunchKernelGGL((gemm_kernel<true, DENSE>), dim3(grid), dim3(kThreads), lds, s,
+        hipLaunchKernelGGL((gemm_kernel<true, DENSE, WAVES, SEGF>), dim3(grid), dim3(kThreads),
+                           lds, s,
                            nullptr, w.h_hi, w.h_lo, a.offsets, a.pair_ids, w.tiles, w.n_tiles, mt,
                            n_ntiles, a.down.base, a.down.expert_stride, a.down.experts, nullptr,
                            (int64_t)0, nullptr, a.down.kpack, nullptr, a.down.scale2, nullptr,
                            a.k, a.F, a.F, a.H, nullptr, nullptr, nullptr, w.hs, w.ypair);
     else
-        hipLaunchKernelGGL((gemm_kernel<false, DENSE>), dim3(grid), dim3(kThreads), lds, s,
+        hipLaunchKernelGGL((gemm_kernel<false, DENSE, WAVES, SEGF>), dim3(grid), dim3(kThreads),
+                           lds, s,
                            (const uint16_t *)w.x16, nullptr, nullptr, a.offsets, a.pair_ids,
                            w.tiles, w.n_tiles, mt, n_ntiles, a.gate.base, a.gate.expert_stride,
                            a.gate.experts, a.up.base, a.up.expert_stride, a.up.experts,
@@ -648,28 +671,32 @@ int launch_gemm_as(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) 
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ELAUNCH;
 }
 
-// from K-step-packed copies the GEMMs stage dense rows (DENSE), from row-major banks 48-byte
-// rows
-template <bool DOWN>
-int launch_gemm(const FfnArgs &a, const PrefillWs &w, int mt, hipStream_t s) {
-    const bool packed = (DOWN ? a.down.kpack : a.gate.kpack) != nullptr;
-    return packed ? launch_gemm_as<DOWN, true>(a, w, mt, s)
-                  : launch_gemm_as<DOWN, false>(a, w, mt, s);
+// h's scale segments: 128 features when ff is not a multiple of 256 (and 32 segments of 128
+// hold it), else 256. With 128, the gate/up GEMM from K-step-packed copies runs 4-wave
+// workgroups over 128 features, so that no N tile is half empty (ff 640: 5 tiles of 128 instead
+// of 3 of 256); from row-major banks it keeps 8 waves over 256 features with one scale per half,
+// so that y does not depend on the form. Measured on the skewed ff-640 routing at T = 4096 (one
+// box): gate/up 641 -> 498 us, the down GEMM, with twice the segment rescales, 522 -> 565 us.
+int h_segment(int32_t F) {
+    return F % gate_up_segment<8>() != 0 && h_segments(F, gate_up_segment<4>()) <= kMaxSeg
+               ? gate_up_segment<4>()
+               : gate_up_segment<8>();
 }
 
 }  // namespace
 
 size_t prefill_ws_bytes(int32_t T, int32_t k, int32_t E, int32_t H, int32_t F) {
     const int32_t P = T * k;
-    return align256(sizeof(int32_t) * (size_t)P) + align256(sizeof(i32x2_t) * (size_t)max_tiles(P, E)) +
+    return align256(sizeof(int32_t) * (size_t)P) +
+           align256(sizeof(i32x2_t) * (size_t)max_tiles(P, E)) +
            256 + 2 * align256(2 * (size_t)P * F) +
-           align256(sizeof(int32_t) * (size_t)P * h_segments(F)) +
+           align256(sizeof(int32_t) * (size_t)P * h_segments(F, kMinSegF)) +
            align256(sizeof(float) * (size_t)P * H);
 }
 
 int launch_prefill(const FfnArgs &a, hipStream_t s) {
     const int32_t P = a.T * a.k;
-    if (h_segments(a.F) > kMaxSeg) return MOE_ESHAPE;
+    if (h_segments(a.F, gate_up_segment<8>()) > kMaxSeg) return MOE_ESHAPE;
     const PrefillWs w = carve(a.ws, a.T, P, a.E, a.H, a.F);
     const int mt = max_tiles(P, a.E);
     const int sched_blocks = std::max(1, std::min(256, (P + kThreadsSched - 1) / kThreadsSched));
@@ -680,9 +707,23 @@ int launch_prefill(const FfnArgs &a, hipStream_t s) {
     if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
     hipLaunchKernelGGL(xcast_kernel, dim3(a.T), dim3(kCastThreads), 0, s, a.x, a.H, w.x16, w.xs);
     if (hipGetLastError() != hipSuccess) return MOE_ELAUNCH;
-    int st = launch_gemm<false>(a, w, mt, s);
-    if (st != MOE_OK) return st;
-    st = launch_gemm<true>(a, w, mt, s);
+    // from K-step-packed copies the GEMMs stage dense rows (DENSE), from row-major banks
+    // 48-byte rows
+    constexpr int kS4 = gate_up_segment<4>(), kS8 = gate_up_segment<8>();
+    int st;
+    if (h_segment(a.F) == kS4) {   // segments of 128 features
+        st = a.gate.kpack ? launch_gemm_as<false, true, 4, kS4>(a, w, mt, s)
+                          : launch_gemm_as<false, false, 8, kS4>(a, w, mt, s);
+        if (st != MOE_OK) return st;
+        st = a.down.kpack ? launch_gemm_as<true, true, 4, kS4>(a, w, mt, s)
+                          : launch_gemm_as<true, false, 4, kS4>(a, w, mt, s);
+    } else {
+        st = a.gate.kpack ? launch_gemm_as<false, true, 8, kS8>(a, w, mt, s)
+                          : launch_gemm_as<false, false, 8, kS8>(a, w, mt, s);
+        if (st != MOE_OK) return st;
+        st = a.down.kpack ? launch_gemm_as<true, true, 4, kS8>(a, w, mt, s)
+                          : launch_gemm_as<true, false, 4, kS8>(a, w, mt, s);
+    }
     if (st != MOE_OK) return st;
     return launch_combine(a.w, w.pos, a.offsets + a.E, w.ypair, a.T, a.k, a.H, a.y, s);
 }
