@@ -54,8 +54,8 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "36e2c02014666ade25c8ae6684a9234c88bd23602e24421723e829b4010e9bfb",
-        "fetch_kib": 54366.9, "write_kib": 168.6,
+        "sha256": "7612eacb942f087410766681827975388f1edd97a30ba0c8b8b99482be4a0533",
+        "fetch_kib": 54367.0, "write_kib": 168.0,
     },
 }
 
