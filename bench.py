@@ -54,7 +54,7 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "7612eacb942f087410766681827975388f1edd97a30ba0c8b8b99482be4a0533",
+        "sha256": "8c49c265595134c7025dd14ddb00cdba640c18a03dbfa68c916e22e7d6b43971",
         "fetch_kib": 54367.0, "write_kib": 168.0,
     },
 }

@@ -418,10 +418,15 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     for (int f = 0; f < kAT; f++)
         arow[f] = DOWN ? kRowsW * wave + 16 * f
                        : (f >= 2 ? kRows / 2 : 0) + (kRowsW / 2) * wave + 16 * (f & 1);
-    // this lane's scale byte and code dwords within a staged block (12-byte loads, 16 apart;
-    // with DENSE the block's 36 bytes in order)
-    const int c0_off = DENSE ? 4 + 8 * q : blk_lds(4 + 8 * q);
-    const int c1_off = DENSE ? 8 + 8 * q : blk_lds(8 + 8 * q);
+    // row-major stage: this lane's scale byte and code dwords within a staged block (12-byte
+    // loads, 16 apart)
+    const int c0_off = blk_lds(4 + 8 * q), c1_off = blk_lds(8 + 8 * q);
+    // DENSE: the stage holds packed runs in fragment order; the LDS offsets of this wave's two
+    // 32-row slices (gate/up: its gate rows' slice, then its up rows' in the up run; down: its 64
+    // rows' two slices)
+    int aslice[2];
+    aslice[0] = DOWN ? 2 * wave * kSliceBytes : wave * kSliceBytes;
+    aslice[1] = DOWN ? (2 * wave + 1) * kSliceBytes : kTileRows * kBlockBytes + wave * kSliceBytes;
 
     const int nsteps = nblk;
     for (int kb = 0; kb < min(kStages - 1, nsteps); kb++)
@@ -463,12 +468,40 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
         auto step = [&](auto full) {
             constexpr int kC = decltype(full)::value ? kCols : kCols / 2;
             uint32_t sb[kAT], cw[kAT][2];
+            if constexpr (DENSE) {
+                // per 32-row slice the scale bytes of its two tiles; the down GEMM also reads both
+                // tiles' codes here (8 bytes a lane), gate/up reads them per sub-step below (all of
+                // them held here spill). Measured fastest of the combinations of 1- or 2-byte
+                // scale reads and 4- or 8-byte code reads that stay in 256 registers.
+                static_assert(kAT == 4, "two slices of two tiles per wave");
 #pragma unroll
-            for (int f = 0; f < kAT; f++) {
-                const uint8_t *blk = st + (arow[f] + n) * kPitch;
-                sb[f] = blk[q];
-                cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
-                cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
+                for (int j = 0; j < 2; j++) {
+                    const uint8_t *sl = st + aslice[j];
+                    if constexpr (DOWN) {
+                        sb[2 * j] = sl[1024 + 2 * lane];
+                        sb[2 * j + 1] = sl[1025 + 2 * lane];
+#pragma unroll
+                        for (int t = 0; t < 2; t++) {
+                            const i32x2_t c =
+                                *reinterpret_cast<const i32x2_t *>(sl + 512 * t + 8 * lane);
+                            cw[2 * j + t][0] = (uint32_t)c[0];
+                            cw[2 * j + t][1] = (uint32_t)c[1];
+                        }
+                    } else {
+                        const uint32_t two =
+                            *reinterpret_cast<const uint16_t *>(sl + 1024 + 2 * lane);
+                        sb[2 * j] = two & 0xFF;
+                        sb[2 * j + 1] = two >> 8;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < kAT; f++) {
+                    const uint8_t *blk = st + (arow[f] + n) * kPitch;
+                    sb[f] = blk[q];
+                    cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
+                    cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
+                }
             }
 #pragma unroll
             for (int s2 = 0; s2 < 2; s2++) {
@@ -483,7 +516,13 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
                 // 16q + 8 s2 .. +7
 #pragma unroll
                 for (int f = 0; f < kAT; f++) {
-                    const f16x8_t af = dequant8_f16(cw[f][s2], sb[f]);
+                    uint32_t cv;
+                    if constexpr (DENSE && !DOWN)
+                        cv = *reinterpret_cast<const uint32_t *>(st + aslice[f >> 1] + 512 * (f & 1) +
+                                                                 8 * lane + 4 * s2);
+                    else
+                        cv = cw[f][s2];
+                    const f16x8_t af = dequant8_f16(cv, sb[f]);
 #pragma unroll
                     for (int o = 0; o < kNB; o++)
 #pragma unroll

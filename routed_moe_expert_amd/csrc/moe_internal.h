@@ -17,6 +17,7 @@ constexpr int kBlockBytes = 36;    // NVFP4: 4 UE4M3 scale bytes + 32 code bytes
 inline int64_t row_bytes(int64_t in_f) { return in_f / kBlockWeights * kBlockBytes; }
 // K-step-packed banks (moe_kpack): rows per group, and bytes per expert of the packed copy
 constexpr int kKpackRows = MOE_KPACK_ROWS;
+constexpr int kSliceBytes = 32 * kBlockBytes;   // one 32-row slice of a packed K-step run
 __host__ __device__ inline int64_t kpack_expert_bytes(int64_t out_f, int64_t in_f) {
     return (out_f + kKpackRows - 1) / kKpackRows * (in_f / kBlockWeights) * kKpackRows *
            kBlockBytes;
