@@ -90,6 +90,25 @@ class DeviceCase:
                 self.active.cpu().numpy(), self.counts.cpu().numpy())
 
 
+def kpack_ref(bank: np.ndarray, rows: int = moe.MOE_KPACK_ROWS) -> np.ndarray:
+    """The packed order from its definition: per expert, row group and K block one run; a run is
+    slices of 32 rows; a slice is, for each of its two 16-row tiles, lane l = n + 16 q's code
+    bytes 4 + 8 q .. 11 + 8 q of row n, then lane by lane the scale byte q of row n of tile 0 and
+    of tile 1. Rows past the bank are zero."""
+    E, O, rb = bank.shape
+    nb, G = rb // 36, -(-O // rows)
+    padded = np.zeros((E, G * rows, rb), np.uint8)
+    padded[:, :O] = bank
+    blk = padded.reshape(E, G, rows // 32, 2, 16, nb, 36)   # e, g, slice, tile, n, b, byte
+    blk = blk.transpose(0, 1, 5, 2, 3, 4, 6)                 # e, g, b, slice, tile, n, byte
+    codes = blk[..., 4:].reshape(*blk.shape[:6], 4, 8)       # ..., q, 8 bytes
+    codes = codes.transpose(0, 1, 2, 3, 4, 6, 5, 7)          # e, g, b, slice, tile, q, n, 8
+    scales = blk[..., :4].transpose(0, 1, 2, 3, 6, 5, 4)     # e, g, b, slice, q, n, tile
+    lead = codes.shape[:4]
+    out = np.concatenate([codes.reshape(*lead, 1024), scales.reshape(*lead, 128)], axis=-1)
+    return out.reshape(-1)
+
+
 def parity(y: np.ndarray, ref: np.ndarray):
     """(relative RMS error, max abs error / RMS(ref))."""
     ref = np.asarray(ref, dtype=np.float64)

@@ -3,6 +3,7 @@ workspaces, and rejects bad arguments on the host before anything is enqueued.""
 import os
 import re
 
+import numpy as np
 import pytest
 
 import routed_moe_expert_amd as moe
@@ -257,3 +258,33 @@ def test_auto_path_refuses_what_the_ffn_refuses():
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_auto_path(*args)
         assert ei.value.status == status
+
+
+def test_kpack_reference_order():
+    """The GPU tests' packed-copy reference, pinned byte by byte to the header's definition: in run
+    (e, g, b), slice s, byte 512 t + 8 l + j is code byte 4 + 8 (l >> 4) + j of row 32 s + 16 t +
+    (l & 15), byte 1024 + 2 l + t its scale byte l >> 4; rows past the bank are zero."""
+    from gpu_util import kpack_ref
+    rng = np.random.default_rng(7)
+    E, O, nb, R = 2, 300, 3, moe.MOE_KPACK_ROWS
+    bank = rng.integers(0, 256, size=(E, O, nb * 36), dtype=np.uint8)
+    out = kpack_ref(bank)
+    G = -(-O // R)
+    assert out.size == E * G * nb * R * 36 == moe.moe_kpack_bytes(E, O, nb * 64)
+    run = R * 36
+    for e in range(E):
+        for g in range(G):
+            for b in range(nb):
+                base = ((e * G + g) * nb + b) * run
+                for o in range(0, run, 7):   # every seventh byte of each run
+                    s, r = divmod(o, 1152)
+                    if r < 1024:
+                        t, rr = divmod(r, 512)
+                        l, j = divmod(rr, 8)
+                        byte = 4 + 8 * (l >> 4) + j
+                    else:
+                        l, t = divmod(r - 1024, 2)
+                        byte = l >> 4
+                    row = g * R + 32 * s + 16 * t + (l & 15)
+                    want = bank[e, row, b * 36 + byte] if row < O else 0
+                    assert out[base + o] == want, (e, g, b, o)

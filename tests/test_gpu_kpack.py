@@ -1,7 +1,8 @@
 """The K-step-packed weight copy (moe_kpack) and the GEMM path reading it. The copy must hold the
 row-major bank's 36-byte blocks in the order the header defines, bit for bit, and y computed from
-the packed copies must equal y from the row-major banks bit for bit: the GEMM stages the same
-bytes into the same LDS places, only from contiguous runs, and does the same arithmetic."""
+the packed copies must equal y from the row-major banks bit for bit: the GEMM feeds the same
+operands to the same MFMA lanes, only staged from contiguous runs in another order, and does the
+same arithmetic."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +10,7 @@ import torch
 import gen
 import oracle
 import routed_moe_expert_amd as moe
-from gpu_util import DeviceCase, assert_parity, to_dev
+from gpu_util import DeviceCase, assert_parity, kpack_ref, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -18,25 +19,6 @@ pytestmark = pytest.mark.gpu
 def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
-
-
-def _kpack_ref(bank: np.ndarray, rows: int = moe.MOE_KPACK_ROWS) -> np.ndarray:
-    """The packed order from its definition: per expert, row group and K block one run; a run is
-    slices of 32 rows; a slice is, for each of its two 16-row tiles, lane l = n + 16 q's code
-    bytes 4 + 8 q .. 11 + 8 q of row n, then lane by lane the scale byte q of row n of tile 0 and
-    of tile 1. Rows past the bank are zero."""
-    E, O, rb = bank.shape
-    nb, G = rb // 36, -(-O // rows)
-    padded = np.zeros((E, G * rows, rb), np.uint8)
-    padded[:, :O] = bank
-    blk = padded.reshape(E, G, rows // 32, 2, 16, nb, 36)   # e, g, slice, tile, n, b, byte
-    blk = blk.transpose(0, 1, 5, 2, 3, 4, 6)                 # e, g, b, slice, tile, n, byte
-    codes = blk[..., 4:].reshape(*blk.shape[:6], 4, 8)       # ..., q, 8 bytes
-    codes = codes.transpose(0, 1, 2, 3, 4, 6, 5, 7)          # e, g, b, slice, tile, q, n, 8
-    scales = blk[..., :4].transpose(0, 1, 2, 3, 6, 5, 4)     # e, g, b, slice, q, n, tile
-    lead = codes.shape[:4]
-    out = np.concatenate([codes.reshape(*lead, 1024), scales.reshape(*lead, 128)], axis=-1)
-    return out.reshape(-1)
 
 
 @pytest.mark.parametrize("E,O,K,table", [(3, 256, 512, False), (2, 640, 320, False),
@@ -49,9 +31,9 @@ def test_kpack_layout(E, O, K, table):
     if table:   # experts in reverse order through a pointer table
         tab = torch.tensor([dev.data_ptr() + (E - 1 - e) * O * rb for e in range(E)],
                            dtype=torch.int64, device="cuda")
-        src, ref = moe.bank(None, 0, experts=tab), _kpack_ref(bank[::-1])
+        src, ref = moe.bank(None, 0, experts=tab), kpack_ref(bank[::-1])
     else:
-        src, ref = moe.bank(dev, O * rb), _kpack_ref(bank)
+        src, ref = moe.bank(dev, O * rb), kpack_ref(bank)
     dst = torch.full((moe.moe_kpack_bytes(E, O, K),), 0xAB, dtype=torch.uint8, device="cuda")
     assert dst.numel() == ref.size
     moe.moe_kpack(src, E, O, K, dst)
