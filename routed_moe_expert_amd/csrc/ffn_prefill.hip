@@ -427,120 +427,131 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     int aslice[2];
     aslice[0] = DOWN ? 2 * wave * kSliceBytes : wave * kSliceBytes;
     aslice[1] = DOWN ? (2 * wave + 1) * kSliceBytes : kTileRows * kBlockBytes + wave * kSliceBytes;
+    // the codes of a K step read up front (down, 4-wave gate/up) or per sub-step (8-wave gate/up,
+    // 6% faster there; up front is 4-5% faster in the other two)
+    constexpr bool kCodesFirst = DOWN || WAVES == 4;
 
     const int nsteps = nblk;
     for (int kb = 0; kb < min(kStages - 1, nsteps); kb++)
 #pragma unroll
         for (int li = 0; li < kLoads; li++) issue_one(kb, li);
-    for (int kb = 0; kb < nsteps; kb++) {
-        if constexpr (DOWN) {
-            // a new h segment (its own scale exponent per column): rescale the running sums to
-            // it, exactly (powers of two)
-            constexpr int seg_steps = segf / kBlockWeights;
-            const int g = kb / seg_steps;
-            if (g > 0 && kb == g * seg_steps) {
+    // The K loop for tiles that reach the second half of the token columns, and one for tiles
+    // that do not (a uniform choice per workgroup, taken once: branching per K step made the
+    // compiler copy the gate/up accumulators between the two paths' registers, 64 moves a step)
+    auto k_loop = [&](auto full) {
+        for (int kb = 0; kb < nsteps; kb++) {
+            if constexpr (DOWN) {
+                // a new h segment (its own scale exponent per column): rescale the running sums to
+                // it, exactly (powers of two)
+                constexpr int seg_steps = segf / kBlockWeights;
+                const int g = kb / seg_steps;
+                if (g > 0 && kb == g * seg_steps) {
 #pragma unroll
-                for (int c = 0; c < kCols; c++) {
-                    const int d = hsc[16 * c + n][g - 1] - hsc[16 * c + n][g];
+                    for (int c = 0; c < kCols; c++) {
+                        const int d = hsc[16 * c + n][g - 1] - hsc[16 * c + n][g];
 #pragma unroll
-                    for (int f = 0; f < kAT0; f++)
+                        for (int f = 0; f < kAT0; f++)
 #pragma unroll
-                        for (int v = 0; v < 4; v++) acc[f][c][v] = ldexpf(acc[f][c][v], d);
-                }
-            }
-        }
-        // step kb landed: at most the loads of the kStages - 2 steps after it still outstanding
-        // (s_waitcnt vmcnt(n))
-        if (kStages == 4 && kb + 2 < nsteps)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads));
-        else if (kStages >= 3 && kb + 1 < nsteps)
-            __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);
-        else
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-        lds_barrier();   // visible to all; the stage of step kb-1 is free
-        // step kb + 2's loads go into that stage, one after each of the first kLoads of the
-        // step's eight MFMA groups (measured a few percent faster than issuing them together:
-        // a wave stalled on a full memory queue then still has MFMAs in flight)
-        const bool refill = kb + kStages - 1 < nsteps;
-        const uint8_t *st = smem + (kb % kStages) * kStageBytes;
-        // One K step in two sub-steps of 32. The second half of the token columns is read and
-        // multiplied only when the tile reaches it (one uniform branch).
-        auto step = [&](auto full) {
-            constexpr int kC = decltype(full)::value ? kCols : kCols / 2;
-            uint32_t sb[kAT], cw[kAT][2];
-            if constexpr (DENSE) {
-                // per 32-row slice the scale bytes of its two tiles; the down GEMM also reads both
-                // tiles' codes here (8 bytes a lane), gate/up reads them per sub-step below (all of
-                // them held here spill). Measured fastest of the combinations of 1- or 2-byte
-                // scale reads and 4- or 8-byte code reads that stay in 256 registers.
-                static_assert(kAT == 4, "two slices of two tiles per wave");
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    const uint8_t *sl = st + aslice[j];
-                    if constexpr (DOWN) {
-                        sb[2 * j] = sl[1024 + 2 * lane];
-                        sb[2 * j + 1] = sl[1025 + 2 * lane];
-#pragma unroll
-                        for (int t = 0; t < 2; t++) {
-                            const i32x2_t c =
-                                *reinterpret_cast<const i32x2_t *>(sl + 512 * t + 8 * lane);
-                            cw[2 * j + t][0] = (uint32_t)c[0];
-                            cw[2 * j + t][1] = (uint32_t)c[1];
-                        }
-                    } else {
-                        const uint32_t two =
-                            *reinterpret_cast<const uint16_t *>(sl + 1024 + 2 * lane);
-                        sb[2 * j] = two & 0xFF;
-                        sb[2 * j + 1] = two >> 8;
+                            for (int v = 0; v < 4; v++) acc[f][c][v] = ldexpf(acc[f][c][v], d);
                     }
                 }
-            } else {
-#pragma unroll
-                for (int f = 0; f < kAT; f++) {
-                    const uint8_t *blk = st + (arow[f] + n) * kPitch;
-                    sb[f] = blk[q];
-                    cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
-                    cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
-                }
             }
+            // step kb landed: at most the loads of the kStages - 2 steps after it still outstanding
+            // (s_waitcnt vmcnt(n))
+            if (kStages == 4 && kb + 2 < nsteps)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * kLoads));
+            else if (kStages >= 3 && kb + 1 < nsteps)
+                __builtin_amdgcn_s_waitcnt(0x0F70 | kLoads);
+            else
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            lds_barrier();   // visible to all; the stage of step kb-1 is free
+            // step kb + 2's loads go into that stage, one after each of the first kLoads of the
+            // step's eight MFMA groups (measured a few percent faster than issuing them together:
+            // a wave stalled on a full memory queue then still has MFMAs in flight)
+            const bool refill = kb + kStages - 1 < nsteps;
+            const uint8_t *st = smem + (kb % kStages) * kStageBytes;
+            // One K step in two sub-steps of 32. The second half of the token columns is read and
+            // multiplied only when the tile reaches it.
+            auto step = [&](auto full) {
+                constexpr int kC = decltype(full)::value ? kCols : kCols / 2;
+                uint32_t sb[kAT], cw[kAT][2];
+                if constexpr (DENSE) {
+                    // per 32-row slice the scale bytes of its two tiles, and (kCodesFirst) both
+                    // tiles' codes, 8 bytes a lane; otherwise the codes are read per sub-step
+                    // below. Measured fastest of the combinations of 1- or 2-byte scale reads and
+                    // 4- or 8-byte code reads.
+                    static_assert(kAT == 4, "two slices of two tiles per wave");
 #pragma unroll
-            for (int s2 = 0; s2 < 2; s2++) {
-                BT bfr[kNB][kC];
+                    for (int j = 0; j < 2; j++) {
+                        const uint8_t *sl = st + aslice[j];
+                        if constexpr (DOWN) {
+                            sb[2 * j] = sl[1024 + 2 * lane];
+                            sb[2 * j + 1] = sl[1025 + 2 * lane];
+                        } else {
+                            const uint32_t two =
+                                *reinterpret_cast<const uint16_t *>(sl + 1024 + 2 * lane);
+                            sb[2 * j] = two & 0xFF;
+                            sb[2 * j + 1] = two >> 8;
+                        }
+                        if constexpr (kCodesFirst)
 #pragma unroll
-                for (int o = 0; o < kNB; o++)
+                            for (int t = 0; t < 2; t++) {
+                                const i32x2_t c = *reinterpret_cast<const i32x2_t *>(
+                                    sl + 512 * t + 8 * lane);
+                                cw[2 * j + t][0] = (uint32_t)c[0];
+                                cw[2 * j + t][1] = (uint32_t)c[1];
+                            }
+                    }
+                } else {
 #pragma unroll
-                    for (int c = 0; c < kC; c++)
-                        bfr[o][c] = *reinterpret_cast<const BT *>(
-                            st + kABytes + o * kBBytesW + 16 * b_slot(16 * c + n, 2 * q + s2));
-                // A: lane (n, q) takes scale group q of its row: sub-step s2 = weights
-                // 16q + 8 s2 .. +7
+                    for (int f = 0; f < kAT; f++) {
+                        const uint8_t *blk = st + (arow[f] + n) * kPitch;
+                        sb[f] = blk[q];
+                        cw[f][0] = *reinterpret_cast<const uint32_t *>(blk + c0_off);
+                        cw[f][1] = *reinterpret_cast<const uint32_t *>(blk + c1_off);
+                    }
+                }
 #pragma unroll
-                for (int f = 0; f < kAT; f++) {
-                    uint32_t cv;
-                    if constexpr (DENSE && !DOWN)
-                        cv = *reinterpret_cast<const uint32_t *>(st + aslice[f >> 1] + 512 * (f & 1) +
-                                                                 8 * lane + 4 * s2);
-                    else
-                        cv = cw[f][s2];
-                    const f16x8_t af = dequant8_f16(cv, sb[f]);
+                for (int s2 = 0; s2 < 2; s2++) {
+                    BT bfr[kNB][kC];
 #pragma unroll
                     for (int o = 0; o < kNB; o++)
 #pragma unroll
-                        for (int c = 0; c < kC; c++) acc[f][c] = mfma_f16(af, bfr[o][c], acc[f][c]);
-                    const int li = s2 * kAT + f;   // MFMA group index, compile-time
-                    if (li < kLoads && refill) {
-                        __builtin_amdgcn_sched_barrier(0);   // keep the load at this point
-                        issue_one(kb + kStages - 1, li);
-                        __builtin_amdgcn_sched_barrier(0);
+                        for (int c = 0; c < kC; c++)
+                            bfr[o][c] = *reinterpret_cast<const BT *>(
+                                st + kABytes + o * kBBytesW + 16 * b_slot(16 * c + n, 2 * q + s2));
+                    // A: lane (n, q) takes scale group q of its row: sub-step s2 = weights
+                    // 16q + 8 s2 .. +7
+#pragma unroll
+                    for (int f = 0; f < kAT; f++) {
+                        uint32_t cv;
+                        if constexpr (DENSE && !kCodesFirst)
+                            cv = *reinterpret_cast<const uint32_t *>(
+                                st + aslice[f >> 1] + 512 * (f & 1) + 8 * lane + 4 * s2);
+                        else
+                            cv = cw[f][s2];
+                        const f16x8_t af = dequant8_f16(cv, sb[f]);
+#pragma unroll
+                        for (int o = 0; o < kNB; o++)
+#pragma unroll
+                            for (int c = 0; c < kC; c++)
+                                acc[f][c] = mfma_f16(af, bfr[o][c], acc[f][c]);
+                        const int li = s2 * kAT + f;   // MFMA group index, compile-time
+                        if (li < kLoads && refill) {
+                            __builtin_amdgcn_sched_barrier(0);   // keep the load at this point
+                            issue_one(kb + kStages - 1, li);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
                     }
                 }
-            }
-        };
-        if (ncol > kCols / 2)
-            step(std::true_type{});
-        else
-            step(std::false_type{});
-    }
+            };
+            step(full);
+        }
+    };
+    if (ncol > kCols / 2)
+        k_loop(std::true_type{});
+    else
+        k_loop(std::false_type{});
 
     // epilogue: lane holds rows 4q..4q+3 of each 16-row A tile for token column 16c + n
     if (DOWN) {
@@ -553,8 +564,9 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
 #pragma unroll
                 for (int f = 0; f < kAT; f++) {
                     const int r = nt * kRows + arow[f] + 4 * q;
-                    const f32x4_t y4 = {ldexpf(acc[f][c][0], sl) * sc0, ldexpf(acc[f][c][1], sl) * sc0,
-                                        ldexpf(acc[f][c][2], sl) * sc0, ldexpf(acc[f][c][3], sl) * sc0};
+                    const f32x4_t y4 = {
+                        ldexpf(acc[f][c][0], sl) * sc0, ldexpf(acc[f][c][1], sl) * sc0,
+                        ldexpf(acc[f][c][2], sl) * sc0, ldexpf(acc[f][c][3], sl) * sc0};
                     if (r < H) *reinterpret_cast<f32x4_t *>(ypair + prow + r) = y4;
                 }
             }
