@@ -435,10 +435,10 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     for (int kb = 0; kb < min(kStages - 1, nsteps); kb++)
 #pragma unroll
         for (int li = 0; li < kLoads; li++) issue_one(kb, li);
-    // The K loop for tiles that reach the second half of the token columns, and one for tiles
-    // that do not (a uniform choice per workgroup, taken once: branching per K step made the
-    // compiler copy the gate/up accumulators between the two paths' registers, 64 moves a step)
-    auto k_loop = [&](auto full) {
+    // The K loop for each count of token column tiles a tile can need (gate/up: 2, 4, 6 or 8 of
+    // 16 columns; down: 2 or 4), one entered per workgroup: a choice per K step made the compiler
+    // copy the gate/up accumulators between the cases' registers, 64 moves a step
+    auto k_loop = [&](auto cols) {
         for (int kb = 0; kb < nsteps; kb++) {
             if constexpr (DOWN) {
                 // a new h segment (its own scale exponent per column): rescale the running sums to
@@ -470,10 +470,9 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
             // a wave stalled on a full memory queue then still has MFMAs in flight)
             const bool refill = kb + kStages - 1 < nsteps;
             const uint8_t *st = smem + (kb % kStages) * kStageBytes;
-            // One K step in two sub-steps of 32. The second half of the token columns is read and
-            // multiplied only when the tile reaches it.
-            auto step = [&](auto full) {
-                constexpr int kC = decltype(full)::value ? kCols : kCols / 2;
+            // One K step in two sub-steps of 32, over the column tiles the tile reaches.
+            auto step = [&](auto cols) {
+                constexpr int kC = decltype(cols)::value;
                 uint32_t sb[kAT], cw[kAT][2];
                 if constexpr (DENSE) {
                     // per 32-row slice the scale bytes of its two tiles, and (kCodesFirst) both
@@ -545,13 +544,18 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
                     }
                 }
             };
-            step(full);
+            step(cols);
         }
     };
-    if (ncol > kCols / 2)
-        k_loop(std::true_type{});
+    using std::integral_constant;
+    if (ncol > 3 * kCols / 4)
+        k_loop(integral_constant<int, kCols>{});
+    else if (ncol > kCols / 2 && kCols % 4 == 0)
+        k_loop(integral_constant<int, 3 * kCols / 4>{});
+    else if (ncol > kCols / 4 || kCols % 4 != 0)
+        k_loop(integral_constant<int, kCols / 2>{});
     else
-        k_loop(std::false_type{});
+        k_loop(integral_constant<int, kCols / 4>{});
 
     // epilogue: lane holds rows 4q..4q+3 of each 16-row A tile for token column 16c + n
     if (DOWN) {
