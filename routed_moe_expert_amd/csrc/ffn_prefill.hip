@@ -380,11 +380,12 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
             bsrc[0][i] = x + off;
         }
     }
-    // load li of step kb: the A loads, then the B loads of each operand
+    // load li of step kb into the stage at LDS offset soff (that of step kb mod kStages): the A
+    // loads, then the B loads of each operand
     constexpr int kLoads = kALoadsMax + kNB * kBUnits;
     static_assert((kStages - 2) * kLoads <= 15, "waits below encode vmcnt in 4 bits");
-    auto issue_one = [&](int kb, int li) {
-        uint8_t *st = smem + (kb % kStages) * kStageBytes;
+    auto issue_one = [&](int kb, int li, int soff) {
+        uint8_t *st = smem + soff;
         if (li < kALoadsMax) {
             if constexpr (DENSE && kUniform)
                 dma16(asrc[li] + (uint32_t)(16 * lane + kb * astep), st + adst[li]);
@@ -434,11 +435,14 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     const int nsteps = nblk;
     for (int kb = 0; kb < min(kStages - 1, nsteps); kb++)
 #pragma unroll
-        for (int li = 0; li < kLoads; li++) issue_one(kb, li);
+        for (int li = 0; li < kLoads; li++) issue_one(kb, li, kb * kStageBytes);
     // The K loop for each count of token column tiles a tile can need (gate/up: 2, 4, 6 or 8 of
     // 16 columns; down: 2 or 4), one entered per workgroup: a choice per K step made the compiler
     // copy the gate/up accumulators between the cases' registers, 64 moves a step
     auto k_loop = [&](auto cols) {
+        // LDS offset of step kb's stage, stepped without a division (with kb % kStages the
+        // compiler spent two VALU adds per LDS address and step)
+        int cur = 0;
         for (int kb = 0; kb < nsteps; kb++) {
             if constexpr (DOWN) {
                 // a new h segment (its own scale exponent per column): rescale the running sums to
@@ -469,7 +473,9 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
             // step's eight MFMA groups (measured a few percent faster than issuing them together:
             // a wave stalled on a full memory queue then still has MFMAs in flight)
             const bool refill = kb + kStages - 1 < nsteps;
-            const uint8_t *st = smem + (kb % kStages) * kStageBytes;
+            const uint8_t *st = smem + cur;
+            // the stage of step kb + kStages - 1 (that of step kb - 1)
+            const int prev = cur == 0 ? (kStages - 1) * kStageBytes : cur - kStageBytes;
             // One K step in two sub-steps of 32, over the column tiles the tile reaches.
             auto step = [&](auto cols) {
                 constexpr int kC = decltype(cols)::value;
@@ -538,13 +544,14 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
                         const int li = s2 * kAT + f;   // MFMA group index, compile-time
                         if (li < kLoads && refill) {
                             __builtin_amdgcn_sched_barrier(0);   // keep the load at this point
-                            issue_one(kb + kStages - 1, li);
+                            issue_one(kb + kStages - 1, li, prev);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
                 }
             };
             step(cols);
+            cur = cur == (kStages - 1) * kStageBytes ? 0 : cur + kStageBytes;
         }
     };
     using std::integral_constant;
