@@ -54,7 +54,7 @@ TRAFFIC = {
     ("gu_decode_kernel", "verify_chunk", 6, 60): {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
-        "sha256": "8c49c265595134c7025dd14ddb00cdba640c18a03dbfa68c916e22e7d6b43971",
+        "sha256": "e29566e8f962d11c3ad900dba8522c109ae073e68dece055e66e21665f6ea2e4",
         "fetch_kib": 54366.9, "write_kib": 169.9,
     },
 }
