@@ -67,7 +67,7 @@ enum {
 #define MOE_MAX_HIDDEN 16384       /* H limit */
 #define MOE_MAX_FF 8192            /* F limit */
 #define MOE_MAX_ROUTER_K 64        /* k limit of moe_router_topk (one slot per wavefront lane) */
-#define MOE_AUTO_PAIRS_PER_EXPERT 24   /* MOE_PATH_AUTO's decode limit: routed pairs per expert */
+#define MOE_AUTO_PAIRS_PER_EXPERT 16   /* MOE_PATH_AUTO's decode limit: routed pairs per expert */
 
 /*
  * One weight bank: expert e's rows start at base + e*expert_stride (bytes, device).
@@ -165,8 +165,8 @@ int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, i
  * split the work the same way, a bandwidth-bound path for a few tokens per expert and grouped GEMMs
  * for prefill (moe_sk_repro.rs, its decode and prefill regimes); the pairs-per-expert limit is near
  * where the two paths measured equal on one MI355X, the GEMMs reading K-step-packed copies (about
- * 21 and 24 pairs per expert on the skewed hidden-4096 routings, 33 on the uniform E256 one; the
- * decode kernels stream an expert's weights once per run of 16 pairs).
+ * 12 and 17 pairs per expert on the skewed hidden-4096 routings at ff 1280 and 640, 18 on the
+ * uniform E256 one; the decode kernels stream an expert's weights once per run of 16 pairs).
  * Returns the path, or minus an MOE_E* code for sizes moe_ffn_nvfp4 would refuse (-MOE_EINVAL,
  * -MOE_ESHAPE).
  */

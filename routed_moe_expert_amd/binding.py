@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe_nvfp4.so")
 
 MOE_OK, MOE_EINVAL, MOE_EWS, MOE_ESHAPE, MOE_ELAUNCH = 0, 1, 2, 3, 4
 MOE_PATH_AUTO, MOE_PATH_DECODE, MOE_PATH_PREFILL = 0, 1, 2
-MOE_AUTO_PAIRS_PER_EXPERT = 24
+MOE_AUTO_PAIRS_PER_EXPERT = 16
 MOE_KPACK_ROWS = 256
 (MOE_KERNEL_NONE, MOE_KERNEL_BUCKET, MOE_KERNEL_GU_DECODE, MOE_KERNEL_DN_DECODE, MOE_KERNEL_COMBINE,
  MOE_KERNEL_SCHEDULE, MOE_KERNEL_GU_PREFILL, MOE_KERNEL_DN_PREFILL, MOE_KERNEL_ROUTER) = range(9)

@@ -237,10 +237,11 @@ def test_layer_workspace_covers_the_two_calls():
     (128, 10, 256, 2560, 640, moe.MOE_PATH_DECODE),    # E256 plateau, 5 pairs per expert
     (128, 1, 1, 2560, 320, moe.MOE_PATH_DECODE),       # shared expert: 128 tokens, one expert
     (512, 8, 288, 4096, 640, moe.MOE_PATH_DECODE),     # skewed prefill T=512: 14.2 pairs/expert
-    (864, 8, 288, 4096, 640, moe.MOE_PATH_DECODE),     # 24 pairs per expert: the limit
-    (865, 8, 288, 4096, 640, moe.MOE_PATH_PREFILL),    # one token past it
+    (576, 8, 288, 4096, 640, moe.MOE_PATH_DECODE),     # 16 pairs per expert: the limit
+    (577, 8, 288, 4096, 640, moe.MOE_PATH_PREFILL),    # one token past it
     (2048, 8, 288, 4096, 640, moe.MOE_PATH_PREFILL),
-    (614, 10, 256, 2560, 640, moe.MOE_PATH_DECODE),    # E256 at 24 pairs per expert
+    (409, 10, 256, 2560, 640, moe.MOE_PATH_DECODE),    # E256 at 16 pairs per expert
+    (410, 10, 256, 2560, 640, moe.MOE_PATH_PREFILL),   # one token past it
     (768, 10, 256, 2560, 640, moe.MOE_PATH_PREFILL),   # E256 at 30 pairs per expert
     (4096, 8, 288, 4096, 1280, moe.MOE_PATH_PREFILL),  # full-width prefill
     (129, 1, 1, 2560, 320, moe.MOE_PATH_PREFILL),      # past 128 tokens, 129 pairs per expert
