@@ -215,6 +215,28 @@ def test_prefill_small(seed, T, k, E, H, F, scales, frac, base, fused):
     assert_parity(y, oracle.ffn_union(case), "prefill_small")
 
 
+# pairs per expert on each side of the GEMMs' column steps: gate/up runs 32, 64, 96 or 128 token
+# columns of a 128-pair M tile, down 16, 32, 48 or 64 of a 64-pair half tile
+COLUMN_COUNTS = [1, 15, 16, 17, 32, 33, 48, 49, 64, 65, 96, 97, 127, 128, 129, 192, 255]
+
+
+@pytest.mark.parametrize("F", [320, 512])
+def test_prefill_column_cases(F):
+    """Experts whose pair counts sit at and beside every column step of both GEMMs, every token
+    compared, on both gate/up kernels (ff 320: 128-feature N tiles, 512: 256-feature ones), from
+    the row-major banks and, bit for bit the same, from the K-step-packed copies."""
+    E, T = len(COLUMN_COUNTS), sum(COLUMN_COUNTS)
+    _print_case("prefill_column_cases", T=T, E=E, F=F)
+    case = gen.make_random_case(61, T, 1, E, 512, F)
+    perm = np.random.default_rng(61).permutation(T)
+    case["ids"] = np.repeat(np.arange(E, dtype=np.int32), COLUMN_COUNTS)[perm].reshape(T, 1)
+    dc = DeviceCase(case)
+    y = dc.run(moe.MOE_PATH_PREFILL)
+    assert_parity(y, oracle.ffn_union(case), f"column cases ff {F}")
+    dc.use_kpack(True)
+    assert np.array_equal(dc.run(moe.MOE_PATH_PREFILL), y), "packed copies differ"
+
+
 @pytest.mark.parametrize("name,T", [("skewed_prefill", 512), ("skewed_prefill", 2048),
                                     ("skewed_prefill", 4096), ("full_prefill", 4096)])
 def test_prefill_workloads(name, T):
