@@ -431,6 +431,7 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     // the codes of a K step read up front (down, 4-wave gate/up) or per sub-step (8-wave gate/up,
     // 6% faster there; up front is 4-5% faster in the other two)
     constexpr bool kCodesFirst = DOWN || WAVES == 4;
+    constexpr bool kLoadsFirst = DOWN;   // where a step's refill loads go (below)
 
     const int nsteps = nblk;
     for (int kb = 0; kb < min(kStages - 1, nsteps); kb++)
@@ -469,9 +470,10 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
             else
                 __builtin_amdgcn_s_waitcnt(0x0F70);
             lds_barrier();   // visible to all; the stage of step kb-1 is free
-            // step kb + 2's loads go into that stage, one after each of the first kLoads of the
-            // step's eight MFMA groups (measured a few percent faster than issuing them together:
-            // a wave stalled on a full memory queue then still has MFMAs in flight)
+            // step kb + kStages - 1's loads go into that stage: in gate/up one after each of the
+            // first kLoads of the step's eight MFMA groups (a wave stalled on a full memory queue
+            // then still has MFMAs in flight; measured 3% faster than issuing them together), in
+            // down all of them before the step's MFMAs (measured 1-3% faster there)
             const bool refill = kb + kStages - 1 < nsteps;
             const uint8_t *st = smem + cur;
             // the stage of step kb + kStages - 1 (that of step kb - 1)
@@ -542,7 +544,7 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
                             for (int c = 0; c < kC; c++)
                                 acc[f][c] = mfma_f16(af, bfr[o][c], acc[f][c]);
                         const int li = s2 * kAT + f;   // MFMA group index, compile-time
-                        if (li < kLoads && refill) {
+                        if (!kLoadsFirst && li < kLoads && refill) {
                             __builtin_amdgcn_sched_barrier(0);   // keep the load at this point
                             issue_one(kb + kStages - 1, li, prev);
                             __builtin_amdgcn_sched_barrier(0);
@@ -550,6 +552,9 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
                     }
                 }
             };
+            if (kLoadsFirst && refill)
+#pragma unroll
+                for (int li = 0; li < kLoads; li++) issue_one(kb + kStages - 1, li, prev);
             step(cols);
             cur = cur == (kStages - 1) * kStageBytes ? 0 : cur + kStageBytes;
         }
