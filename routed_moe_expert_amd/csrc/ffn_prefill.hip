@@ -8,7 +8,8 @@
 //             device CSR (no host read-back); also the pair -> CSR slot map for the combine.
 //   xcast:    x to f16 per token row, scaled by a power of two (exact), for the gate/up GEMM.
 //   gemm:     one workgroup per (N tile, M tile); gate/up: 8 waves, 512 weight rows, one
-//             workgroup per CU; down: 4 waves, 256 rows, two workgroups per CU, which
+//             workgroup per CU (or 4 waves, 256 rows, two per CU where ff is not a multiple of
+//             256); down: 4 waves, 256 rows, two workgroups per CU, which
 //             fall out of step with each other, so that one computes while the other waits
 //             at its barrier or for its loads (down GEMM 5-7% faster than one 8-wave
 //             workgroup with three stages). The A operand is the
@@ -17,21 +18,23 @@
 //             since every E2M1 x UE4M3 product is an f16 value. The B operand is the M tile's
 //             token rows (x gathered by token for gate/up, the h_hi / h_lo rows of the CSR
 //             slots for down) with an XOR swizzle of their 16-byte parts so that fragment reads
-//             are free of bank conflicts. Gate/up keeps two K steps in flight (three LDS
-//             stages), each down workgroup one (two stages).
+//             are free of bank conflicts. From row-major banks gate/up keeps two K steps in
+//             flight (three LDS stages), each down workgroup one (two stages); from K-step-packed
+//             copies (36 bytes a row in LDS) one more each.
 //             MFMA 16x16x32 with fp32 accumulation; a wave owns 64 rows x 128
 //             tokens (gate/up) or 64 rows x 64 tokens (down, whose workgroups take half an M
-//             tile so that h_hi and h_lo fit the stages) and skips the second half of its token
-//             columns when the tile does not reach them. Each weight row is decoded by one wave
-//             only, and each B fragment read from LDS feeds four MFMAs: per K step the LDS
-//             reads of a workgroup (the B tile once per wave) stay below what the matrix cores
-//             take to consume them, which at 32 rows per wave they did not.
+//             tile so that h_hi and h_lo fit the stages) and runs only the steps of 32
+//             (gate/up) or 16 (down) token columns that the tile reaches. Each weight row is
+//             decoded by one wave only, and each B fragment read from LDS feeds four MFMAs: per
+//             K step the LDS reads of a workgroup (the B tile once per wave) stay below what
+//             the matrix cores take to consume them, which at 32 rows per wave they did not.
 //             Both multiply in f16 (v_mfma_f32_16x16x32_f16: weights decoded to f16 at half
 //             the VALU of bf16, which has no packed multiply). Gate/up takes x cast per token
 //             (exact, power-of-two scaled) and unscales its sums per token column.
-//             Gate/up: rows are 256 gate rows and the matching up rows; the epilogue forms
+//             Gate/up: rows are the tile's gate rows and the matching up rows; the epilogue forms
 //             h = SiLU(g) * u and stores it as an f16 pair, h = 2^s (h_hi + h_lo) with one
-//             power-of-two s per (pair, the tile's 256 features) bringing their largest |h| into
+//             power-of-two s per (pair, h segment of 256 features, or 128 where ff is not a
+//             multiple of 256) bringing their largest |h| into
 //             [2^14, 2^15) (about 22 significant bits). Down: the same tile times h_hi plus times
 //             h_lo, K segment by K segment: at each new segment the running fp32 sums are
 //             rescaled to its exponent (exact), and the epilogue applies the last one; into the
@@ -220,21 +223,22 @@ __host__ __device__ constexpr int blk_lds(int b) { return 16 * (b / 12) + b % 12
 __device__ __forceinline__ int b_swz(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int b_slot(int r, int p) { return r * 8 + (p ^ b_swz(r)); }
 
-// One workgroup: N tile nt of M tile ti (gate/up: 512 weight rows, all of the tile's up to 128
-// pairs; down: 256 rows, the half hf of 64 pairs). DOWN = false: gate/up (A rows are 256 gate
-// rows then the matching up rows; K = H; B = x rows by token); DOWN = true: down (A rows are 256
-// rows of W_d; K = F; B = h_hi and h_lo rows by CSR slot, with their scale exponents per
-// 256-feature segment). N tiles may run past the matrix: rows beyond it are zero (packed copies)
-// or read the last row (row-major banks), and are not stored.
+// One workgroup: N tile nt of M tile ti (gate/up: 64 weight rows per wave, half gate rows and
+// half the matching up rows, over all of the tile's up to 128 pairs; down: 256 rows, the half hf
+// of 64 pairs). DOWN = false: gate/up (A rows are the tile's gate rows then its up rows; K = H;
+// B = x rows by token); DOWN = true: down (A rows are 256 rows of W_d; K = F; B = h_hi and h_lo
+// rows by CSR slot, with their scale exponents per SEGF-feature segment). N tiles may run past
+// the matrix: rows beyond it are zero (packed copies) or read the last row (row-major banks), and
+// are not stored.
 //
 // Each K step of 64 stages one NVFP4 block of every A row and the B rows in one of kStages LDS
 // stages: kStages - 1 steps are in flight while one is computed, which (at two waves per SIMD and
-// 64 MFMAs per wave per step) covers the latency of these loads. A row's block arrives by three
-// 12-byte direct-to-LDS loads (lane i of a load lands at +16 i, so a row takes 48 bytes of LDS),
-// or, with DENSE (gate/up from K-step-packed copies, whose K step is one contiguous run per bank),
-// by 16-byte loads of the run into rows 36 bytes apart, which frees the LDS for a fourth stage.
-// Each wave issues a fixed number of loads per step, so its count of outstanding loads is exact
-// and the waits are partial.
+// up to 64 MFMAs per wave per step) covers the latency of these loads. A row's block arrives by
+// three 12-byte direct-to-LDS loads (lane i of a load lands at +16 i, so a row takes 48 bytes of
+// LDS), or, with DENSE (from K-step-packed copies, whose K step is one contiguous run per bank),
+// by 16-byte loads of the run as it is: 36 bytes a row, in the order the waves read their A
+// fragments, which frees LDS for another stage. Each wave issues a fixed number of loads per
+// step, so its count of outstanding loads is exact and the waits are partial.
 template <bool DOWN, bool DENSE, int WAVES, int SEGF>
 __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ hin_hi,
@@ -323,8 +327,8 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
     // the dense loads of a wave read one run (a wave-uniform base plus 16 bytes per lane) unless
     // a wave's 64 units straddle the gate and up runs (4-wave gate/up: 288 units per run)
     constexpr bool kUniform = DOWN || kRunUnits % 64 == 0;
-    const bool packed = kp0 != nullptr;
-    const int64_t astep = packed ? (int64_t)kKpackRows * kBlockBytes : kBlockBytes;
+    // DENSE reads K-step-packed copies (kp0, kp1), the other form the row-major banks
+    const int64_t astep = DENSE ? (int64_t)kKpackRows * kBlockBytes : kBlockBytes;
     const int64_t epack = kpack_expert_bytes(n_out, K);
     const uint8_t *asrc[kALoadsMax];
     int adst[kALoadsMax];   // LDS offset of the wave's load i within a stage
@@ -353,12 +357,7 @@ __global__ __launch_bounds__(WAVES * 64, WAVES == 8 ? 1 : 2) void gemm_kernel(
         const int half = DOWN ? kRows : kRows / 2;   // gate/up: gate rows, then the up rows
         const bool second = !DOWN && row >= half;
         const int r = second ? row - half : row;     // row within the bank's N tile
-        const uint8_t *base;
-        if (packed)
-            base = (second ? kp1 : kp0) + e * epack + (int64_t)nt * nblk * astep +
-                   (int64_t)r * kBlockBytes;
-        else
-            base = (second ? e1 : e0) + (int64_t)min(nt * half + r, n_out - 1) * rb;
+        const uint8_t *base = (second ? e1 : e0) + (int64_t)min(nt * half + r, n_out - 1) * rb;
         asrc[i] = base + 12 * (u % 3);
     }
     static_assert(DENSE || kAUnits == kALoadsMax * kThreads,
