@@ -231,20 +231,35 @@ __global__ __launch_bounds__(kThreads) void bucket_scan_kernel(
     const int NB = E + 1;
     int32_t *tot = smem;
     int *wsum = tot + NB;
+    // the chunks' counts are read kBatch at a time with independent loads (one round trip per
+    // batch; read, write and read again one chunk after another, they took a round trip each)
+    constexpr int kBatch = 16;
     for (int key = threadIdx.x; key < NB; key += kThreads) {
         int run = 0;
-        for (int c = 0; c < n_chunks; c++) {
-            const int v = hist[(int64_t)c * NB + key];
-            hist[(int64_t)c * NB + key] = run;
-            run += v;
+        for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+#pragma unroll
+            for (int u = 0; u < kBatch; u++)
+                run += c0 + u < n_chunks ? hist[(int64_t)(c0 + u) * NB + key] : 0;
         }
         tot[key] = run;
     }
     lds_barrier();
-    write_csr_head(tot, E, wsum, offsets, active, counts);
+    write_csr_head(tot, E, wsum, offsets, active, counts);   // tot[key]: the key's first slot
+    // each (chunk, key) count becomes the chunk's first slot for the key
     for (int key = threadIdx.x; key < NB; key += kThreads) {
-        const int base = tot[key];
-        for (int c = 0; c < n_chunks; c++) hist[(int64_t)c * NB + key] += base;
+        int run = tot[key];
+        for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+            int v[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; u++)
+                v[u] = c0 + u < n_chunks ? hist[(int64_t)(c0 + u) * NB + key] : 0;
+#pragma unroll
+            for (int u = 0; u < kBatch; u++)
+                if (c0 + u < n_chunks) {
+                    hist[(int64_t)(c0 + u) * NB + key] = run;
+                    run += v[u];
+                }
+        }
     }
 }
 
