@@ -55,7 +55,7 @@ TRAFFIC = {
         "sources": ["routed_moe_expert_amd/csrc/ffn_decode.hip",
                     "routed_moe_expert_amd/csrc/moe_internal.h"],
         "sha256": "e29566e8f962d11c3ad900dba8522c109ae073e68dece055e66e21665f6ea2e4",
-        "fetch_kib": 54366.9, "write_kib": 168.2,
+        "fetch_kib": 54367.0, "write_kib": 168.2,
     },
 }
 
