@@ -143,12 +143,17 @@ __global__ __launch_bounds__(kCastThreads) void xcast_kernel(const uint16_t *__r
     const int t = blockIdx.x, tid = threadIdx.x;
     const u32x4_t *src = reinterpret_cast<const u32x4_t *>(x + (int64_t)t * H);
     const int n8 = H / 8;   // 8 bf16 per 16-byte part
+    // the row is read once: a thread's parts stay in registers (H <= MOE_MAX_HIDDEN)
+    constexpr int kParts = MOE_MAX_HIDDEN / 8 / kCastThreads;
+    u32x4_t part[kParts];
     uint32_t amax = 0;      // |x| as bf16 bits: ordered like the magnitudes for finite values
-    for (int i = tid; i < n8; i += kCastThreads) {
-        const u32x4_t v = src[i];
+#pragma unroll
+    for (int u = 0; u < kParts; u++) {
+        const int i = tid + u * kCastThreads;
+        part[u] = i < n8 ? src[i] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < 4; j++)
-            amax = max(amax, max(v[j] & 0x7fffu, (v[j] >> 16) & 0x7fffu));
+            amax = max(amax, max(part[u][j] & 0x7fffu, (part[u][j] >> 16) & 0x7fffu));
     }
     for (int d = 32; d > 0; d >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, d, 64));
     if ((tid & 63) == 0) wmax[tid >> 6] = amax;
@@ -161,8 +166,11 @@ __global__ __launch_bounds__(kCastThreads) void xcast_kernel(const uint16_t *__r
     const int sc = mx > 0.f ? e - 15 : 0;
     const float inv = ldexpf(1.0f, -sc);
     u32x4_t *dst = reinterpret_cast<u32x4_t *>(x16 + (int64_t)t * H);
-    for (int i = tid; i < n8; i += kCastThreads) {
-        const u32x4_t v = src[i];
+#pragma unroll
+    for (int u = 0; u < kParts; u++) {
+        const int i = tid + u * kCastThreads;
+        if (i >= n8) break;
+        const u32x4_t v = part[u];
         u32x4_t o;
 #pragma unroll
         for (int j = 0; j < 4; j++) {
