@@ -69,7 +69,11 @@ def test_layer_at_max_width(seed, H, F):
                            moe.MOE_PATH_DECODE, dc.ws, dc.ws_bytes, raise_on_error=False)
     assert st == moe.MOE_ESHAPE
     ref = oracle.ffn_union(case)
-    assert_parity(dc.run(moe.MOE_PATH_AUTO), ref, f"max width H={H} F={F}")
+    y = dc.run(moe.MOE_PATH_AUTO)
+    assert_parity(y, ref, f"max width H={H} F={F}")
+    # the GEMM path from the K-step-packed copies at the widest K and row counts
+    dc.use_kpack()
+    assert np.array_equal(dc.run(moe.MOE_PATH_AUTO), y), "packed copies differ at max width"
 
 
 def test_decode_pairs_beyond_lds_plan():
