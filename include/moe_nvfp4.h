@@ -165,7 +165,7 @@ int moe_route_bucket(const int32_t *topk_ids, int32_t T, int32_t k, int32_t E, i
  * split the work the same way, a bandwidth-bound path for a few tokens per expert and grouped GEMMs
  * for prefill (moe_sk_repro.rs, its decode and prefill regimes); the pairs-per-expert limit is near
  * where the two paths measured equal on one MI355X, the GEMMs reading K-step-packed copies (about
- * 12 and 17 pairs per expert on the skewed hidden-4096 routings at ff 1280 and 640, 18 on the
+ * 12 and 16 pairs per expert on the skewed hidden-4096 routings at ff 1280 and 640, 18 on the
  * uniform E256 one; the decode kernels stream an expert's weights once per run of 16 pairs).
  * Returns the path, or minus an MOE_E* code for sizes moe_ffn_nvfp4 would refuse (-MOE_EINVAL,
  * -MOE_ESHAPE).
